@@ -1,0 +1,31 @@
+"""CPU oracle for the gated linear attention prefill forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import anything from this package.  It
+shares no code with the HIP library and never imports it.
+
+Parity status of each function (what pins it is in ``tests/test_oracle.py``):
+
+* ``token_recurrence`` (C, fp64): pinned by brute force, the g == 0 closed
+  form, hand-derived golden fixtures, split invariance, the T == 1 and
+  vanishing-gate special cases, and linearity / permutation invariants.
+* ``brute_force``, ``closed_form_zero_gate``: pinned against each other, the
+  golden fixtures and ``token_recurrence``.
+* ``chunk_cumsum``: pinned by its definition against ``numpy.cumsum`` of the
+  whole sequence and by the chunk totals.
+* ``intra_scores``: pinned against ``brute_force`` (the within-chunk part of
+  the output) and against a direct O(C^2 K) loop on tiny inputs.
+* ``chunked_reference``: pinned against ``token_recurrence`` at several chunk
+  sizes (chunking is a reordering of the same sums).
+"""
+
+from .reference import (  # noqa: F401
+    brute_force,
+    build_oracle_library,
+    chunk_cumsum,
+    chunked_reference,
+    closed_form_zero_gate,
+    intra_scores,
+    oracle_threads,
+    token_recurrence,
+)

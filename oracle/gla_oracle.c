@@ -1,0 +1,125 @@
+/*
+ * fp64 token-by-token oracle for the gated linear attention prefill forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header or constant with the HIP
+ * library.
+ *
+ * What it computes (plain definition, no chunking, no reordering):
+ *
+ *   for every (b, h) independently
+ *     S <- h0[b,h]  (K x V, or 0 when h0 is NULL)
+ *     for t = 0 .. T-1
+ *       S[d, :] <- exp(g[t, d]) * S[d, :]      for every key dim d
+ *       S       <- S + k_t^T v_t                 (rank-1 write)
+ *       o[t, :] <- scale * (q_t . S)             (uses S after token t)
+ *     h_final[b,h] <- S
+ *
+ * Sources: the state update "h <- h*g + k^T v" with a D x D state
+ * (blog "Linear Attention 在 GPU 上到底慢在哪", section 学长的反馈); the
+ * update-then-output recurrence in the pseudocode of "线性注意力GPU算子库的定义
+ * 与技术解析" (section 四, 工作原理); the high-precision token-by-token
+ * reference asked for in "面向长序列大模型的线性注意力算子性能评测方法与优化实践"
+ * (section 六.1).  The gate is a log-decay applied on the key (row) axis:
+ * decay = exp(g).
+ *
+ * Optional: `states` receives the state *before* token n*record_every, for
+ * n = 0 .. ceil(T/record_every)-1, i.e. the chunk-start states of a chunked
+ * evaluation with chunk = record_every.  That is still the plain recurrence,
+ * only observed at fixed token indices.
+ *
+ * Layouts (row-major, contiguous): q,k,g [B,H,T,K]; v,o [B,H,T,V];
+ * h0,h_final [B,H,K,V]; states [B,H,N,K,V].  All doubles.
+ * Parallelised with OpenMP over (b, h, block of 16 value columns): the value
+ * columns of S are independent because the decay acts on rows only.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_VBLK 16
+
+int gla_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int gla_oracle_f64(const double *q, const double *k, const double *v,
+                   const double *g, const double *h0, double *o,
+                   double *h_final, double *states, long B, long H, long T,
+                   long K, long V, double scale, long record_every,
+                   int threads) {
+    if (B < 0 || H < 0 || T < 0 || K <= 0 || V <= 0) return -1;
+    if (states && record_every <= 0) return -1;
+    const long BH = B * H;
+    const long nvb = (V + ORACLE_VBLK - 1) / ORACLE_VBLK;
+    const long nrec = (states && T > 0) ? (T + record_every - 1) / record_every : 0;
+    int status = 0;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long job = 0; job < BH * nvb; ++job) {
+        const long bh = job / nvb;
+        const long vb = job % nvb;
+        const long c0 = vb * ORACLE_VBLK;
+        const long nc = (V - c0) < ORACLE_VBLK ? (V - c0) : ORACLE_VBLK;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(K * nc));
+        double *decay = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!S || !decay) {
+            free(S);
+            free(decay);
+#pragma omp atomic write
+            status = -2;
+            continue;
+        }
+        for (long d = 0; d < K; ++d)
+            for (long c = 0; c < nc; ++c)
+                S[d * nc + c] = h0 ? h0[(bh * K + d) * V + c0 + c] : 0.0;
+
+        for (long t = 0; t < T; ++t) {
+            const double *qt = q + (bh * T + t) * K;
+            const double *kt = k + (bh * T + t) * K;
+            const double *gt = g + (bh * T + t) * K;
+            const double *vt = v + (bh * T + t) * V + c0;
+            if (states && t % record_every == 0) {
+                double *dst = states + ((bh * nrec + t / record_every) * K) * V;
+                for (long d = 0; d < K; ++d)
+                    for (long c = 0; c < nc; ++c) dst[d * V + c0 + c] = S[d * nc + c];
+            }
+            for (long d = 0; d < K; ++d) decay[d] = exp(gt[d]);
+            /* S[d,:] = exp(g[t,d]) * S[d,:] + k[t,d] * v[t,:] */
+            for (long d = 0; d < K; ++d) {
+                const double a = decay[d], kd = kt[d];
+                double *row = S + d * nc;
+                for (long c = 0; c < nc; ++c) row[c] = a * row[c] + kd * vt[c];
+            }
+            /* o[t,:] = scale * sum_d q[t,d] * S[d,:] */
+            double *ot = o + (bh * T + t) * V + c0;
+            for (long c = 0; c < nc; ++c) ot[c] = 0.0;
+            for (long d = 0; d < K; ++d) {
+                const double qd = qt[d];
+                const double *row = S + d * nc;
+                for (long c = 0; c < nc; ++c) ot[c] += qd * row[c];
+            }
+            for (long c = 0; c < nc; ++c) ot[c] *= scale;
+        }
+        if (h_final)
+            for (long d = 0; d < K; ++d)
+                for (long c = 0; c < nc; ++c)
+                    h_final[(bh * K + d) * V + c0 + c] = S[d * nc + c];
+        free(S);
+        free(decay);
+    }
+    return status;
+}
