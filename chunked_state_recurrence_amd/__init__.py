@@ -1,0 +1,23 @@
+"""MI355X-native chunked gated linear attention (GLA) prefill forward.
+
+The computation lives in libgla.so (hand-written HIP kernels for gfx950 behind
+the C ABI in include/gla.h); this package is its thin Python binding.  Build
+the library with ``python -m chunked_state_recurrence_amd.build``.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    GLAError,
+    GLALibraryMissing,
+    LIB_PATH,
+    gla_fwd,
+    gla_fwd_f32,
+    gla_stage_cumsum,
+    gla_stage_intra,
+    gla_stage_states,
+    load_library,
+    release,
+    set_tuning,
+    strerror,
+    version,
+)

@@ -1,0 +1,192 @@
+"""ctypes binding of libgla.so (include/gla.h, include/gla_stages.h).
+
+Argument marshalling only: shape/dtype/device checks, output allocation with
+torch, and the call.  Every step of the computation runs in the HIP kernels
+of libgla.so.  If the library has not been built, calls raise
+``GLALibraryMissing``; there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgla.so")
+
+GLA_OK = 0
+ERRORS = {
+    -1: "GLA_ERR_NULL", -2: "GLA_ERR_SHAPE", -3: "GLA_ERR_UNSUPPORTED", -4: "GLA_ERR_ALIGN",
+    -5: "GLA_ERR_LAUNCH", -6: "GLA_ERR_ALLOC", -7: "GLA_ERR_ALIAS", -8: "GLA_ERR_DEVICE",
+}
+
+# every symbol include/gla.h and include/gla_stages.h declare
+EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_version",
+            "gla_release", "gla_stage_cumsum", "gla_stage_intra", "gla_stage_states")
+
+
+class GLALibraryMissing(RuntimeError):
+    pass
+
+
+class GLAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgla.so and declare the C signatures (no GPU call is made)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise GLALibraryMissing(
+            f"{path} is not built; run `python -m chunked_state_recurrence_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.gla_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
+    lib.gla_fwd_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
+    lib.gla_stage_states.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
+    lib.gla_stage_cumsum.argtypes = [P, P, P, I, I, I, I, I, P]
+    lib.gla_stage_intra.argtypes = [P, P, P, P, I, I, I, I, I, F, P]
+    lib.gla_set_tuning.argtypes = [I, I]
+    lib.gla_strerror.argtypes = [I]
+    lib.gla_strerror.restype = ctypes.c_char_p
+    lib.gla_version.argtypes = []
+    lib.gla_release.argtypes = []
+    lib.gla_release.restype = None
+    for name in ("gla_fwd", "gla_fwd_f32", "gla_stage_states", "gla_stage_cumsum",
+                 "gla_stage_intra", "gla_set_tuning", "gla_version"):
+        getattr(lib, name).restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(code: int):
+    if code != GLA_OK:
+        raise GLAError(code, load_library().gla_strerror(code).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _fwd(fn, io_dtype, q, k, v, g, h0, chunk, scale, want_final, o, h_final, stream,
+         states=None):
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    for t, n, dt, shp in ((q, "q", io_dtype, (B, H, T, K)), (k, "k", io_dtype, (B, H, T, K)),
+                          (v, "v", io_dtype, (B, H, T, V)), (g, "g", torch.float32, (B, H, T, K)),
+                          (h0, "h0", torch.float32, (B, H, K, V))):
+        _need(t, n, dt, shp, dev)
+    if scale is None:
+        scale = K ** -0.5
+    if o is None:
+        o = torch.empty((B, H, T, V), dtype=io_dtype, device=dev)
+    _need(o, "o", io_dtype, (B, H, T, V), dev)
+    if want_final and h_final is None:
+        h_final = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+    _need(h_final, "h_final", torch.float32, (B, H, K, V), dev)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(o), _ptr(h_final)]
+    if states is not None:
+        args.append(_ptr(states))
+    rc = fn(*args, B, H, T, K, V, int(chunk), float(scale), _stream(stream))
+    _check(rc)
+    return o, h_final
+
+
+def gla_fwd(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=False, o=None,
+            h_final=None, stream=None):
+    """bf16 forward: q, k, v bf16 [B,H,T,D]; g fp32 [B,H,T,D]; h0 fp32 [B,H,D,D] or None.
+
+    Returns (o bf16 [B,H,T,D], h_final fp32 [B,H,D,D] or None).
+    """
+    return _fwd(load_library().gla_fwd, torch.bfloat16, q, k, v, g, h0, chunk, scale,
+                want_final, o, h_final, stream)
+
+
+def gla_fwd_f32(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=False, o=None,
+                h_final=None, stream=None):
+    """fp32 forward: the same operation with fp32 q, k, v and o."""
+    return _fwd(load_library().gla_fwd_f32, torch.float32, q, k, v, g, h0, chunk, scale,
+                want_final, o, h_final, stream)
+
+
+def gla_stage_states(q, k, v, g, h0=None, *, chunk=64, scale=None, stream=None):
+    """bf16 forward that also returns the chunk-start states [B,H,N,D,D] fp32."""
+    B, H, T, K = q.shape
+    n = (T + chunk - 1) // chunk
+    states = torch.empty((B, H, n, K, v.shape[-1]), dtype=torch.float32, device=q.device)
+    o, hf = _fwd(load_library().gla_stage_states, torch.bfloat16, q, k, v, g, h0, chunk, scale,
+                 True, None, None, stream, states=states)
+    return o, hf, states
+
+
+def gla_stage_cumsum(g, *, chunk=64, stream=None):
+    """Chunk-local cumsum of g: returns (Gc [B,H,T,D], Gamma [B,H,N,D]) fp32."""
+    B, H, T, K = g.shape
+    _need(g, "g", torch.float32, (B, H, T, K), g.device)
+    n = (T + chunk - 1) // chunk
+    gc = torch.empty_like(g)
+    gam = torch.empty((B, H, n, K), dtype=torch.float32, device=g.device)
+    _check(load_library().gla_stage_cumsum(_ptr(g), _ptr(gc), _ptr(gam), B, H, T, K, int(chunk),
+                                           _stream(stream)))
+    return gc, gam
+
+
+def gla_stage_intra(q, k, g, *, chunk=64, scale=None, stream=None):
+    """Scaled intra-chunk scores A [B,H,N,C,C] fp32 (bf16 q, k; fp32 g)."""
+    B, H, T, K = q.shape
+    for t, n, dt in ((q, "q", torch.bfloat16), (k, "k", torch.bfloat16), (g, "g", torch.float32)):
+        _need(t, n, dt, (B, H, T, K), q.device)
+    if scale is None:
+        scale = K ** -0.5
+    n = (T + chunk - 1) // chunk
+    A = torch.empty((B, H, n, chunk, chunk), dtype=torch.float32, device=q.device)
+    _check(load_library().gla_stage_intra(_ptr(q), _ptr(k), _ptr(g), _ptr(A), B, H, T, K,
+                                          int(chunk), float(scale), _stream(stream)))
+    return A
+
+
+def set_tuning(target_wgs: int = 0, head_group: int = 0):
+    _check(load_library().gla_set_tuning(int(target_wgs), int(head_group)))
+
+
+def version() -> int:
+    return int(load_library().gla_version())
+
+
+def strerror(code: int) -> str:
+    return load_library().gla_strerror(int(code)).decode()
+
+
+def release():
+    load_library().gla_release()

@@ -1,0 +1,300 @@
+// gla_api.hip — C ABI of libgla.so: argument validation, segment scheduling,
+// workspace, launches.  Declarations and contracts: include/gla.h and
+// include/gla_stages.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "gla.h"
+#include "gla_stages.h"
+#include "gla_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kDefaultTargetWgs = 256;
+
+struct DeviceState {
+    int arch_ok = -1;  // -1 unknown, 0 not gfx950, 1 gfx950
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+};
+
+std::mutex g_mu;
+std::vector<DeviceState> g_dev;
+int g_target_wgs = kDefaultTargetWgs;
+int g_head_group = 0;
+
+int current_device(DeviceState **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GLA_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (size_t(dev) >= g_dev.size()) g_dev.resize(dev + 1);
+    DeviceState &d = g_dev[dev];
+    if (d.arch_ok < 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GLA_ERR_DEVICE;
+        d.arch_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    }
+    if (d.arch_ok != 1) return GLA_ERR_DEVICE;
+    *out = &d;
+    return GLA_OK;
+}
+
+int ensure_workspace(DeviceState *d, size_t bytes, float **out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (d->ws_bytes < bytes) {
+        if (d->ws) {
+            (void)hipFree(d->ws);  // hipFree waits for work that may still use it
+            d->ws = nullptr;
+            d->ws_bytes = 0;
+        }
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return GLA_ERR_ALLOC;
+        }
+        d->ws = p;
+        d->ws_bytes = bytes;
+    }
+    *out = static_cast<float *>(d->ws);
+    return GLA_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+struct Call {
+    int dtype;
+    const void *q, *k, *v;
+    const float *g, *h0;
+    void *o;
+    float *h_final;
+    float *states;  // stage output (chunk-start states) or nullptr
+    int B, H, T, K, V, chunk;
+    float scale;
+    hipStream_t stream;
+};
+
+int default_chunk(int dtype, int D) {
+    if (gla::chunk_supported(dtype, D, 64)) return 64;
+    return 32;
+}
+
+int validate(Call &c) {
+    if (c.B <= 0 || c.H <= 0 || c.T < 0 || c.K <= 0 || c.V <= 0) return GLA_ERR_SHAPE;
+    if (long(c.B) * c.H > (1L << 30) || long(c.T) * c.K >= (1L << 29)) return GLA_ERR_SHAPE;
+    if (c.K != c.V || (c.K != 64 && c.K != 128)) return GLA_ERR_UNSUPPORTED;
+    if (c.chunk < 0) return GLA_ERR_UNSUPPORTED;
+    if (c.chunk == 0) c.chunk = default_chunk(c.dtype, c.K);
+    if (!gla::chunk_supported(c.dtype, c.K, c.chunk)) return GLA_ERR_UNSUPPORTED;
+    if (c.T > 0 && (!c.q || !c.k || !c.v || !c.g || !c.o)) return GLA_ERR_NULL;
+    const void *ptrs[] = {c.q, c.k, c.v, c.g, c.h0, c.o, c.h_final, c.states};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return GLA_ERR_ALIGN;
+    const size_t es = c.dtype == gla::DTYPE_BF16 ? 2 : 4;
+    const size_t bht = size_t(c.B) * c.H * c.T;
+    const size_t nqk = bht * c.K * es, nv = bht * c.V * es, ng = bht * c.K * 4;
+    const size_t nst = size_t(c.B) * c.H * c.K * c.V * 4;
+    const size_t nchunks = c.T > 0 ? size_t((c.T + c.chunk - 1) / c.chunk) : 0;
+    const size_t nstates = size_t(c.B) * c.H * nchunks * c.K * c.V * 4;
+    struct R { const void *p; size_t n; } ins[] = {{c.q, nqk}, {c.k, nqk}, {c.v, nv}, {c.g, ng}, {c.h0, nst}};
+    for (const R &r : ins) {
+        if (overlaps(c.o, nv, r.p, r.n)) return GLA_ERR_ALIAS;
+        if (overlaps(c.h_final, nst, r.p, r.n)) return GLA_ERR_ALIAS;
+        if (overlaps(c.states, nstates, r.p, r.n)) return GLA_ERR_ALIAS;
+    }
+    if (overlaps(c.h_final, nst, c.o, nv)) return GLA_ERR_ALIAS;
+    if (overlaps(c.states, nstates, c.o, nv) || overlaps(c.states, nstates, c.h_final, nst))
+        return GLA_ERR_ALIAS;
+    return GLA_OK;
+}
+
+struct Plan {
+    int P, cps;
+};
+
+Plan plan_segments(int nbh, int N, int target) {
+    int P = std::max(1, (target + nbh - 1) / nbh);
+    P = std::min(P, N);
+    const int cps = (N + P - 1) / P;
+    P = (N + cps - 1) / cps;
+    return {P, cps};
+}
+
+int run_forward(Call &c) {
+    int rc = validate(c);
+    if (rc != GLA_OK) return rc;
+    DeviceState *dev = nullptr;
+    if ((rc = current_device(&dev)) != GLA_OK) return rc;
+    const int D = c.K;
+    const long BH = long(c.B) * c.H;
+    if (c.T == 0) {
+        if (c.h_final && gla::launch_copy_state(c.h_final, c.h0, BH * D * D, c.stream) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+        return GLA_OK;
+    }
+    const int N = (c.T + c.chunk - 1) / c.chunk;
+    int target, hg;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        target = g_target_wgs;
+        hg = g_head_group;
+    }
+    long group = hg > 0 ? std::min<long>(hg, BH) : BH;
+    group = std::min<long>(group, 65535);
+
+    // workspace: the largest group's (P-1) segment states and decays
+    size_t need = 0;
+    for (long g0 = 0; g0 < BH; g0 += group) {
+        const int nbh = int(std::min(group, BH - g0));
+        const Plan pl = plan_segments(nbh, N, target);
+        need = std::max(need, size_t(nbh) * size_t(pl.P - 1) * size_t(D) * (D + 1) * 4);
+    }
+    float *ws = nullptr;
+    if (need > 0 && (rc = ensure_workspace(dev, need, &ws)) != GLA_OK) return rc;
+
+    for (long g0 = 0; g0 < BH; g0 += group) {
+        const int nbh = int(std::min(group, BH - g0));
+        const Plan pl = plan_segments(nbh, N, target);
+        gla::KernelParams p{};
+        p.q = c.q; p.k = c.k; p.v = c.v; p.g = c.g; p.h0 = c.h0;
+        p.o = c.o; p.h_final = c.h_final;
+        p.ws_E = ws;
+        p.ws_G = ws ? ws + size_t(nbh) * (pl.P - 1) * D * D : nullptr;
+        p.dump = c.states; p.dump2 = nullptr;
+        p.T = c.T; p.N = N; p.cps = pl.cps; p.P = pl.P; p.bh0 = g0; p.scale = c.scale;
+        if (pl.P > 1) {
+            if (gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_SEG, p, pl.P - 1, nbh, c.stream) != hipSuccess)
+                return GLA_ERR_LAUNCH;
+            if (gla::launch_scan(p.ws_E, p.ws_G, c.h0, g0, nbh, pl.P, D, c.stream) != hipSuccess)
+                return GLA_ERR_LAUNCH;
+        }
+        if (gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_OUT, p, pl.P, nbh, c.stream) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+    }
+    return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_fwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g,
+            const float *h0, gla_bf16 *o, float *h_final, int B, int H, int T, int K, int V,
+            int chunk, float scale, void *stream) {
+    Call c{gla::DTYPE_BF16, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
+           static_cast<hipStream_t>(stream)};
+    return run_forward(c);
+}
+
+int gla_fwd_f32(const float *q, const float *k, const float *v, const float *g, const float *h0,
+                float *o, float *h_final, int B, int H, int T, int K, int V, int chunk, float scale,
+                void *stream) {
+    Call c{gla::DTYPE_F32, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
+           static_cast<hipStream_t>(stream)};
+    return run_forward(c);
+}
+
+int gla_stage_states(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g,
+                     const float *h0, gla_bf16 *o, float *h_final, float *states, int B, int H,
+                     int T, int K, int V, int chunk, float scale, void *stream) {
+    if (T > 0 && !states) return GLA_ERR_NULL;
+    Call c{gla::DTYPE_BF16, q, k, v, g, h0, o, h_final, states, B, H, T, K, V, chunk, scale,
+           static_cast<hipStream_t>(stream)};
+    return run_forward(c);
+}
+
+static int run_stage(int mode, const void *q, const void *k, const float *g, float *out,
+                     float *out2, int B, int H, int T, int K, int chunk, float scale, void *stream) {
+    Call c{gla::DTYPE_BF16, q, k, q, g, nullptr, out, nullptr, nullptr, B, H, T, K, K, chunk, scale,
+           static_cast<hipStream_t>(stream)};
+    if (B <= 0 || H <= 0 || T < 0 || K <= 0) return GLA_ERR_SHAPE;
+    if (K != 64 && K != 128) return GLA_ERR_UNSUPPORTED;
+    if (chunk < 0) return GLA_ERR_UNSUPPORTED;
+    if (chunk == 0) c.chunk = default_chunk(c.dtype, K);
+    if (!gla::chunk_supported(c.dtype, K, c.chunk)) return GLA_ERR_UNSUPPORTED;
+    if (T == 0) return GLA_OK;
+    if (!g || !out || (mode == gla::MODE_INTRA && (!q || !k)) || (mode == gla::MODE_CUMSUM && !out2))
+        return GLA_ERR_NULL;
+    const void *ptrs[] = {q, k, g, out, out2};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return GLA_ERR_ALIGN;
+    DeviceState *dev = nullptr;
+    int rc = current_device(&dev);
+    if (rc != GLA_OK) return rc;
+    const int N = (T + c.chunk - 1) / c.chunk;
+    const long BH = long(B) * H;
+    gla::KernelParams p{};
+    p.q = q; p.k = k; p.v = q; p.g = g;
+    p.dump = out; p.dump2 = out2;
+    p.T = T; p.N = N; p.cps = 1; p.P = N; p.scale = scale;
+    for (long g0 = 0; g0 < BH; g0 += 65535) {
+        p.bh0 = g0;
+        const int nbh = int(std::min<long>(65535, BH - g0));
+        if (gla::launch_chunk_kernel(c.dtype, K, c.chunk, mode, p, N, nbh, c.stream) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+    }
+    return GLA_OK;
+}
+
+int gla_stage_cumsum(const float *g, float *gc, float *gamma, int B, int H, int T, int K, int chunk,
+                     void *stream) {
+    return run_stage(gla::MODE_CUMSUM, nullptr, nullptr, g, gc, gamma, B, H, T, K, chunk, 1.0f, stream);
+}
+
+int gla_stage_intra(const gla_bf16 *q, const gla_bf16 *k, const float *g, float *A, int B, int H,
+                    int T, int K, int chunk, float scale, void *stream) {
+    return run_stage(gla::MODE_INTRA, q, k, g, A, nullptr, B, H, T, K, chunk, scale, stream);
+}
+
+int gla_set_tuning(int target_wgs, int head_group) {
+    if (target_wgs < 0 || head_group < 0) return GLA_ERR_SHAPE;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_target_wgs = target_wgs > 0 ? target_wgs : kDefaultTargetWgs;
+    g_head_group = head_group;
+    return GLA_OK;
+}
+
+const char *gla_strerror(int code) {
+    switch (code) {
+        case GLA_OK: return "ok";
+        case GLA_ERR_NULL: return "a required pointer is NULL";
+        case GLA_ERR_SHAPE: return "invalid shape (B, H >= 1, T >= 0, sizes within limits)";
+        case GLA_ERR_UNSUPPORTED: return "unsupported head dim or chunk size";
+        case GLA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+        case GLA_ERR_LAUNCH: return "kernel launch failed";
+        case GLA_ERR_ALLOC: return "workspace allocation failed";
+        case GLA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+        case GLA_ERR_DEVICE: return "no usable gfx950 HIP device";
+        default: return "unknown error code";
+    }
+}
+
+int gla_version(void) { return kVersion; }
+
+void gla_release(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    for (size_t i = 0; i < g_dev.size(); ++i) {
+        if (g_dev[i].ws) {
+            (void)hipSetDevice(int(i));
+            (void)hipFree(g_dev[i].ws);
+            g_dev[i].ws = nullptr;
+            g_dev[i].ws_bytes = 0;
+        }
+    }
+    if (cur >= 0) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

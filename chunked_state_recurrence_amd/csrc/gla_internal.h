@@ -1,0 +1,41 @@
+// gla_internal.h — shared between the kernels and the C-ABI layer of libgla.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace gla {
+
+enum { DTYPE_BF16 = 0, DTYPE_F32 = 1 };
+
+// MODE_OUT: output pass from given segment start states (writes o, h_final,
+//           and optionally the chunk-start states into `dump`).
+// MODE_SEG: end state of each segment from a zero start (writes ws_E, ws_G).
+// MODE_INTRA / MODE_CUMSUM: single stages written to `dump` / `dump2`.
+enum { MODE_OUT = 0, MODE_SEG = 1, MODE_INTRA = 2, MODE_CUMSUM = 3 };
+
+struct KernelParams {
+    const void *q, *k, *v;
+    const float *g;
+    const float *h0;
+    void *o;
+    float *h_final;
+    float *ws_E;   // [nbh][P-1][D][D]  segment end states, then segment start states
+    float *ws_G;   // [nbh][P-1][D]     segment total log2-decay
+    float *dump;   // stage outputs
+    float *dump2;
+    int T;         // tokens per (batch, head)
+    int N;         // chunks per (batch, head)
+    int cps;       // chunks per segment
+    int P;         // segments
+    long bh0;      // first (batch, head) row of this launch
+    float scale;
+};
+
+bool chunk_supported(int dtype, int D, int C);
+hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, const KernelParams &p,
+                               int grid_x, int grid_y, hipStream_t s);
+hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,
+                       int P, int D, hipStream_t s);
+hipError_t launch_copy_state(float *dst, const float *src, long n, hipStream_t s);
+
+}  // namespace gla

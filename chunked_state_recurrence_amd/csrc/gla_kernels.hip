@@ -1,0 +1,766 @@
+// gla_kernels.hip — gfx950 kernels for the chunked gated-linear-attention
+// prefill forward.
+//
+// Math (per batch row and head): S_t = diag(exp g_t) S_{t-1} + k_t^T v_t,
+// o_t = scale q_t S_t (blog "Linear Attention 在 GPU 上到底慢在哪", section
+// 学长的反馈; pseudocode of "线性注意力GPU算子库的定义与技术解析", section 四).
+// The chunk form follows the GPU flow of that page (section 四, steps 1-3):
+// per chunk of C tokens,
+//   Gc      = chunk-local inclusive cumsum of g            (stage "cumsum")
+//   A[i,j]  = sum_d q_i k_j exp(Gc_i - Gc_j), j <= i        (intra-chunk scores)
+//   o_i     = scale (q_i exp(Gc_i)) S_n + scale sum_j A_ij v_j   (output)
+//   S_{n+1} = diag(exp Gamma) S_n + (k exp(Gamma - Gc))^T V      (state pass)
+// which are the five kernels the blog profiles (section 实验结果, Kernel
+// Profiling: cumsum, intra_sub_inter, intra_sub_intra, chunk_fwd_kernel_h,
+// chunk_gla_fwd_kernel_o), fused here into one pass per sequence segment.
+//
+// Sequence parallelism (same page, section 三.1: chunks processed in
+// parallel, states merged across them): the T axis is split into P segments.
+//   launch 1 (MODE_SEG): each segment's end state from a zero start, E_r,
+//                        and its total log-decay;
+//   launch 2 (scan):     S_start(r+1) = diag(exp Gamma_r) S_start(r) + E_r;
+//   launch 3 (MODE_OUT): every segment replays its chunks from S_start(r),
+//                        writing o (and h_final for the last segment).
+//
+// Work-group = C/16 waves; wave w owns rows [16w, 16w+16) of a chunk for the
+// gate cumsum and the exponentials, row block w of the score matrix, and
+// value columns [w*D/(C/16), ...) of the state S and of the output.  S lives
+// in MFMA accumulators for the whole segment.  Exponentials use exp2 with
+// log2-scaled gates.  Within-chunk factors use one reference point per
+// 16-row block, so every exponent but the diagonal blocks' is <= 0; a
+// diagonal block whose gate span exceeds SPAN_GUARD (log2 units) is formed
+// elementwise instead (the blog's intra_sub_inter / intra_sub_intra split).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gla_internal.h"
+
+namespace gla {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSpanGuard = 80.0f;  // log2 units: factors stay within 2^+-80
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Element types.  bf16: one v_mfma_f32_16x16x32_bf16 per 32-deep step.  f32:
+// the same 32-deep step as eight v_mfma_f32_16x16x4f32.  Both take operand
+// fragments of 8 values per lane: lane l holds row/column (l & 15) and the 8
+// reduction positions {8*(l>>4) .. +7} of a 32-deep block.  Any fixed
+// assignment of reduction positions works as long as both operands use it.
+// ---------------------------------------------------------------------------
+struct BF16 {
+    using gmem_t = uint16_t;
+    using lds_t = __bf16;
+    using frag_t = bf16x8_t;
+    __device__ static float g2f(gmem_t x) { return __uint_as_float(uint32_t(x) << 16); }
+    __device__ static lds_t f2l(float x) { return (__bf16)x; }
+    __device__ static float l2f(lds_t x) { return (float)x; }
+    __device__ static frag_t ld_frag(const lds_t *p) { return *reinterpret_cast<const frag_t *>(p); }
+    __device__ static void st_frag(lds_t *p, frag_t f) { *reinterpret_cast<frag_t *>(p) = f; }
+    __device__ static frag_t pack(const float *x) {
+        frag_t f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (__bf16)x[i];
+        return f;
+    }
+    __device__ static void unpack(frag_t f, float *x) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)f[i];
+    }
+    __device__ static f32x4_t mma(frag_t a, frag_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // store 4 consecutive outputs (8 bytes) at byte offset `off`
+    __device__ static void st4(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
+        bf16x4_t b;
+        b[0] = (__bf16)v[0]; b[1] = (__bf16)v[1]; b[2] = (__bf16)v[2]; b[3] = (__bf16)v[3];
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, b), r, off, 0, 0);
+    }
+};
+
+struct F32 {
+    using gmem_t = float;
+    using lds_t = float;
+    using frag_t = f32x8_t;
+    __device__ static float g2f(gmem_t x) { return x; }
+    __device__ static lds_t f2l(float x) { return x; }
+    __device__ static float l2f(lds_t x) { return x; }
+    __device__ static frag_t ld_frag(const lds_t *p) {
+        const f32x4_t a = reinterpret_cast<const f32x4_t *>(p)[0];
+        const f32x4_t b = reinterpret_cast<const f32x4_t *>(p)[1];
+        frag_t f;
+        f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+        f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+        return f;
+    }
+    __device__ static void st_frag(lds_t *p, frag_t f) {
+        reinterpret_cast<f32x4_t *>(p)[0] = f32x4_t{f[0], f[1], f[2], f[3]};
+        reinterpret_cast<f32x4_t *>(p)[1] = f32x4_t{f[4], f[5], f[6], f[7]};
+    }
+    __device__ static frag_t pack(const float *x) {
+        frag_t f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = x[i];
+        return f;
+    }
+    __device__ static void unpack(frag_t f, float *x) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = f[i];
+    }
+    __device__ static f32x4_t mma(frag_t a, frag_t b, f32x4_t c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+        return c;
+    }
+    __device__ static void st4(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
+        typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), r, off, 0, 0);
+    }
+};
+
+// Buffer descriptors (gfx9 raw buffers): a load past num_records returns 0
+// and a store past it is dropped, which masks the partial last chunk
+// without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, long bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes), 0x00020000);
+}
+
+// CPL consecutive elements of one row of q, k or v, as loaded from HBM.
+template <typename E, int CPL> struct Raw;
+template <> struct Raw<BF16, 2> {
+    uint32_t x;
+    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+    __device__ float get(int u) const { return __uint_as_float(u ? (x & 0xffff0000u) : (x << 16)); }
+};
+template <> struct Raw<BF16, 1> {
+    uint16_t x;
+    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+    __device__ float get(int) const { return __uint_as_float(uint32_t(x) << 16); }
+};
+template <> struct Raw<F32, 2> {
+    u32x2_t x;
+    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
+    __device__ float get(int u) const { return __uint_as_float(u ? x.y : x.x); }
+};
+template <> struct Raw<F32, 1> {
+    uint32_t x;
+    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+    __device__ float get(int) const { return __uint_as_float(x); }
+};
+template <int CPL> struct RawG;
+template <> struct RawG<2> {
+    u32x2_t x;
+    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
+    __device__ float get(int u) const { return __uint_as_float(u ? x.y : x.x); }
+};
+template <> struct RawG<1> {
+    uint32_t x;
+    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+    __device__ float get(int) const { return __uint_as_float(x); }
+};
+
+// Column position inside a row of the row-major q/k tiles in LDS.  Within
+// every 32-column block, key dims {4a..4a+3} (a < 4) go to 8a.., and
+// {16+4a..} go to 8a+4..: a fragment read of 8 consecutive positions then
+// holds exactly the key dims of two 16-row accumulator tiles of S, so S can be
+// fed to the MFMA straight from its accumulators.
+__device__ __forceinline__ int perm_col(int c) {
+    const int blk = c & ~31, in = c & 31, a = in >> 2, e = in & 3;
+    return blk + (a < 4 ? (a << 3) + e : ((a - 4) << 3) + 4 + e);
+}
+
+// LDS carve-up (bytes).  Pitches pad rows by 16 bytes against bank conflicts.
+template <typename E, int D, int C> struct Layout {
+    static constexpr int es = sizeof(typename E::lds_t);
+    static constexpr int NW = C / 16;
+    static constexpr int QP = D + 16 / es;   // Qb / Qh / Kb row pitch (elements)
+    static constexpr int TP = C + 16 / es;   // Kht / Vt / A row pitch (elements)
+    static constexpr int qb = 0;
+    static constexpr int qh = qb + C * QP * es;
+    static constexpr int kb = qh + C * QP * es;
+    static constexpr int kht = kb + C * QP * es;
+    static constexpr int vt = kht + D * TP * es;
+    static constexpr int a = vt + D * TP * es;
+    static constexpr int btot = a + C * TP * es;          // float [2][NW][D]
+    static constexpr int bb = btot + 2 * NW * D * 4;       // float [NW][D] block totals (permuted cols)
+    static constexpr int eg = bb + NW * D * 4;             // float [D]     exp2(Gamma) (natural cols)
+    static constexpr int bytes = eg + D * 4;
+};
+
+template <typename T> __device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+template <typename E, int D, int C, int MODE>
+__global__ void __launch_bounds__(C / 16 * 64)
+chunk_kernel(const KernelParams p) {
+    constexpr int NW = C / 16;     // waves == 16-row blocks per chunk
+    constexpr int CPL = D / 64;    // key/value columns per lane in the row mapping
+    constexpr int VS = D / NW;     // value columns per wave
+    constexpr int NTW = VS / 16;   // 16-wide value tiles per wave
+    constexpr int MT = D / 16;     // 16-row key tiles of S
+    constexpr int KS = D / 32;     // 32-deep key steps
+    constexpr int TS = C / 32;     // 32-deep token steps
+    static_assert(NTW >= 1 && TS >= 1 && CPL >= 1, "unsupported tile shape");
+    constexpr bool kOut = MODE == MODE_OUT;
+    constexpr bool kSeg = MODE == MODE_SEG;
+    constexpr bool kIntra = MODE == MODE_INTRA;
+    constexpr bool kCumsum = MODE == MODE_CUMSUM;
+    constexpr bool kScores = kOut || kIntra;     // needs the score matrix
+    constexpr bool kState = kOut || kSeg;        // carries S
+    using L = Layout<E, D, C>;
+    using lds_t = typename E::lds_t;
+    using gmem_t = typename E::gmem_t;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
+    lds_t *sQb = reinterpret_cast<lds_t *>(smem + L::qb);
+    lds_t *sQh = reinterpret_cast<lds_t *>(smem + L::qh);
+    lds_t *sKb = reinterpret_cast<lds_t *>(smem + L::kb);
+    lds_t *sKht = reinterpret_cast<lds_t *>(smem + L::kht);
+    lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);
+    lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);
+    float *sBtot = reinterpret_cast<float *>(smem + L::btot);
+    float *sBb = reinterpret_cast<float *>(smem + L::bb);
+    float *sEG = reinterpret_cast<float *>(smem + L::eg);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int n16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int seg = blockIdx.x;
+    const long bhl = blockIdx.y;               // index inside this launch's head group
+    const long bh = p.bh0 + bhl;               // absolute (batch, head) row
+    const int T = p.T;
+    const int c_begin = seg * p.cps;
+    const int c_end = min(p.N, c_begin + p.cps);
+    const int vb = w * VS;                     // this wave's first value column
+
+    const gmem_t *gq = reinterpret_cast<const gmem_t *>(p.q) + bh * long(T) * D;
+    const gmem_t *gk = reinterpret_cast<const gmem_t *>(p.k) + bh * long(T) * D;
+    const gmem_t *gv = reinterpret_cast<const gmem_t *>(p.v) + bh * long(T) * D;
+    const float *gg = p.g + bh * long(T) * D;
+
+    // ---- state init ---------------------------------------------------------
+    f32x4_t S[MT][NTW];
+    if constexpr (kState) {
+        const float *src = nullptr;
+        if constexpr (kOut) {
+            if (seg == 0) src = p.h0 ? p.h0 + bh * D * D : nullptr;
+            else src = p.ws_E + (bhl * (p.P - 1) + seg - 1) * long(D) * D;
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[mt][nt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] : 0.f;
+    }
+    if constexpr (kOut) {  // blocks above the diagonal of A are never written: zero them once
+        for (int i = tid; i < C * L::TP; i += NW * 64) sA[i] = E::f2l(0.f);
+    }
+    float seg_gamma[CPL];
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) seg_gamma[u] = 0.f;
+
+    // ---- raw rows of the current chunk (this wave's 16 rows, CPL columns) --
+    Raw<E, CPL> rq[16], rk[16], rv[16];
+    RawG<CPL> rg[16];
+    constexpr int es = sizeof(gmem_t);
+    const rsrc_t bq = make_rsrc(gq, long(T) * D * es);
+    const rsrc_t bk = make_rsrc(gk, long(T) * D * es);
+    const rsrc_t bv = make_rsrc(gv, long(T) * D * es);
+    const rsrc_t bg = make_rsrc(gg, long(T) * D * 4);
+    auto load_chunk = [&](int c) {
+        const int row0 = c * C + 16 * w;           // rows past T read as zero
+        const int eoff = row0 * D + lane * CPL;    // element offset of row i = 0
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            rg[i].load(bg, (eoff + i * D) * 4);
+            if constexpr (kScores) rq[i].load(bq, (eoff + i * D) * es);
+            if constexpr (!kCumsum) rk[i].load(bk, (eoff + i * D) * es);
+            if constexpr (kState) rv[i].load(bv, (eoff + i * D) * es);
+        }
+    };
+    if (c_begin < c_end) load_chunk(c_begin);
+
+    int buf = 0;
+    for (int c = c_begin; c < c_end; ++c) {
+        const int t0 = c * C;
+        // ---- a1: gate cumsum (log2 units) inside this wave's 16-row block.
+        // Every exponent below is a direct sum of gates of one sign (a prefix,
+        // a suffix or a run of block totals), never a difference of two
+        // prefix sums: that keeps huge gates from cancelling into O(1)
+        // exponent errors.
+        float Pf[16][CPL];   // inclusive prefix within the block
+        float Sf[16][CPL];   // exclusive suffix within the block
+        float Bw[CPL];
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                run += rg[i].get(u) * kLog2e;
+                Pf[i][u] = run;
+            }
+            Bw[u] = run;
+            float suf = 0.f;
+#pragma unroll
+            for (int i = 15; i >= 0; --i) {
+                Sf[i][u] = suf;
+                suf += rg[i].get(u) * kLog2e;
+            }
+            sBtot[(buf * NW + w) * D + lane * CPL + u] = run;
+        }
+        float span = 0.f;
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) span = fmaxf(span, -Bw[u]);
+        span = wave_max(span);
+        __syncthreads();  // B1: block totals visible
+
+        float rw[CPL], aw[CPL], gam[CPL];   // blocks before w, after w, all
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+            float before = 0.f, after = 0.f, tot = 0.f;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const float b = sBtot[(buf * NW + j) * D + lane * CPL + u];
+                if (j < w) before += b;
+                if (j > w) after += b;
+                tot += b;
+            }
+            rw[u] = before;
+            aw[u] = after;
+            gam[u] = tot;
+        }
+
+        if constexpr (kCumsum) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int t = t0 + 16 * w + i;
+                if (t < T)
+#pragma unroll
+                    for (int u = 0; u < CPL; ++u)
+                        p.dump[(bh * long(T) + t) * D + lane * CPL + u] = (rw[u] + Pf[i][u]) * kLn2;
+            }
+            if (w == 0)
+#pragma unroll
+                for (int u = 0; u < CPL; ++u)
+                    p.dump2[(bh * long(p.N) + c) * D + lane * CPL + u] = gam[u] * kLn2;
+            if (c + 1 < c_end) load_chunk(c + 1);
+            buf ^= 1;
+            continue;
+        }
+
+        // ---- operand tiles into LDS -----------------------------------------
+        if constexpr (kScores) {
+            float ew[CPL], xk[CPL];
+#pragma unroll
+            for (int u = 0; u < CPL; ++u) {
+                ew[u] = fexp2(rw[u]);    // chunk start -> block start   <= 1
+                xk[u] = fexp2(aw[u]);    // block end   -> chunk end     <= 1
+                const int col = lane * CPL + u;
+                sBb[w * D + perm_col(col)] = Bw[u];
+                if constexpr (kOut) if (w == 0) sEG[col] = fexp2(gam[u]);
+            }
+            float khv[16][CPL];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float qb[CPL], qh[CPL], kb[CPL];
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) {
+                    const float eq = fexp2(Pf[i][u]);    // block start -> row i   <= 1
+                    const float ek = fexp2(Sf[i][u]);    // row i -> block end     <= 1
+                    qb[u] = p.scale * rq[i].get(u) * eq;
+                    qh[u] = qb[u] * ew[u];               // scale q exp(Gc_i)
+                    kb[u] = rk[i].get(u) * ek;
+                    khv[i][u] = kb[u] * xk[u];           // k exp(Gamma - Gc_i)
+                }
+                const int row = 16 * w + i;
+                const int pc = perm_col(lane * CPL);
+                if constexpr (CPL == 2) {
+                    typedef typename E::lds_t l2_t __attribute__((ext_vector_type(2)));
+                    l2_t a, b, d;
+                    a[0] = E::f2l(qb[0]); a[1] = E::f2l(qb[1]);
+                    b[0] = E::f2l(qh[0]); b[1] = E::f2l(qh[1]);
+                    d[0] = E::f2l(kb[0]); d[1] = E::f2l(kb[1]);
+                    *reinterpret_cast<l2_t *>(sQb + row * L::QP + pc) = a;
+                    *reinterpret_cast<l2_t *>(sQh + row * L::QP + pc) = b;
+                    *reinterpret_cast<l2_t *>(sKb + row * L::QP + pc) = d;
+                } else {
+                    sQb[row * L::QP + pc] = E::f2l(qb[0]);
+                    sQh[row * L::QP + pc] = E::f2l(qh[0]);
+                    sKb[row * L::QP + pc] = E::f2l(kb[0]);
+                }
+            }
+            if constexpr (kOut) {
+                // transposed: Kht[d][token], Vt[v][token]; 16 consecutive tokens per column
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) {
+                    const int col = lane * CPL + u;
+                    float kk[16], vv[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) { kk[i] = khv[i][u]; vv[i] = rv[i].get(u); }
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        E::st_frag(sKht + col * L::TP + 16 * w + 8 * h, E::pack(kk + 8 * h));
+                        E::st_frag(sVt + col * L::TP + 16 * w + 8 * h, E::pack(vv + 8 * h));
+                    }
+                }
+            }
+            // diagonal block with a large gate span: exact elementwise scores,
+            // A[i][j] = scale sum_d q_i k_j exp(g_{j+1} + ... + g_i)
+            if (span > kSpanGuard) {
+#pragma unroll 1
+                for (int i = 0; i < 16; ++i) {
+                    float qi[CPL], ex[CPL];
+#pragma unroll
+                    for (int u = 0; u < CPL; ++u) {
+                        qi[u] = 0.f;
+                        ex[u] = 0.f;
+#pragma unroll
+                        for (int x = 0; x < 16; ++x)
+                            if (x == i) qi[u] = rq[x].get(u);
+                    }
+                    for (int j = i; j >= 0; --j) {
+                        float part = 0.f;
+#pragma unroll
+                        for (int u = 0; u < CPL; ++u) {
+                            // rows live in registers: select row j
+                            float kj = 0.f, gj = 0.f;
+#pragma unroll
+                            for (int x = 0; x < 16; ++x)
+                                if (x == j) { kj = rk[x].get(u); gj = rg[x].get(u) * kLog2e; }
+                            part += qi[u] * kj * fexp2(ex[u]);
+                            ex[u] += gj;   // exponent for j-1: g_j + ... + g_i
+                        }
+                        const float s = wave_sum(part) * p.scale;
+                        if (lane == 0) {
+                            if constexpr (kOut) sA[(16 * w + i) * L::TP + 16 * w + j] = E::f2l(s);
+                            else p.dump[((bh * long(p.N) + c) * C + 16 * w + i) * C + 16 * w + j] = s;
+                        }
+                    }
+                    if constexpr (kIntra) {  // zeros above the diagonal of this block
+                        if (lane < 16 && lane > i)
+                            p.dump[((bh * long(p.N) + c) * C + 16 * w + i) * C + 16 * w + lane] = 0.f;
+                    }
+                }
+            }
+        }
+        if constexpr (kSeg) {
+#pragma unroll
+            for (int u = 0; u < CPL; ++u) {
+                const int col = lane * CPL + u;
+                if (w == 0) sEG[col] = fexp2(gam[u]);
+                float kk[16], vv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    kk[i] = rk[i].get(u) * fexp2(Sf[i][u] + aw[u]);  // k exp(Gamma - Gc_i)
+                    vv[i] = rv[i].get(u);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    E::st_frag(sKht + col * L::TP + 16 * w + 8 * h, E::pack(kk + 8 * h));
+                    E::st_frag(sVt + col * L::TP + 16 * w + 8 * h, E::pack(vv + 8 * h));
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) seg_gamma[u] += gam[u];
+
+        // prefetch the next chunk; the loads fly during the matrix work below
+        if (c + 1 < c_end) load_chunk(c + 1);
+        __syncthreads();  // B2: operand tiles visible
+
+        // ---- a2: scores of row block I = w, column blocks J <= I --------------
+        // Tile (I, J) = Kb[J] Qb[I]^T with the k side moved from the end of
+        // block J to the start of block I: factor exp(B_{J+1} + ... + B_{I-1})
+        // (<= 1); on the diagonal the factor is exp(-B_I) (<= 2^kSpanGuard).
+        if constexpr (kScores) {
+            const int I = w;
+#pragma unroll
+            for (int J = 0; J < NW; ++J) {
+                if (J > I) {
+                    if constexpr (kIntra) {  // zero tile above the diagonal
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            p.dump[((bh * long(p.N) + c) * C + 16 * I + n16) * C + 16 * J + 4 * q4 + e] = 0.f;
+                    }
+                    continue;
+                }
+                if (J == I && span > kSpanGuard) continue;  // formed elementwise above
+                const bool rescale = (J < I - 1) || (J == I);
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int pos = ks * 32 + 8 * q4;
+                    typename E::frag_t a = E::ld_frag(sKb + (16 * J + n16) * L::QP + pos);
+                    if (rescale) {
+                        float x[8], ex[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ex[e] = 0.f;
+                        if (J == I) {
+                            const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sBb + I * D + pos);
+                            const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sBb + I * D + pos + 4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) { ex[e] = -b0[e]; ex[4 + e] = -b1[e]; }
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < NW; ++j) {
+                                if (j <= J || j >= I) continue;
+                                const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sBb + j * D + pos);
+                                const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sBb + j * D + pos + 4);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) { ex[e] += b0[e]; ex[4 + e] += b1[e]; }
+                            }
+                        }
+                        E::unpack(a, x);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] *= fexp2(ex[e]);
+                        a = E::pack(x);
+                    }
+                    const typename E::frag_t b = E::ld_frag(sQb + (16 * I + n16) * L::QP + pos);
+                    acc = E::mma(a, b, acc);
+                }
+                // acc[e] = A[16I + n16][16J + 4q4 + e]
+                if (J == I) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * q4 + e > n16) acc[e] = 0.f;
+                }
+                if constexpr (kOut) {
+                    typedef typename E::lds_t l4_t __attribute__((ext_vector_type(4)));
+                    l4_t v4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v4[e] = E::f2l(acc[e]);
+                    *reinterpret_cast<l4_t *>(sA + (16 * I + n16) * L::TP + 16 * J + 4 * q4) = v4;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        p.dump[((bh * long(p.N) + c) * C + 16 * I + n16) * C + 16 * J + 4 * q4 + e] = acc[e];
+                }
+            }
+        }
+        if constexpr (kIntra) {
+            buf ^= 1;
+            __syncthreads();  // LDS reuse by the next chunk
+            continue;
+        }
+
+        typename E::frag_t vf[NTW][TS];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int ts = 0; ts < TS; ++ts)
+                vf[nt][ts] = E::ld_frag(sVt + (vb + 16 * nt + n16) * L::TP + ts * 32 + 8 * q4);
+
+        if constexpr (kOut) {
+            __syncthreads();  // B3: score tiles visible
+            if (p.dump) {     // chunk-start states (stage test only)
+                float *dst = p.dump + (bh * long(p.N) + c) * long(D) * D;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
+            }
+            // ---- a4: O^T tiles (value tile nt, token tile m) ---------------------
+            f32x4_t O[NTW][NW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int m = 0; m < NW; ++m) O[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // inter-chunk: O^T += S^T (q exp Gc)^T, S straight from its accumulators
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                __builtin_amdgcn_sched_barrier(0);  // bound the fragment loads in flight
+                typename E::frag_t sf[NTW];
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { x[e] = S[2 * ks][nt][e]; x[4 + e] = S[2 * ks + 1][nt][e]; }
+                    sf[nt] = E::pack(x);
+                }
+#pragma unroll
+                for (int m = 0; m < NW; ++m) {
+                    const typename E::frag_t b = E::ld_frag(sQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) O[nt][m] = E::mma(sf[nt], b, O[nt][m]);
+                }
+            }
+            // intra-chunk: O^T += V^T A^T over causal token steps
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < NW; ++m) {
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+                    if (ts * 32 > 16 * m + 15) continue;
+                    const typename E::frag_t b = E::ld_frag(sA + (16 * m + n16) * L::TP + ts * 32 + 8 * q4);
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) O[nt][m] = E::mma(vf[nt][ts], b, O[nt][m]);
+                }
+            }
+            const rsrc_t bo = make_rsrc(reinterpret_cast<gmem_t *>(p.o) + bh * long(T) * D, long(T) * D * es);
+#pragma unroll
+            for (int m = 0; m < NW; ++m) {
+                const int row = t0 + 16 * m + n16;   // rows past T are dropped
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    E::st4(bo, (row * D + vb + 16 * nt + 4 * q4) * es, O[nt][m]);
+            }
+        }
+
+        // ---- a3: S <- diag(exp2 Gamma) S + Kht^T V ------------------------------
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4_t eg = *reinterpret_cast<const f32x4_t *>(sEG + 16 * mt + 4 * q4);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[mt][nt][e] *= eg[e];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if ((mt & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ts = 0; ts < TS; ++ts) {
+                const typename E::frag_t a = E::ld_frag(sKht + (16 * mt + n16) * L::TP + ts * 32 + 8 * q4);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) S[mt][nt] = E::mma(a, vf[nt][ts], S[mt][nt]);
+            }
+        }
+        buf ^= 1;
+    }
+
+    // ---- segment end --------------------------------------------------------
+    if constexpr (kState) {
+        float *dst = nullptr;
+        if constexpr (kOut) {
+            if (seg == p.P - 1 && p.h_final) dst = p.h_final + bh * long(D) * D;
+        } else {
+            dst = p.ws_E + (bhl * (p.P - 1) + seg) * long(D) * D;
+            if (w == 0)
+#pragma unroll
+                for (int u = 0; u < CPL; ++u)
+                    p.ws_G[(bhl * (p.P - 1) + seg) * D + lane * CPL + u] = seg_gamma[u];
+        }
+        if (dst) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
+        }
+    }
+}
+
+// Exclusive scan of the segment maps: E_r <- S_start(r+1) in place.
+// One thread per (head, key dim, value column).
+__global__ void __launch_bounds__(256)
+scan_kernel(float *__restrict__ ws_E, const float *__restrict__ ws_G,
+            const float *__restrict__ h0, long bh0, int nbh, int P, int D) {
+    const long idx = long(blockIdx.x) * 256 + threadIdx.x;
+    const long DD = long(D) * D;
+    if (idx >= long(nbh) * DD) return;
+    const long bhl = idx / DD;
+    const long dv = idx - bhl * DD;
+    const int d = int(dv / D);
+    float s = h0 ? h0[(bh0 + bhl) * DD + dv] : 0.f;
+    float *e = ws_E + bhl * (P - 1) * DD + dv;
+    const float *gm = ws_G + bhl * (P - 1) * D + d;
+    for (int r = 0; r < P - 1; ++r) {
+        s = fexp2(gm[long(r) * D]) * s + e[long(r) * DD];
+        e[long(r) * DD] = s;
+    }
+}
+
+// T == 0: h_final <- h0 (or 0).
+__global__ void __launch_bounds__(256)
+copy_state_kernel(float *__restrict__ dst, const float *__restrict__ src, long n) {
+    const long i = long(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C, int MODE>
+static hipError_t launch_one(const KernelParams &p, int grid_x, int grid_y, hipStream_t s) {
+    if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
+    hipLaunchKernelGGL((chunk_kernel<E, D, C, MODE>), dim3(grid_x, grid_y), dim3(C / 16 * 64), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename E, int D, int C>
+static hipError_t dispatch_mode(int mode, const KernelParams &p, int gx, int gy, hipStream_t s) {
+    switch (mode) {
+        case MODE_OUT: return launch_one<E, D, C, MODE_OUT>(p, gx, gy, s);
+        case MODE_SEG: return launch_one<E, D, C, MODE_SEG>(p, gx, gy, s);
+        case MODE_INTRA: return launch_one<E, D, C, MODE_INTRA>(p, gx, gy, s);
+        case MODE_CUMSUM: return launch_one<E, D, C, MODE_CUMSUM>(p, gx, gy, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, const KernelParams &p,
+                               int gx, int gy, hipStream_t s) {
+    if (dtype == DTYPE_BF16) {
+        if (D == 128 && C == 64) return dispatch_mode<BF16, 128, 64>(mode, p, gx, gy, s);
+        if (D == 128 && C == 32) return dispatch_mode<BF16, 128, 32>(mode, p, gx, gy, s);
+        if (D == 64 && C == 64) return dispatch_mode<BF16, 64, 64>(mode, p, gx, gy, s);
+        if (D == 64 && C == 32) return dispatch_mode<BF16, 64, 32>(mode, p, gx, gy, s);
+    } else if (dtype == DTYPE_F32) {
+        if (D == 64 && C == 64) return dispatch_mode<F32, 64, 64>(mode, p, gx, gy, s);
+        if (D == 64 && C == 32) return dispatch_mode<F32, 64, 32>(mode, p, gx, gy, s);
+        if (D == 128 && C == 32) return dispatch_mode<F32, 128, 32>(mode, p, gx, gy, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool chunk_supported(int dtype, int D, int C) {
+    if (dtype == DTYPE_BF16) return (D == 128 || D == 64) && (C == 64 || C == 32);
+    if (dtype == DTYPE_F32) return (D == 64 && (C == 64 || C == 32)) || (D == 128 && C == 32);
+    return false;
+}
+
+hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,
+                       int P, int D, hipStream_t s) {
+    const long n = long(nbh) * D * D;
+    const long blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(scan_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, ws_E, ws_G, h0, bh0, nbh, P, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_state(float *dst, const float *src, long n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const long blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(copy_state_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, dst, src, n);
+    return hipGetLastError();
+}
+
+}  // namespace gla

@@ -1,0 +1,90 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+headers declare, and rejects bad arguments with the documented codes before
+anything is enqueued (fake device pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_state_recurrence_amd as gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gla.h", "gla_stages.h")]
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gla.LIB_PATH),
+                                reason="libgla.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gla_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_headers_declare_the_binding_symbols():
+    assert sorted(gla.EXPORTED) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gla.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_host_only_calls():
+    assert gla.version() == 100
+    assert gla.strerror(0) == "ok"
+    for code in range(-8, 0):
+        assert gla.strerror(code) != "unknown error code"
+    assert gla.strerror(-99) == "unknown error code"
+    gla.set_tuning(0, 0)
+    with pytest.raises(gla.GLAError):
+        gla.set_tuning(-1, 0)
+
+
+FAKE = 1 << 40          # 16-byte aligned, never dereferenced
+STEP = 1 << 32          # far apart: no overlap between fake buffers
+
+
+def _call(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + STEP, v=FAKE + 2 * STEP, g=FAKE + 3 * STEP, h0=None,
+             o=FAKE + 4 * STEP, hf=None, B=1, H=2, T=100, K=128, V=128, chunk=64, scale=0.1)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.gla_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["h0"]), vp(a["o"]),
+                       vp(a["hf"]), a["B"], a["H"], a["T"], a["K"], a["V"], a["chunk"],
+                       a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(H=-1), -2), (dict(T=-5), -2), (dict(T=1 << 24), -2),
+    (dict(K=128, V=64), -3), (dict(K=96, V=96), -3), (dict(chunk=48), -3), (dict(chunk=128), -3),
+    (dict(q=None), -1), (dict(g=None), -1), (dict(o=None), -1),
+    (dict(q=FAKE + 8), -4), (dict(hf=FAKE + 5 * STEP + 4), -4),
+    (dict(o=FAKE + 64), -7), (dict(hf=FAKE + 4 * STEP + 4096), -7),
+    (dict(h0=FAKE + 6 * STEP, hf=FAKE + 6 * STEP), -7),
+])
+def test_argument_errors(kw, code):
+    lib = gla.load_library()
+    assert _call(lib, **kw) == code
+
+
+def test_fp32_chunk_support_table():
+    lib = gla.load_library()
+    vp = ctypes.c_void_p
+
+    def f32(K, chunk):
+        return lib.gla_fwd_f32(vp(FAKE), vp(FAKE + STEP), vp(FAKE + 2 * STEP), vp(FAKE + 3 * STEP),
+                               None, vp(FAKE + 4 * STEP), None, 1, 1, 10, K, K, chunk, 1.0, None)
+    assert f32(128, 64) == -3
+    assert f32(64, 128) == -3
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(gla.GLALibraryMissing):
+        gla.load_library(str(tmp_path / "libgla.so"))

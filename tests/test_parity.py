@@ -1,0 +1,281 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bar (stated by the benchmark spec and the evaluation page's correctness
+method, "面向长序列大模型的线性注意力算子性能评测方法与优化实践" section 六.1):
+max|o - o_ref| / max|o_ref| <= 1e-2 for bf16 output, <= 1e-3 for fp32 output,
+the same normalised error for the final state, and no NaN/Inf.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_state_recurrence_amd as gla
+import oracle
+from chunked_state_recurrence_amd.workloads import WORKLOADS, make_inputs, to_f64_numpy
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+TOL_F32 = 1e-3
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def nerr(out, ref):
+    out = np.asarray(out, dtype=np.float64)
+    return float(np.max(np.abs(out - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+@pytest.fixture(autouse=True)
+def _default_tuning():
+    gla.set_tuning(0, 0)
+    yield
+    gla.set_tuning(0, 0)
+
+
+def gpu_run(x, *, fp32=False, chunk=0, want_final=True, scale=None):
+    d = {n: (None if x[n] is None else x[n].to(DEV)) for n in ("q", "k", "v", "g", "h0")}
+    fn = gla.gla_fwd_f32 if fp32 else gla.gla_fwd
+    o, hf = fn(d["q"], d["k"], d["v"], d["g"], d["h0"], chunk=chunk, scale=scale,
+               want_final=want_final)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), (None if hf is None else hf.cpu().numpy())
+
+
+def oracle_run(x, scale, heads=None):
+    f = {n: to_f64_numpy(x[n]) for n in ("q", "k", "v", "g", "h0")}
+    if heads is not None:  # sampled (b, h) pairs, each run over the full sequence
+        f = {n: (None if a is None else np.stack([a[b, h] for (b, h) in heads])[None])
+             for n, a in f.items()}
+    o, hf, _ = oracle.token_recurrence(f["q"], f["k"], f["v"], f["g"], f["h0"], scale)
+    return o, hf
+
+
+def check(x, scale, o, hf, tol, heads=None):
+    assert np.isfinite(o).all(), "non-finite output"
+    ro, rh = oracle_run(x, scale, heads)
+    if heads is not None:
+        o = np.stack([o[b, h] for (b, h) in heads])[None]
+        hf = None if hf is None else np.stack([hf[b, h] for (b, h) in heads])[None]
+    e = nerr(o, ro)
+    say(f"    output err {e:.3e} (tol {tol:g})")
+    assert e <= tol
+    if hf is not None:
+        assert np.isfinite(hf).all()
+        eh = nerr(hf, rh)
+        say(f"    h_final err {eh:.3e}")
+        assert eh <= tol
+    return e
+
+
+# ---------------------------------------------------------------- tiny fp32 ---
+
+@pytest.mark.parametrize("gate", ["ls16", "zero"])
+@pytest.mark.parametrize("chunk", [64, 32])
+def test_tiny_f32_workload(gate, chunk):
+    wl = WORKLOADS["tiny_f32"]
+    say(f"[tiny_f32] gate={gate} chunk={chunk}")
+    x = make_inputs(wl, gate=gate)
+    o, hf = gpu_run(x, fp32=True, chunk=chunk)
+    check(x, wl.scale, o, hf, TOL_F32)
+    if gate == "zero":  # the closed form agrees too
+        f = {n: to_f64_numpy(x[n]) for n in "qkv"}
+        oc, _ = oracle.closed_form_zero_gate(f["q"], f["k"], f["v"], None, wl.scale)
+        assert nerr(o, oc) <= TOL_F32
+
+
+def test_f32_head_dim_128():
+    wl = WORKLOADS["tiny_f32"]
+    x = make_inputs(dataclass_replace(wl, D=128), T=200, H=2)
+    say("[f32 D=128] T=200 chunk=32")
+    o, hf = gpu_run(x, fp32=True, chunk=32)
+    check(x, 128 ** -0.5, o, hf, TOL_F32)
+
+
+def dataclass_replace(wl, **kw):
+    import dataclasses
+    return dataclasses.replace(wl, **kw)
+
+
+# ------------------------------------------------------- bf16 small shapes ---
+
+SMALL = [
+    # (B, H, T, D, chunk, h0)
+    (1, 2, 1, 128, 64, False),
+    (2, 3, 63, 128, 64, True),
+    (1, 2, 64, 128, 64, False),
+    (2, 2, 65, 128, 64, True),
+    (1, 3, 200, 128, 32, True),
+    (2, 2, 1000, 128, 64, True),
+    (1, 2, 777, 64, 64, True),
+    (1, 2, 300, 64, 32, False),
+]
+
+
+@pytest.mark.parametrize("B,H,T,D,chunk,h0", SMALL)
+def test_bf16_small_shapes(B, H, T, D, chunk, h0):
+    wl = dataclass_replace(WORKLOADS["prefill_4k"], D=D)
+    say(f"[bf16 small] B={B} H={H} T={T} D={D} chunk={chunk} h0={h0}")
+    x = make_inputs(wl, B=B, H=H, T=T, seed=T + D, h0_std=0.5 if h0 else None)
+    o, hf = gpu_run(x, chunk=chunk)
+    check(x, D ** -0.5, o, hf, TOL_BF16)
+
+
+@pytest.mark.parametrize("target", [1, 4, 64, 100000])
+def test_bf16_segment_splits(target):
+    """Force 1 .. N segments so the segment-state pass and scan are exercised."""
+    wl = WORKLOADS["prefill_4k"]
+    x = make_inputs(wl, B=1, H=2, T=1000, seed=5, h0_std=0.3)
+    say(f"[segments] target_wgs={target}")
+    gla.set_tuning(target, 0)
+    o, hf = gpu_run(x)
+    check(x, wl.scale, o, hf, TOL_BF16)
+
+
+def test_bf16_head_groups():
+    wl = WORKLOADS["prefill_4k"]
+    x = make_inputs(wl, B=2, H=3, T=500, seed=6, h0_std=0.3)
+    say("[head groups] group=4 target=32")
+    gla.set_tuning(32, 4)
+    o, hf = gpu_run(x)
+    check(x, wl.scale, o, hf, TOL_BF16)
+
+
+@pytest.mark.parametrize("gate", ["const:-30", "const:-10000", "ls41", "mixed"])
+def test_bf16_extreme_gates(gate):
+    wl = WORKLOADS["prefill_4k"]
+    say(f"[extreme gates] {gate}")
+    if gate == "mixed":  # ordinary gates with rare huge drops
+        x = make_inputs(wl, B=1, H=2, T=700, seed=8, h0_std=0.3)
+        gen = torch.Generator().manual_seed(9)
+        spikes = torch.rand(x["g"].shape, generator=gen) < 0.01
+        x["g"] = torch.where(spikes, torch.full_like(x["g"], -200.0), x["g"])
+    else:
+        x = make_inputs(wl, B=1, H=2, T=700, seed=8, gate=gate, h0_std=0.3)
+    o, hf = gpu_run(x)
+    check(x, wl.scale, o, hf, TOL_BF16)
+
+
+def test_bf16_chunk_invariance():
+    wl = WORKLOADS["prefill_4k"]
+    x = make_inputs(wl, B=1, H=2, T=640, seed=10, h0_std=0.2)
+    say("[chunk invariance] 32 vs 64")
+    o32, h32 = gpu_run(x, chunk=32)
+    o64, h64 = gpu_run(x, chunk=64)
+    check(x, wl.scale, o32, h32, TOL_BF16)
+    check(x, wl.scale, o64, h64, TOL_BF16)
+
+
+def test_bf16_split_invariance():
+    """[0, T1) then [T1, T) with h0 = h_final of the first part."""
+    wl = WORKLOADS["prefill_4k"]
+    x = make_inputs(wl, B=1, H=2, T=900, seed=11, h0_std=0.2)
+    say("[split invariance] T1=333")
+    o, hf = gpu_run(x)
+    t1 = 333
+    xa = {n: (x[n] if n == "h0" else x[n][:, :, :t1].contiguous()) for n in x}
+    oa, ha = gpu_run(xa)
+    xb = {n: x[n][:, :, t1:].contiguous() for n in "qkvg"}
+    xb["h0"] = torch.from_numpy(ha)
+    ob, hb = gpu_run(xb)
+    ref_o, ref_h = oracle_run(x, wl.scale)
+    assert nerr(np.concatenate([oa, ob], axis=2), ref_o) <= TOL_BF16
+    assert nerr(hb, ref_h) <= TOL_BF16
+
+
+def test_bitwise_repeatable():
+    wl = WORKLOADS["prefill_4k"]
+    x = make_inputs(wl, B=1, H=4, T=2048, seed=12)
+    say("[repeatable]")
+    o1, h1 = gpu_run(x)
+    o2, h2 = gpu_run(x)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+def test_zero_length_sequence():
+    d = dict(q=torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device=DEV),
+             g=torch.empty(1, 2, 0, 128, device=DEV))
+    h0 = torch.randn(1, 2, 128, 128, device=DEV)
+    say("[T=0]")
+    o, hf = gla.gla_fwd(d["q"], d["q"], d["q"], d["g"], h0, want_final=True)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 2, 0, 128)
+    assert torch.equal(hf, h0)
+    o, hf = gla.gla_fwd(d["q"], d["q"], d["q"], d["g"], None, want_final=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(hf) == 0
+
+
+# ----------------------------------------------------------------- stages ---
+
+def test_stage_cumsum():
+    x = make_inputs(WORKLOADS["prefill_4k"], B=1, H=2, T=300, seed=13)
+    say("[stage cumsum]")
+    gc, gam = gla.gla_stage_cumsum(x["g"].to(DEV), chunk=64)
+    torch.cuda.synchronize()
+    rgc, rgam = oracle.chunk_cumsum(to_f64_numpy(x["g"]), 64)
+    assert nerr(gc.cpu().numpy(), rgc) < 1e-5
+    assert nerr(gam.cpu().numpy(), rgam) < 1e-5
+
+
+@pytest.mark.parametrize("gate", ["ls16", "const:-30"])
+def test_stage_intra(gate):
+    wl = WORKLOADS["prefill_4k"]
+    x = make_inputs(wl, B=1, H=2, T=200, seed=14, gate=gate)
+    say(f"[stage intra] gate={gate}")
+    A = gla.gla_stage_intra(x["q"].to(DEV), x["k"].to(DEV), x["g"].to(DEV), chunk=64)
+    torch.cuda.synchronize()
+    ref = oracle.intra_scores(to_f64_numpy(x["q"]), to_f64_numpy(x["k"]), to_f64_numpy(x["g"]),
+                              64, scale=wl.scale)
+    A = A.cpu().numpy()
+    # rows/cols past T in the last chunk are don't-care; compare the valid part
+    T = 200
+    for n in range(ref.shape[2]):
+        L = min(64, T - 64 * n)
+        e = nerr(A[:, :, n, :L, :L], ref[:, :, n, :L, :L])
+        assert e <= TOL_BF16, (n, e)
+        assert np.all(A[:, :, n][:, :, np.triu_indices(64, 1)[0], np.triu_indices(64, 1)[1]] == 0)
+
+
+def test_stage_states():
+    wl = WORKLOADS["prefill_4k"]
+    x = make_inputs(wl, B=1, H=2, T=500, seed=15, h0_std=0.3)
+    say("[stage states]")
+    gla.set_tuning(8, 0)  # several segments: states come through the scan
+    d = {n: x[n].to(DEV) for n in ("q", "k", "v", "g", "h0")}
+    o, hf, st = gla.gla_stage_states(d["q"], d["k"], d["v"], d["g"], d["h0"], chunk=64)
+    torch.cuda.synchronize()
+    f = {n: to_f64_numpy(x[n]) for n in ("q", "k", "v", "g", "h0")}
+    _, _, rst = oracle.token_recurrence(f["q"], f["k"], f["v"], f["g"], f["h0"], wl.scale,
+                                        record_every=64)
+    assert nerr(st.cpu().numpy(), rst) <= TOL_BF16
+
+
+# ----------------------------------------------------- full-size workloads ---
+
+FULL = [
+    ("prefill_4k", [(0, 0), (0, 15)]),
+    ("prefill_16k", [(0, 3), (0, 12)]),
+    ("batch16_4k", [(0, 0), (7, 9), (15, 15)]),
+    ("long_128k", [(0, 5)]),
+]
+
+
+@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
+def test_full_size_workload_sampled_heads(name, heads):
+    """Full-size run in the benchmark's launch configuration; sampled (b, h)
+    pairs are checked over their whole sequence against the oracle, every
+    output is checked finite."""
+    wl = WORKLOADS[name]
+    say(f"[full {name}] B={wl.B} H={wl.H} T={wl.T} sampled={heads}")
+    x = make_inputs(wl)
+    o, hf = gpu_run(x, want_final=wl.want_final)
+    check(x, wl.scale, o, hf, TOL_BF16, heads=heads)
