@@ -1,0 +1,290 @@
+"""Benchmark: chunked GLA prefill forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_16k]
+
+A step is one gla_fwd call over the whole workload (every stage of the path:
+segment end states, their scan, and the fused cumsum / intra-chunk / output /
+state pass), inputs resident in HBM.  Two independent input sets alternate
+between steps so that the 256 MB Infinity Cache cannot serve a whole step
+from the previous one.  K steps are timed between two synchronisations with
+HIP events; the dominant kernel (the output pass) is timed on its own launch
+stream with the library's event tracing inside the same timed region.
+
+Prints one JSON line.  ``value`` is prefill tokens/s = B*T / step time.
+``roofline`` prices the output pass against HBM bandwidth with the
+algorithmic bytes of the workload (bf16 q, k, v, o + fp32 g per token-head,
+plus the fp32 final state); ``cpu_baseline`` is the fp64 oracle timed on the
+host cores over a bounded sample of the same workload.
+
+Helpers for the counter runs (used under rocprofv3):
+    --copy-calibration  also runs a plain device copy of known size, so
+                        FETCH_SIZE / WRITE_SIZE can be scaled to bytes
+    --summarize-counters DIR  parses rocprofv3 counter CSVs under DIR and
+                        writes profiles/counters_<workload>.json
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "prefill tokens/s, chunk GLA fwd H=16 D=128 bf16; % MFMA peak / HBM BW"
+# The pages' number for this workload (FLA chunk_gla, RTX 4090, bf16, H=16,
+# D=128, B=1, T=16K: 2.17 ms) as tokens/s: another machine, context only.
+PAGES_TOKENS_PER_S = {"prefill_16k": 1 * 16384 / 2.17e-3, "prefill_4k": 1 * 4096 / 0.47e-3}
+KERNEL_SOURCES = [os.path.join(ROOT, "chunked_state_recurrence_amd", "csrc", f)
+                  for f in ("gla_kernels.hip", "gla_api.hip", "gla_internal.h")]
+COPY_BYTES = 1 << 30
+
+
+def algorithmic_bytes(wl) -> int:
+    """bf16 q, k, v, o (2 B each) + fp32 g (4 B) per token-head element row,
+    plus the fp32 h0 read and h_final write when present."""
+    th = wl.B * wl.H * wl.T
+    es = 2 if wl.dtype == "bf16" else 4
+    per_token_head = wl.D * (4 * es + 4)          # 1536 B at D=128, bf16
+    state = wl.B * wl.H * wl.D * wl.D * 4
+    return th * per_token_head + (state if wl.want_final else 0) + (state if wl.h0_std else 0)
+
+
+def algorithmic_flops(wl, chunk: int) -> int:
+    """Per token-head: scores (C+1)K, A.V (C+1)V, q.S 2KV, K^T V 2KV (the dense
+    T^2 work the chunk form avoids is not counted)."""
+    th = wl.B * wl.H * wl.T
+    return th * (4 * wl.D * wl.D + (chunk + 1) * 2 * wl.D)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, x, budget_s: float = 20.0):
+    """Time the fp64 oracle on the host: whole heads of the workload, as many
+    as fit the time budget (at least one), extrapolated to tokens/s of the
+    full workload."""
+    import numpy as np
+    import oracle
+    from chunked_state_recurrence_amd.workloads import to_f64_numpy
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+
+    def run(sel):
+        f = {n: (None if x[n] is None else
+                 np.stack([to_f64_numpy(x[n][b, h]) for (b, h) in sel])[None])
+             for n in ("q", "k", "v", "g", "h0")}
+        t0 = time.perf_counter()
+        oracle.token_recurrence(f["q"], f["k"], f["v"], f["g"], f["h0"], wl.scale,
+                                threads=threads)
+        return time.perf_counter() - t0
+
+    t1 = run(pairs[:1])
+    n = max(1, min(len(pairs), int(budget_s / max(t1, 1e-6))))
+    n = max(n, min(len(pairs), threads))  # keep every thread busy when it is cheap
+    t = run(pairs[:n]) if n > 1 else t1
+    full = t * len(pairs) / n
+    return {"value": wl.B * wl.T / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.B * wl.H} (batch, head) sequences, full T={wl.T}, fp64 "
+                      f"token recurrence, {t:.2f} s; scaled to all heads",
+            "seconds": round(t, 3)}
+
+
+def read_counters(wl_name: str):
+    path = os.path.join(ROOT, "profiles", f"counters_{wl_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_digest") != source_digest():
+        return None  # the kernel changed since the counters were taken
+    return c
+
+
+def summarize_counters(outdir: str, wl_name: str):
+    """Parse rocprofv3 counter-collection CSVs (one pass for FETCH_SIZE, one
+    for WRITE_SIZE) and write profiles/counters_<workload>.json."""
+    import csv
+    rows = []
+    for p in glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {outdir}")
+    acc = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        ctr = r.get("Counter_Name", "")
+        val = float(r.get("Counter_Value", "nan"))
+        if "chunk_kernel" in name and "ELi0E" in name:
+            kind = "output"
+        elif "chunk_kernel" in name and "ELi1E" in name:
+            kind = "segment"
+        elif "scan_kernel" in name:
+            kind = "scan"
+        elif "copy" in name.lower() or "elementwise" in name.lower():
+            kind = "copy"
+        else:
+            continue
+        acc.setdefault((kind, ctr), []).append(val)
+    summary = {k[0] + ":" + k[1]: statistics.median(v) for k, v in acc.items()}
+    out = {"workload": wl_name, "source_digest": source_digest(), "median_per_dispatch_KiB": summary,
+           "copy_bytes": COPY_BYTES}
+    cf, cw = summary.get("copy:FETCH_SIZE"), summary.get("copy:WRITE_SIZE")
+    if cf and cw:
+        out["fetch_factor"] = COPY_BYTES / (cf * 1024.0)
+        out["write_factor"] = COPY_BYTES / (cw * 1024.0)
+    path = os.path.join(ROOT, "profiles", f"counters_{wl_name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_16k")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--target-wgs", type=int, default=0)
+    ap.add_argument("--head-group", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-counters", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunked_state_recurrence_amd as gla
+    from chunked_state_recurrence_amd.workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    if wl.dtype != "bf16":
+        raise SystemExit("bench.py measures the bf16 workloads")
+    dev = torch.device("cuda:0")
+    gla.set_tuning(args.target_wgs, args.head_group)
+    chunk = args.chunk or 64
+
+    host = make_inputs(wl)
+    sets = []
+    for s in range(2):
+        d = {n: (None if host[n] is None else host[n].to(dev)) for n in ("q", "k", "v", "g", "h0")}
+        if s == 1:  # a second, independent copy of the same inputs
+            d = {n: (None if t is None else t.clone()) for n, t in d.items()}
+        d["o"] = torch.empty(wl.B, wl.H, wl.T, wl.D, dtype=torch.bfloat16, device=dev)
+        d["hf"] = (torch.empty(wl.B, wl.H, wl.D, wl.D, dtype=torch.float32, device=dev)
+                   if wl.want_final else None)
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        d = sets[i & 1]
+        gla.gla_fwd(d["q"], d["k"], d["v"], d["g"], d["h0"], chunk=chunk, scale=wl.scale,
+                    o=d["o"], h_final=d["hf"], want_final=wl.want_final, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps between synchronisations; per-step and per-kernel
+    # HIP events on the launch stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    gla.profile_start(8 * args.steps + 8)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    kernels = gla.profile_stop()
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = total_ms / args.steps
+
+    if args.copy_calibration:  # a plain copy of known size for counter scaling
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    by_kind = {}
+    for kind, kms in kernels:
+        by_kind.setdefault(kind, []).append(kms)
+    out_ms = statistics.mean(by_kind["output"])
+    bytes_alg = algorithmic_bytes(wl)
+    achieved = bytes_alg / (out_ms * 1e-3) / 1e9
+    flops = algorithmic_flops(wl, chunk)
+
+    traffic = None
+    c = read_counters(args.workload)
+    if c and "fetch_factor" in c:
+        m = c["median_per_dispatch_KiB"]
+        f, w = m.get("output:FETCH_SIZE"), m.get("output:WRITE_SIZE")
+        if f is not None and w is not None:
+            traffic = int(f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"])
+
+    res = {
+        "metric": METRIC,
+        "value": wl.B * wl.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.D, "V": wl.D,
+                   "chunk": chunk, "h_final": wl.want_final, "h0": wl.h0_std is not None,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "output pass (chunk_kernel<BF16,128,64,MODE_OUT>)",
+                     "kernel_ms": out_ms},
+        "whole_path": {"hbm_frac": bytes_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+                       "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                       "algorithmic_bytes": bytes_alg, "algorithmic_flops": flops},
+        "kernels_ms": {k: statistics.mean(v) for k, v in by_kind.items()},
+        "latency_ms": {"mean": ms, "p50": statistics.median(per_step),
+                       "p95": sorted(per_step)[min(len(per_step) - 1, int(0.95 * len(per_step)))],
+                       "p99": sorted(per_step)[min(len(per_step) - 1, int(0.99 * len(per_step)))]},
+    }
+    if wl.name in PAGES_TOKENS_PER_S:
+        res["vs_baseline"] = res["value"] / PAGES_TOKENS_PER_S[wl.name]
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, host)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,6 +16,8 @@ from ._binding import (  # noqa: F401
     gla_stage_intra,
     gla_stage_states,
     load_library,
+    profile_start,
+    profile_stop,
     release,
     set_tuning,
     strerror,

@@ -24,7 +24,13 @@ ERRORS = {
 
 # every symbol include/gla.h and include/gla_stages.h declare
 EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_version",
-            "gla_release", "gla_stage_cumsum", "gla_stage_intra", "gla_stage_states")
+            "gla_release", "gla_profile_start", "gla_profile_stop", "gla_stage_cumsum",
+            "gla_stage_intra", "gla_stage_states")
+KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other"}
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("ms", ctypes.c_float)]
 
 
 class GLALibraryMissing(RuntimeError):
@@ -62,6 +68,10 @@ def load_library(path: str = LIB_PATH):
     lib.gla_version.argtypes = []
     lib.gla_release.argtypes = []
     lib.gla_release.restype = None
+    lib.gla_profile_start.argtypes = [I]
+    lib.gla_profile_stop.argtypes = [ctypes.POINTER(_KernelTime), I, ctypes.POINTER(I)]
+    lib.gla_profile_start.restype = ctypes.c_int
+    lib.gla_profile_stop.restype = ctypes.c_int
     for name in ("gla_fwd", "gla_fwd_f32", "gla_stage_states", "gla_stage_cumsum",
                  "gla_stage_intra", "gla_set_tuning", "gla_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -178,6 +188,20 @@ def gla_stage_intra(q, k, g, *, chunk=64, scale=None, stream=None):
 
 def set_tuning(target_wgs: int = 0, head_group: int = 0):
     _check(load_library().gla_set_tuning(int(target_wgs), int(head_group)))
+
+
+def profile_start(capacity: int):
+    """Start tracing launches (HIP events around each kernel on its stream)."""
+    _check(load_library().gla_profile_start(int(capacity)))
+
+
+def profile_stop():
+    """Stop tracing; returns [(kind_name, ms), ...] in launch order."""
+    lib = load_library()
+    buf = (_KernelTime * 65536)()
+    n = ctypes.c_int(0)
+    _check(lib.gla_profile_stop(buf, 65536, ctypes.byref(n)))
+    return [(KERNEL_KINDS.get(buf[i].kind, "other"), float(buf[i].ms)) for i in range(n.value)]
 
 
 def version() -> int:

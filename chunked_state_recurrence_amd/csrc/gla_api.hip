@@ -29,6 +29,33 @@ std::vector<DeviceState> g_dev;
 int g_target_wgs = kDefaultTargetWgs;
 int g_head_group = 0;
 
+// launch tracing (gla_profile_start / gla_profile_stop)
+struct Trace {
+    bool active = false;
+    int capacity = 0;
+    int used = 0;
+    std::vector<hipEvent_t> ev;   // 2 per launch
+    std::vector<int> kind;
+};
+Trace g_trace;
+
+// Run `launch` bracketed by trace events when tracing is active.
+template <typename F>
+hipError_t traced(int kind, hipStream_t s, F &&launch) {
+    int slot = -1;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (g_trace.active && g_trace.used < g_trace.capacity) slot = g_trace.used++;
+    }
+    if (slot >= 0) {
+        g_trace.kind[slot] = kind;
+        (void)hipEventRecord(g_trace.ev[2 * slot], s);
+    }
+    const hipError_t e = launch();
+    if (slot >= 0) (void)hipEventRecord(g_trace.ev[2 * slot + 1], s);
+    return e;
+}
+
 int current_device(DeviceState **out) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GLA_ERR_DEVICE;
@@ -139,7 +166,9 @@ int run_forward(Call &c) {
     const int D = c.K;
     const long BH = long(c.B) * c.H;
     if (c.T == 0) {
-        if (c.h_final && gla::launch_copy_state(c.h_final, c.h0, BH * D * D, c.stream) != hipSuccess)
+        if (c.h_final && traced(GLA_KERNEL_OTHER, c.stream, [&] {
+                return gla::launch_copy_state(c.h_final, c.h0, BH * D * D, c.stream);
+            }) != hipSuccess)
             return GLA_ERR_LAUNCH;
         return GLA_OK;
     }
@@ -174,12 +203,18 @@ int run_forward(Call &c) {
         p.dump = c.states; p.dump2 = nullptr;
         p.T = c.T; p.N = N; p.cps = pl.cps; p.P = pl.P; p.bh0 = g0; p.scale = c.scale;
         if (pl.P > 1) {
-            if (gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_SEG, p, pl.P - 1, nbh, c.stream) != hipSuccess)
+            if (traced(GLA_KERNEL_SEGMENT, c.stream, [&] {
+                    return gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_SEG, p, pl.P - 1, nbh, c.stream);
+                }) != hipSuccess)
                 return GLA_ERR_LAUNCH;
-            if (gla::launch_scan(p.ws_E, p.ws_G, c.h0, g0, nbh, pl.P, D, c.stream) != hipSuccess)
+            if (traced(GLA_KERNEL_SCAN, c.stream, [&] {
+                    return gla::launch_scan(p.ws_E, p.ws_G, c.h0, g0, nbh, pl.P, D, c.stream);
+                }) != hipSuccess)
                 return GLA_ERR_LAUNCH;
         }
-        if (gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_OUT, p, pl.P, nbh, c.stream) != hipSuccess)
+        if (traced(GLA_KERNEL_OUTPUT, c.stream, [&] {
+                return gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_OUT, p, pl.P, nbh, c.stream);
+            }) != hipSuccess)
             return GLA_ERR_LAUNCH;
     }
     return GLA_OK;
@@ -241,7 +276,9 @@ static int run_stage(int mode, const void *q, const void *k, const float *g, flo
     for (long g0 = 0; g0 < BH; g0 += 65535) {
         p.bh0 = g0;
         const int nbh = int(std::min<long>(65535, BH - g0));
-        if (gla::launch_chunk_kernel(c.dtype, K, c.chunk, mode, p, N, nbh, c.stream) != hipSuccess)
+        if (traced(GLA_KERNEL_OTHER, c.stream, [&] {
+                return gla::launch_chunk_kernel(c.dtype, K, c.chunk, mode, p, N, nbh, c.stream);
+            }) != hipSuccess)
             return GLA_ERR_LAUNCH;
     }
     return GLA_OK;
@@ -262,6 +299,50 @@ int gla_set_tuning(int target_wgs, int head_group) {
     std::lock_guard<std::mutex> lk(g_mu);
     g_target_wgs = target_wgs > 0 ? target_wgs : kDefaultTargetWgs;
     g_head_group = head_group;
+    return GLA_OK;
+}
+
+static void trace_clear() {
+    for (hipEvent_t e : g_trace.ev)
+        if (e) (void)hipEventDestroy(e);
+    g_trace = Trace{};
+}
+
+int gla_profile_start(int capacity) {
+    if (capacity < 0) return GLA_ERR_SHAPE;
+    std::lock_guard<std::mutex> lk(g_mu);
+    trace_clear();
+    g_trace.ev.assign(2 * size_t(capacity), nullptr);
+    g_trace.kind.assign(size_t(capacity), GLA_KERNEL_OTHER);
+    for (hipEvent_t &e : g_trace.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            (void)hipGetLastError();
+            trace_clear();
+            return GLA_ERR_ALLOC;
+        }
+    }
+    g_trace.capacity = capacity;
+    g_trace.active = true;
+    return GLA_OK;
+}
+
+int gla_profile_stop(gla_kernel_time *out, int max, int *count) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_trace.active = false;
+    const int n = g_trace.used;
+    if (n > 0 && (!out || !count)) {
+        trace_clear();
+        return GLA_ERR_NULL;
+    }
+    int written = 0;
+    for (int i = 0; i < n && i < max; ++i) {
+        float ms = -1.f;
+        if (hipEventSynchronize(g_trace.ev[2 * i + 1]) == hipSuccess)
+            (void)hipEventElapsedTime(&ms, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]);
+        out[written++] = gla_kernel_time{g_trace.kind[i], ms};
+    }
+    if (count) *count = written;
+    trace_clear();
     return GLA_OK;
 }
 

@@ -143,21 +143,47 @@ template <> struct Raw<BF16, 2> {
     uint32_t x;
     __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
     __device__ float get(int u) const { return __uint_as_float(u ? (x & 0xffff0000u) : (x << 16)); }
+    // column u of 8 consecutive rows, as a bf16 fragment (byte permutes, no conversion)
+    __device__ static bf16x8_t col8(const Raw *r, int u) {
+        u32x4_t w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = __builtin_amdgcn_perm(r[2 * j + 1].x, r[2 * j].x, u ? 0x07060302u : 0x05040100u);
+        return __builtin_bit_cast(bf16x8_t, w);
+    }
 };
 template <> struct Raw<BF16, 1> {
     uint16_t x;
     __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
     __device__ float get(int) const { return __uint_as_float(uint32_t(x) << 16); }
+    __device__ static bf16x8_t col8(const Raw *r, int) {
+        u32x4_t w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = uint32_t(r[2 * j].x) | (uint32_t(r[2 * j + 1].x) << 16);
+        return __builtin_bit_cast(bf16x8_t, w);
+    }
 };
 template <> struct Raw<F32, 2> {
     u32x2_t x;
     __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
     __device__ float get(int u) const { return __uint_as_float(u ? x.y : x.x); }
+    __device__ static f32x8_t col8(const Raw *r, int u) {
+        f32x8_t f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = r[j].get(u);
+        return f;
+    }
 };
 template <> struct Raw<F32, 1> {
     uint32_t x;
     __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
     __device__ float get(int) const { return __uint_as_float(x); }
+    __device__ static f32x8_t col8(const Raw *r, int) {
+        f32x8_t f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = r[j].get(0);
+        return f;
+    }
 };
 template <int CPL> struct RawG;
 template <> struct RawG<2> {
@@ -210,6 +236,14 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Two ways to form a chunk's scores and operands, chosen per chunk (the
+// choice is uniform over the work-group: every wave sees the chunk totals):
+//  * fast: one reference point at the chunk start, q exp(Gc) and k exp(-Gc),
+//    when every key dim decays by at most 2^kSpanGuard over the chunk; the
+//    score tiles are then plain MFMA products.
+//  * guarded: one reference point per 16-row block (all off-diagonal factors
+//    <= 1), with exact elementwise diagonal blocks where a block's span
+//    exceeds 2^kSpanGuard.
 template <typename E, int D, int C, int MODE>
 __global__ void __launch_bounds__(C / 16 * 64)
 chunk_kernel(const KernelParams p) {
@@ -220,6 +254,7 @@ chunk_kernel(const KernelParams p) {
     constexpr int MT = D / 16;     // 16-row key tiles of S
     constexpr int KS = D / 32;     // 32-deep key steps
     constexpr int TS = C / 32;     // 32-deep token steps
+    constexpr int NTILE = NW * (NW + 1) / 2;   // causal 16x16 score tiles
     static_assert(NTW >= 1 && TS >= 1 && CPL >= 1, "unsupported tile shape");
     constexpr bool kOut = MODE == MODE_OUT;
     constexpr bool kSeg = MODE == MODE_SEG;
@@ -230,14 +265,15 @@ chunk_kernel(const KernelParams p) {
     using L = Layout<E, D, C>;
     using lds_t = typename E::lds_t;
     using gmem_t = typename E::gmem_t;
+    using frag_t = typename E::frag_t;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
-    lds_t *sQb = reinterpret_cast<lds_t *>(smem + L::qb);
-    lds_t *sQh = reinterpret_cast<lds_t *>(smem + L::qh);
-    lds_t *sKb = reinterpret_cast<lds_t *>(smem + L::kb);
-    lds_t *sKht = reinterpret_cast<lds_t *>(smem + L::kht);
-    lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);
-    lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);
+    lds_t *sQb = reinterpret_cast<lds_t *>(smem + L::qb);   // guarded: q, block-start reference
+    lds_t *sQh = reinterpret_cast<lds_t *>(smem + L::qh);   // scale q exp(Gc)
+    lds_t *sKb = reinterpret_cast<lds_t *>(smem + L::kb);   // fast: k exp(-Gc); guarded: block-end reference
+    lds_t *sKht = reinterpret_cast<lds_t *>(smem + L::kht); // (k exp(Gamma - Gc))^T
+    lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);   // v^T
+    lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);     // scaled scores, row-major
     float *sBtot = reinterpret_cast<float *>(smem + L::btot);
     float *sBb = reinterpret_cast<float *>(smem + L::bb);
     float *sEG = reinterpret_cast<float *>(smem + L::eg);
@@ -276,7 +312,7 @@ chunk_kernel(const KernelParams p) {
                 for (int e = 0; e < 4; ++e)
                     S[mt][nt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] : 0.f;
     }
-    if constexpr (kOut) {  // blocks above the diagonal of A are never written: zero them once
+    if constexpr (kOut) {  // tiles above the diagonal of A are never written: zero them once
         for (int i = tid; i < C * L::TP; i += NW * 64) sA[i] = E::f2l(0.f);
     }
     float seg_gamma[CPL];
@@ -304,38 +340,66 @@ chunk_kernel(const KernelParams p) {
     };
     if (c_begin < c_end) load_chunk(c_begin);
 
+    // 16 consecutive tokens of column `col` into a transposed tile (2 fragments)
+    auto store_col16 = [&](lds_t *tile, int col, const float *x16) {
+        E::st_frag(tile + col * L::TP + 16 * w, E::pack(x16));
+        E::st_frag(tile + col * L::TP + 16 * w + 8, E::pack(x16 + 8));
+    };
+    auto store_v_cols = [&]() {
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+            const int col = lane * CPL + u;
+            E::st_frag(sVt + col * L::TP + 16 * w, Raw<E, CPL>::col8(rv, u));
+            E::st_frag(sVt + col * L::TP + 16 * w + 8, Raw<E, CPL>::col8(rv + 8, u));
+        }
+    };
+    auto store_row_pair = [&](lds_t *tile, int row, const float *x) {
+        const int pc = perm_col(lane * CPL);
+        if constexpr (CPL == 2) {
+            typedef lds_t l2_t __attribute__((ext_vector_type(2)));
+            l2_t a;
+            a[0] = E::f2l(x[0]);
+            a[1] = E::f2l(x[1]);
+            *reinterpret_cast<l2_t *>(tile + row * L::QP + pc) = a;
+        } else {
+            tile[row * L::QP + pc] = E::f2l(x[0]);
+        }
+    };
+    auto sink_tile = [&](int c, int I, int J, f32x4_t acc) {
+        // acc[e] = A[16I + n16][16J + 4q4 + e]
+        if constexpr (kOut) {
+            typedef lds_t l4_t __attribute__((ext_vector_type(4)));
+            l4_t v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = E::f2l(acc[e]);
+            *reinterpret_cast<l4_t *>(sA + (16 * I + n16) * L::TP + 16 * J + 4 * q4) = v4;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                p.dump[((bh * long(p.N) + c) * C + 16 * I + n16) * C + 16 * J + 4 * q4 + e] = acc[e];
+        }
+    };
+
     int buf = 0;
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
         // ---- a1: gate cumsum (log2 units) inside this wave's 16-row block.
-        // Every exponent below is a direct sum of gates of one sign (a prefix,
-        // a suffix or a run of block totals), never a difference of two
-        // prefix sums: that keeps huge gates from cancelling into O(1)
-        // exponent errors.
+        // Every exponent formed below is a sum of gates of one sign (a prefix,
+        // a suffix, a run of block totals), never a difference of two prefix
+        // sums, so huge gates cannot cancel into large exponent errors.
         float Pf[16][CPL];   // inclusive prefix within the block
-        float Sf[16][CPL];   // exclusive suffix within the block
         float Bw[CPL];
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
             float run = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                run += rg[i].get(u) * kLog2e;
+                run = __builtin_fmaf(rg[i].get(u), kLog2e, run);
                 Pf[i][u] = run;
             }
             Bw[u] = run;
-            float suf = 0.f;
-#pragma unroll
-            for (int i = 15; i >= 0; --i) {
-                Sf[i][u] = suf;
-                suf += rg[i].get(u) * kLog2e;
-            }
             sBtot[(buf * NW + w) * D + lane * CPL + u] = run;
         }
-        float span = 0.f;
-#pragma unroll
-        for (int u = 0; u < CPL; ++u) span = fmaxf(span, -Bw[u]);
-        span = wave_max(span);
         __syncthreads();  // B1: block totals visible
 
         float rw[CPL], aw[CPL], gam[CPL];   // blocks before w, after w, all
@@ -372,118 +436,132 @@ chunk_kernel(const KernelParams p) {
             continue;
         }
 
+        // chunk span, identical in every wave (each wave holds all columns)
+        float cspan = 0.f;
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) cspan = fmaxf(cspan, -gam[u]);
+        cspan = wave_max(cspan);
+        const bool fast = cspan <= kSpanGuard;
+        float bspan = 0.f;   // this wave's block span (guarded path)
+
         // ---- operand tiles into LDS -----------------------------------------
         if constexpr (kScores) {
-            float ew[CPL], xk[CPL];
+            float eg[CPL];
 #pragma unroll
             for (int u = 0; u < CPL; ++u) {
-                ew[u] = fexp2(rw[u]);    // chunk start -> block start   <= 1
-                xk[u] = fexp2(aw[u]);    // block end   -> chunk end     <= 1
-                const int col = lane * CPL + u;
-                sBb[w * D + perm_col(col)] = Bw[u];
-                if constexpr (kOut) if (w == 0) sEG[col] = fexp2(gam[u]);
+                eg[u] = fexp2(gam[u]);
+                if constexpr (kOut) if (w == 0) sEG[lane * CPL + u] = eg[u];
             }
-            float khv[16][CPL];
+            if (fast) {
+                float kh[CPL][16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float qb[CPL], qh[CPL], kb[CPL];
-#pragma unroll
-                for (int u = 0; u < CPL; ++u) {
-                    const float eq = fexp2(Pf[i][u]);    // block start -> row i   <= 1
-                    const float ek = fexp2(Sf[i][u]);    // row i -> block end     <= 1
-                    qb[u] = p.scale * rq[i].get(u) * eq;
-                    qh[u] = qb[u] * ew[u];               // scale q exp(Gc_i)
-                    kb[u] = rk[i].get(u) * ek;
-                    khv[i][u] = kb[u] * xk[u];           // k exp(Gamma - Gc_i)
-                }
-                const int row = 16 * w + i;
-                const int pc = perm_col(lane * CPL);
-                if constexpr (CPL == 2) {
-                    typedef typename E::lds_t l2_t __attribute__((ext_vector_type(2)));
-                    l2_t a, b, d;
-                    a[0] = E::f2l(qb[0]); a[1] = E::f2l(qb[1]);
-                    b[0] = E::f2l(qh[0]); b[1] = E::f2l(qh[1]);
-                    d[0] = E::f2l(kb[0]); d[1] = E::f2l(kb[1]);
-                    *reinterpret_cast<l2_t *>(sQb + row * L::QP + pc) = a;
-                    *reinterpret_cast<l2_t *>(sQh + row * L::QP + pc) = b;
-                    *reinterpret_cast<l2_t *>(sKb + row * L::QP + pc) = d;
-                } else {
-                    sQb[row * L::QP + pc] = E::f2l(qb[0]);
-                    sQh[row * L::QP + pc] = E::f2l(qh[0]);
-                    sKb[row * L::QP + pc] = E::f2l(kb[0]);
-                }
-            }
-            if constexpr (kOut) {
-                // transposed: Kht[d][token], Vt[v][token]; 16 consecutive tokens per column
-#pragma unroll
-                for (int u = 0; u < CPL; ++u) {
-                    const int col = lane * CPL + u;
-                    float kk[16], vv[16];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) { kk[i] = khv[i][u]; vv[i] = rv[i].get(u); }
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        E::st_frag(sKht + col * L::TP + 16 * w + 8 * h, E::pack(kk + 8 * h));
-                        E::st_frag(sVt + col * L::TP + 16 * w + 8 * h, E::pack(vv + 8 * h));
-                    }
-                }
-            }
-            // diagonal block with a large gate span: exact elementwise scores,
-            // A[i][j] = scale sum_d q_i k_j exp(g_{j+1} + ... + g_i)
-            if (span > kSpanGuard) {
-#pragma unroll 1
                 for (int i = 0; i < 16; ++i) {
-                    float qi[CPL], ex[CPL];
+                    float qh[CPL], kt[CPL];
 #pragma unroll
                     for (int u = 0; u < CPL; ++u) {
-                        qi[u] = 0.f;
-                        ex[u] = 0.f;
-#pragma unroll
-                        for (int x = 0; x < 16; ++x)
-                            if (x == i) qi[u] = rq[x].get(u);
+                        const float t = rw[u] + Pf[i][u];                   // Gc_i, in [-kSpanGuard, 0]
+                        qh[u] = rq[i].get(u) * (p.scale * fexp2(t));          // scale q exp(Gc)
+                        kt[u] = rk[i].get(u) * fexp2(-t);                     // k exp(-Gc)
+                        kh[u][i] = kt[u] * eg[u];                             // k exp(Gamma - Gc)
                     }
-                    for (int j = i; j >= 0; --j) {
-                        float part = 0.f;
+                    store_row_pair(sQh, 16 * w + i, qh);
+                    store_row_pair(sKb, 16 * w + i, kt);
+                }
+                if constexpr (kOut) {
+#pragma unroll
+                    for (int u = 0; u < CPL; ++u) store_col16(sKht, lane * CPL + u, kh[u]);
+                }
+            } else {
+                float Sf[16][CPL];   // exclusive suffix within the block
+                float ew[CPL], xk[CPL];
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) {
+                    float suf = 0.f;
+#pragma unroll
+                    for (int i = 15; i >= 0; --i) {
+                        Sf[i][u] = suf;
+                        suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
+                    }
+                    ew[u] = fexp2(rw[u]);    // chunk start -> block start   <= 1
+                    xk[u] = fexp2(aw[u]);    // block end   -> chunk end     <= 1
+                    sBb[w * D + perm_col(lane * CPL + u)] = Bw[u];
+                    bspan = fmaxf(bspan, -Bw[u]);
+                }
+                bspan = wave_max(bspan);
+                float kh[CPL][16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float qb[CPL], qh[CPL], kb[CPL];
+#pragma unroll
+                    for (int u = 0; u < CPL; ++u) {
+                        qb[u] = p.scale * rq[i].get(u) * fexp2(Pf[i][u]);  // block start -> row i
+                        qh[u] = qb[u] * ew[u];
+                        kb[u] = rk[i].get(u) * fexp2(Sf[i][u]);            // row i -> block end
+                        kh[u][i] = kb[u] * xk[u];
+                    }
+                    store_row_pair(sQb, 16 * w + i, qb);
+                    store_row_pair(sQh, 16 * w + i, qh);
+                    store_row_pair(sKb, 16 * w + i, kb);
+                }
+                if constexpr (kOut) {
+#pragma unroll
+                    for (int u = 0; u < CPL; ++u) store_col16(sKht, lane * CPL + u, kh[u]);
+                }
+                // diagonal block with a large span: exact elementwise scores,
+                // A[i][j] = scale sum_d q_i k_j exp(g_{j+1} + ... + g_i)
+                if (bspan > kSpanGuard) {
+#pragma unroll 1
+                    for (int i = 0; i < 16; ++i) {
+                        float qi[CPL], ex[CPL];
 #pragma unroll
                         for (int u = 0; u < CPL; ++u) {
-                            // rows live in registers: select row j
-                            float kj = 0.f, gj = 0.f;
+                            qi[u] = 0.f;
+                            ex[u] = 0.f;
 #pragma unroll
                             for (int x = 0; x < 16; ++x)
-                                if (x == j) { kj = rk[x].get(u); gj = rg[x].get(u) * kLog2e; }
-                            part += qi[u] * kj * fexp2(ex[u]);
-                            ex[u] += gj;   // exponent for j-1: g_j + ... + g_i
+                                if (x == i) qi[u] = rq[x].get(u);
                         }
-                        const float s = wave_sum(part) * p.scale;
-                        if (lane == 0) {
-                            if constexpr (kOut) sA[(16 * w + i) * L::TP + 16 * w + j] = E::f2l(s);
-                            else p.dump[((bh * long(p.N) + c) * C + 16 * w + i) * C + 16 * w + j] = s;
+                        for (int j = i; j >= 0; --j) {
+                            float part = 0.f;
+#pragma unroll
+                            for (int u = 0; u < CPL; ++u) {
+                                float kj = 0.f, gj = 0.f;   // select register row j
+#pragma unroll
+                                for (int x = 0; x < 16; ++x)
+                                    if (x == j) { kj = rk[x].get(u); gj = rg[x].get(u) * kLog2e; }
+                                part += qi[u] * kj * fexp2(ex[u]);
+                                ex[u] += gj;   // exponent for j-1: g_j + ... + g_i
+                            }
+                            const float s = wave_sum(part) * p.scale;
+                            if (lane == 0) {
+                                if constexpr (kOut) sA[(16 * w + i) * L::TP + 16 * w + j] = E::f2l(s);
+                                else p.dump[((bh * long(p.N) + c) * C + 16 * w + i) * C + 16 * w + j] = s;
+                            }
                         }
-                    }
-                    if constexpr (kIntra) {  // zeros above the diagonal of this block
-                        if (lane < 16 && lane > i)
-                            p.dump[((bh * long(p.N) + c) * C + 16 * w + i) * C + 16 * w + lane] = 0.f;
+                        if constexpr (kIntra) {  // zeros above the diagonal of this block
+                            if (lane < 16 && lane > i)
+                                p.dump[((bh * long(p.N) + c) * C + 16 * w + i) * C + 16 * w + lane] = 0.f;
+                        }
                     }
                 }
             }
+            if constexpr (kOut) store_v_cols();
         }
         if constexpr (kSeg) {
 #pragma unroll
             for (int u = 0; u < CPL; ++u) {
                 const int col = lane * CPL + u;
                 if (w == 0) sEG[col] = fexp2(gam[u]);
-                float kk[16], vv[16];
+                float kk[16];
+                float suf = aw[u];   // blocks after w, then rows after i: exponent <= 0
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    kk[i] = rk[i].get(u) * fexp2(Sf[i][u] + aw[u]);  // k exp(Gamma - Gc_i)
-                    vv[i] = rv[i].get(u);
+                for (int i = 15; i >= 0; --i) {
+                    kk[i] = rk[i].get(u) * fexp2(suf);     // k exp(Gamma - Gc_i)
+                    suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
                 }
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    E::st_frag(sKht + col * L::TP + 16 * w + 8 * h, E::pack(kk + 8 * h));
-                    E::st_frag(sVt + col * L::TP + 16 * w + 8 * h, E::pack(vv + 8 * h));
-                }
+                store_col16(sKht, col, kk);
             }
+            store_v_cols();
         }
 #pragma unroll
         for (int u = 0; u < CPL; ++u) seg_gamma[u] += gam[u];
@@ -492,72 +570,85 @@ chunk_kernel(const KernelParams p) {
         if (c + 1 < c_end) load_chunk(c + 1);
         __syncthreads();  // B2: operand tiles visible
 
-        // ---- a2: scores of row block I = w, column blocks J <= I --------------
-        // Tile (I, J) = Kb[J] Qb[I]^T with the k side moved from the end of
-        // block J to the start of block I: factor exp(B_{J+1} + ... + B_{I-1})
-        // (<= 1); on the diagonal the factor is exp(-B_I) (<= 2^kSpanGuard).
+        // ---- a2: causal score tiles -------------------------------------------
         if constexpr (kScores) {
-            const int I = w;
+            if (fast) {
+                // tile (I, J) = Kt[J] Qh[I]^T; tiles dealt round-robin to the waves
 #pragma unroll
-            for (int J = 0; J < NW; ++J) {
-                if (J > I) {
-                    if constexpr (kIntra) {  // zero tile above the diagonal
+                for (int t = 0; t < NTILE; ++t) {
+                    if (t % NW != w) continue;
+                    int I = 0, J = t;
+#pragma unroll
+                    for (int r = 0; r < NW; ++r)
+                        if (J > r) { J -= r + 1; I = r + 1; }
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int pos = ks * 32 + 8 * q4;
+                        acc = E::mma(E::ld_frag(sKb + (16 * J + n16) * L::QP + pos),
+                                     E::ld_frag(sQh + (16 * I + n16) * L::QP + pos), acc);
+                    }
+                    if (I == J) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            p.dump[((bh * long(p.N) + c) * C + 16 * I + n16) * C + 16 * J + 4 * q4 + e] = 0.f;
+                            if (4 * q4 + e > n16) acc[e] = 0.f;
                     }
-                    continue;
+                    sink_tile(c, I, J, acc);
                 }
-                if (J == I && span > kSpanGuard) continue;  // formed elementwise above
-                const bool rescale = (J < I - 1) || (J == I);
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            } else {
+                // row block I = w: tile (I, J) = Kb[J] Qb[I]^T with the k side
+                // moved from the end of block J to the start of block I, factor
+                // exp(B_{J+1} + ... + B_{I-1}) (<= 1); on the diagonal exp(-B_I)
+                const int I = w;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int pos = ks * 32 + 8 * q4;
-                    typename E::frag_t a = E::ld_frag(sKb + (16 * J + n16) * L::QP + pos);
-                    if (rescale) {
-                        float x[8], ex[8];
+                for (int J = 0; J < NW; ++J) {
+                    if (J > I) continue;
+                    if (J == I && bspan > kSpanGuard) continue;  // formed elementwise
+                    const bool rescale = (J < I - 1) || (J == I);
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) ex[e] = 0.f;
-                        if (J == I) {
-                            const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sBb + I * D + pos);
-                            const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sBb + I * D + pos + 4);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int pos = ks * 32 + 8 * q4;
+                        frag_t a = E::ld_frag(sKb + (16 * J + n16) * L::QP + pos);
+                        if (rescale) {
+                            float x[8], ex[8];
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) { ex[e] = -b0[e]; ex[4 + e] = -b1[e]; }
-                        } else {
+                            for (int e = 0; e < 8; ++e) ex[e] = 0.f;
+                            if (J == I) {
+                                const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sBb + I * D + pos);
+                                const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sBb + I * D + pos + 4);
 #pragma unroll
-                            for (int j = 0; j < NW; ++j) {
-                                if (j <= J || j >= I) continue;
-                                const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sBb + j * D + pos);
-                                const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sBb + j * D + pos + 4);
+                                for (int e = 0; e < 4; ++e) { ex[e] = -b0[e]; ex[4 + e] = -b1[e]; }
+                            } else {
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) { ex[e] += b0[e]; ex[4 + e] += b1[e]; }
+                                for (int j = 0; j < NW; ++j) {
+                                    if (j <= J || j >= I) continue;
+                                    const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sBb + j * D + pos);
+                                    const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sBb + j * D + pos + 4);
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) { ex[e] += b0[e]; ex[4 + e] += b1[e]; }
+                                }
                             }
+                            E::unpack(a, x);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x[e] *= fexp2(ex[e]);
+                            a = E::pack(x);
                         }
-                        E::unpack(a, x);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) x[e] *= fexp2(ex[e]);
-                        a = E::pack(x);
+                        acc = E::mma(a, E::ld_frag(sQb + (16 * I + n16) * L::QP + pos), acc);
                     }
-                    const typename E::frag_t b = E::ld_frag(sQb + (16 * I + n16) * L::QP + pos);
-                    acc = E::mma(a, b, acc);
+                    if (J == I) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q4 + e > n16) acc[e] = 0.f;
+                    }
+                    sink_tile(c, I, J, acc);
                 }
-                // acc[e] = A[16I + n16][16J + 4q4 + e]
-                if (J == I) {
+            }
+            if constexpr (kIntra) {  // zero tiles above the diagonal of row block w
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * q4 + e > n16) acc[e] = 0.f;
-                }
-                if constexpr (kOut) {
-                    typedef typename E::lds_t l4_t __attribute__((ext_vector_type(4)));
-                    l4_t v4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v4[e] = E::f2l(acc[e]);
-                    *reinterpret_cast<l4_t *>(sA + (16 * I + n16) * L::TP + 16 * J + 4 * q4) = v4;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        p.dump[((bh * long(p.N) + c) * C + 16 * I + n16) * C + 16 * J + 4 * q4 + e] = acc[e];
+                for (int J = 0; J < NW; ++J) {
+                    if (J <= w) continue;
+                    sink_tile(c, w, J, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 }
             }
         }
@@ -567,7 +658,7 @@ chunk_kernel(const KernelParams p) {
             continue;
         }
 
-        typename E::frag_t vf[NTW][TS];
+        frag_t vf[NTW][TS];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
@@ -592,11 +683,11 @@ chunk_kernel(const KernelParams p) {
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                 for (int m = 0; m < NW; ++m) O[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            // inter-chunk: O^T += S^T (q exp Gc)^T, S straight from its accumulators
+            // inter-chunk: O^T += S^T (scale q exp Gc)^T, S straight from its accumulators
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 __builtin_amdgcn_sched_barrier(0);  // bound the fragment loads in flight
-                typename E::frag_t sf[NTW];
+                frag_t sf[NTW];
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     float x[8];
@@ -606,7 +697,7 @@ chunk_kernel(const KernelParams p) {
                 }
 #pragma unroll
                 for (int m = 0; m < NW; ++m) {
-                    const typename E::frag_t b = E::ld_frag(sQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
+                    const frag_t b = E::ld_frag(sQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) O[nt][m] = E::mma(sf[nt], b, O[nt][m]);
                 }
@@ -618,7 +709,7 @@ chunk_kernel(const KernelParams p) {
 #pragma unroll
                 for (int ts = 0; ts < TS; ++ts) {
                     if (ts * 32 > 16 * m + 15) continue;
-                    const typename E::frag_t b = E::ld_frag(sA + (16 * m + n16) * L::TP + ts * 32 + 8 * q4);
+                    const frag_t b = E::ld_frag(sA + (16 * m + n16) * L::TP + ts * 32 + 8 * q4);
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) O[nt][m] = E::mma(vf[nt][ts], b, O[nt][m]);
                 }
@@ -636,18 +727,18 @@ chunk_kernel(const KernelParams p) {
         // ---- a3: S <- diag(exp2 Gamma) S + Kht^T V ------------------------------
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const f32x4_t eg = *reinterpret_cast<const f32x4_t *>(sEG + 16 * mt + 4 * q4);
+            const f32x4_t egv = *reinterpret_cast<const f32x4_t *>(sEG + 16 * mt + 4 * q4);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[mt][nt][e] *= eg[e];
+                for (int e = 0; e < 4; ++e) S[mt][nt][e] *= egv[e];
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             if ((mt & 1) == 0) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ts = 0; ts < TS; ++ts) {
-                const typename E::frag_t a = E::ld_frag(sKht + (16 * mt + n16) * L::TP + ts * 32 + 8 * q4);
+                const frag_t a = E::ld_frag(sKht + (16 * mt + n16) * L::TP + ts * 32 + 8 * q4);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) S[mt][nt] = E::mma(a, vf[nt][ts], S[mt][nt]);
             }

@@ -97,6 +97,32 @@ int gla_fwd_f32(const float *q, const float *k, const float *v,
  */
 int gla_set_tuning(int target_wgs, int head_group);
 
+/*
+ * Launch tracing.  Between gla_profile_start and gla_profile_stop every
+ * kernel the library enqueues is bracketed by two HIP events recorded on
+ * the launch stream, so its device duration can be read back.  Kinds:
+ * GLA_KERNEL_OUTPUT (the fused chunk pass that writes o), GLA_KERNEL_SEGMENT
+ * (segment end states), GLA_KERNEL_SCAN (segment-state scan),
+ * GLA_KERNEL_OTHER.  gla_profile_start(capacity) creates the events
+ * (capacity launches; more are not traced) and returns GLA_OK or
+ * GLA_ERR_ALLOC.  gla_profile_stop waits for the traced work, writes up to
+ * `max` records in launch order to `out`, stores the number written in
+ * *count, destroys the events and returns GLA_OK (GLA_ERR_NULL if out or
+ * count is NULL while records exist).  Not thread-safe with concurrent
+ * gla_fwd calls.
+ */
+#define GLA_KERNEL_OUTPUT  0
+#define GLA_KERNEL_SEGMENT 1
+#define GLA_KERNEL_SCAN    2
+#define GLA_KERNEL_OTHER   3
+typedef struct {
+    int kind;     /* GLA_KERNEL_* */
+    float ms;     /* device time between the bracketing events */
+} gla_kernel_time;
+
+int gla_profile_start(int capacity);
+int gla_profile_stop(gla_kernel_time *out, int max, int *count);
+
 /* Human-readable text for a return code (static storage, never NULL). */
 const char *gla_strerror(int code);
 
