@@ -119,33 +119,34 @@ def read_counters(wl_name: str):
 
 def summarize_counters(outdir: str, wl_name: str):
     """Parse rocprofv3 counter-collection CSVs (one pass for FETCH_SIZE, one
-    for WRITE_SIZE) and write profiles/counters_<workload>.json."""
+    for WRITE_SIZE, each run with --copy-calibration) and write
+    profiles/counters_<workload>.json.  The calibration copies are the device
+    copies dispatched after the last chunk kernel."""
     import csv
-    rows = []
+    per_counter = {}
     for p in glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True):
         with open(p) as f:
-            rows += list(csv.DictReader(f))
-    if not rows:
-        raise SystemExit(f"no *counter_collection.csv under {outdir}")
-    acc = {}
-    for r in rows:
-        name = r.get("Kernel_Name", "")
-        ctr = r.get("Counter_Name", "")
-        val = float(r.get("Counter_Value", "nan"))
-        if "chunk_kernel" in name and "ELi0E" in name:
-            kind = "output"
-        elif "chunk_kernel" in name and "ELi1E" in name:
-            kind = "segment"
-        elif "scan_kernel" in name:
-            kind = "scan"
-        elif "copy" in name.lower() or "elementwise" in name.lower():
-            kind = "copy"
-        else:
-            continue
-        acc.setdefault((kind, ctr), []).append(val)
-    summary = {k[0] + ":" + k[1]: statistics.median(v) for k, v in acc.items()}
-    out = {"workload": wl_name, "source_digest": source_digest(), "median_per_dispatch_KiB": summary,
-           "copy_bytes": COPY_BYTES}
+            rows = list(csv.DictReader(f))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        last_chunk = max((int(r["Dispatch_Id"]) for r in rows if "chunk_kernel" in r["Kernel_Name"]),
+                         default=-1)
+        for r in rows:
+            name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            if "chunk_kernel" in name:
+                kind = {"0": "output", "1": "segment"}.get(name.split(",")[3].strip(" >")[:1])
+            elif "scan_kernel" in name:
+                kind = "scan"
+            elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_chunk:
+                kind = "copy"
+            else:
+                kind = None
+            if kind:
+                per_counter.setdefault((kind, ctr), []).append(val)
+    if not per_counter:
+        raise SystemExit(f"no counter rows under {outdir}")
+    summary = {k[0] + ":" + k[1]: statistics.median(v) for k, v in per_counter.items()}
+    out = {"workload": wl_name, "source_digest": source_digest(),
+           "median_per_dispatch_KiB": summary, "copy_bytes": COPY_BYTES}
     cf, cw = summary.get("copy:FETCH_SIZE"), summary.get("copy:WRITE_SIZE")
     if cf and cw:
         out["fetch_factor"] = COPY_BYTES / (cf * 1024.0)

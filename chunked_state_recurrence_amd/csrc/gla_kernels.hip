@@ -22,14 +22,11 @@
 //   launch 3 (MODE_OUT): every segment replays its chunks from S_start(r),
 //                        writing o (and h_final for the last segment).
 //
-// Work-group = C/16 waves; wave w owns rows [16w, 16w+16) of a chunk for the
-// gate cumsum and the exponentials, row block w of the score matrix, and
-// value columns [w*D/(C/16), ...) of the state S and of the output.  S lives
-// in MFMA accumulators for the whole segment.  Exponentials use exp2 with
-// log2-scaled gates.  Within-chunk factors use one reference point per
-// 16-row block, so every exponent but the diagonal blocks' is <= 0; a
-// diagonal block whose gate span exceeds SPAN_GUARD (log2 units) is formed
-// elementwise instead (the blog's intra_sub_inter / intra_sub_intra split).
+// Work-group = NW waves (8 chunk rows each, 16 when the head dim is 64);
+// wave w owns its rows for the gate cumsum and the exponentials, and value
+// columns [w*D/NW, (w+1)*D/NW) of the state S and of the output.  S lives in
+// MFMA accumulators for a whole segment.  Exponentials use exp2 with
+// log2-scaled gates.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -141,7 +138,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, long bytes) {
 template <typename E, int CPL> struct Raw;
 template <> struct Raw<BF16, 2> {
     uint32_t x;
-    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+    __device__ void load(rsrc_t r, int off, int soff) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
     __device__ float get(int u) const { return __uint_as_float(u ? (x & 0xffff0000u) : (x << 16)); }
     // column u of 8 consecutive rows, as a bf16 fragment (byte permutes, no conversion)
     __device__ static bf16x8_t col8(const Raw *r, int u) {
@@ -154,7 +151,7 @@ template <> struct Raw<BF16, 2> {
 };
 template <> struct Raw<BF16, 1> {
     uint16_t x;
-    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+    __device__ void load(rsrc_t r, int off, int soff) { x = __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0); }
     __device__ float get(int) const { return __uint_as_float(uint32_t(x) << 16); }
     __device__ static bf16x8_t col8(const Raw *r, int) {
         u32x4_t w;
@@ -165,7 +162,7 @@ template <> struct Raw<BF16, 1> {
 };
 template <> struct Raw<F32, 2> {
     u32x2_t x;
-    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
+    __device__ void load(rsrc_t r, int off, int soff) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0); }
     __device__ float get(int u) const { return __uint_as_float(u ? x.y : x.x); }
     __device__ static f32x8_t col8(const Raw *r, int u) {
         f32x8_t f;
@@ -176,7 +173,7 @@ template <> struct Raw<F32, 2> {
 };
 template <> struct Raw<F32, 1> {
     uint32_t x;
-    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+    __device__ void load(rsrc_t r, int off, int soff) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
     __device__ float get(int) const { return __uint_as_float(x); }
     __device__ static f32x8_t col8(const Raw *r, int) {
         f32x8_t f;
@@ -188,12 +185,12 @@ template <> struct Raw<F32, 1> {
 template <int CPL> struct RawG;
 template <> struct RawG<2> {
     u32x2_t x;
-    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
+    __device__ void load(rsrc_t r, int off, int soff) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0); }
     __device__ float get(int u) const { return __uint_as_float(u ? x.y : x.x); }
 };
 template <> struct RawG<1> {
     uint32_t x;
-    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+    __device__ void load(rsrc_t r, int off, int soff) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
     __device__ float get(int) const { return __uint_as_float(x); }
 };
 
@@ -207,54 +204,64 @@ __device__ __forceinline__ int perm_col(int c) {
     return blk + (a < 4 ? (a << 3) + e : ((a - 4) << 3) + 4 + e);
 }
 
-// LDS carve-up (bytes).  Pitches pad rows by 16 bytes against bank conflicts.
-template <typename E, int D, int C> struct Layout {
+// Waves per work-group: 8 chunk rows per wave while every wave still owns at
+// least one 16-wide tile of value columns, else 16 rows per wave.
+template <int D, int C> struct Shape {
+    static constexpr int NW = (C / 8 < D / 16) ? C / 8 : D / 16;
+    static constexpr int RPW = C / NW;   // chunk rows per wave (8 or 16)
+    static_assert(RPW == 8 || RPW == 16, "unsupported chunk / head-dim pair");
+};
+
+// LDS carve-up (bytes) per mode; pitches pad rows by 16 bytes against bank
+// conflicts.  Only the tiles a mode uses are allocated, so the state-only
+// pass fits several work-groups per CU.
+template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int es = sizeof(typename E::lds_t);
-    static constexpr int NW = C / 16;
-    static constexpr int QP = D + 16 / es;   // Qb / Qh / Kb row pitch (elements)
+    static constexpr int NW = Shape<D, C>::NW;
+    static constexpr bool scores = MODE == MODE_OUT || MODE == MODE_INTRA;
+    static constexpr bool state = MODE == MODE_OUT || MODE == MODE_SEG;
+    static constexpr int QP = D + 16 / es;   // Qh / Kt row pitch (elements)
     static constexpr int TP = C + 16 / es;   // Kht / Vt / A row pitch (elements)
-    static constexpr int qb = 0;
-    static constexpr int qh = qb + C * QP * es;
-    static constexpr int kb = qh + C * QP * es;
-    static constexpr int kht = kb + C * QP * es;
-    static constexpr int vt = kht + D * TP * es;
-    static constexpr int a = vt + D * TP * es;
-    static constexpr int btot = a + C * TP * es;          // float [2][NW][D]
-    static constexpr int bb = btot + 2 * NW * D * 4;       // float [NW][D] block totals (permuted cols)
-    static constexpr int eg = bb + NW * D * 4;             // float [D]     exp2(Gamma) (natural cols)
+    static constexpr int DP = D + 4;         // decay tile row pitch (floats)
+    static constexpr int qh = 0;
+    static constexpr int kt = qh + (scores ? C * QP * es : 0);
+    static constexpr int kht = kt + (scores ? C * QP * es : 0);
+    static constexpr int vt = kht + (state ? D * TP * es : 0);
+    static constexpr int a = vt + (state ? D * TP * es : 0);
+    static constexpr int dec = a + (MODE == MODE_OUT ? C * TP * es : 0);
+    static constexpr int btot = dec + (scores ? C * DP * 4 : 0);   // float [2][NW][D]
+    static constexpr int eg = btot + 2 * NW * D * 4;              // float [D] exp2(Gamma)
     static constexpr int bytes = eg + D * 4;
 };
 
-template <typename T> __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
 }
 
-// Two ways to form a chunk's scores and operands, chosen per chunk (the
-// choice is uniform over the work-group: every wave sees the chunk totals):
+// Two ways to form a chunk's scores, chosen per chunk (uniformly over the
+// work-group: every wave holds all key dims of the chunk totals):
 //  * fast: one reference point at the chunk start, q exp(Gc) and k exp(-Gc),
 //    when every key dim decays by at most 2^kSpanGuard over the chunk; the
-//    score tiles are then plain MFMA products.
-//  * guarded: one reference point per 16-row block (all off-diagonal factors
-//    <= 1), with exact elementwise diagonal blocks where a block's span
-//    exceeds 2^kSpanGuard.
+//    score tiles are then plain MFMA products;
+//  * exact: otherwise A[i][j] = sum_d q_i k_j prod_{r=j+1..i} exp(g_r) is
+//    formed elementwise from running products of per-token decays (factors
+//    in (0, 1], so nothing overflows and underflow is the true value).
+// Q and the state-update operand are bounded (exponents <= 0) on both paths.
 template <typename E, int D, int C, int MODE>
-__global__ void __launch_bounds__(C / 16 * 64)
+__global__ void __launch_bounds__((Shape<D, C>::NW * 64))
 chunk_kernel(const KernelParams p) {
-    constexpr int NW = C / 16;     // waves == 16-row blocks per chunk
-    constexpr int CPL = D / 64;    // key/value columns per lane in the row mapping
-    constexpr int VS = D / NW;     // value columns per wave
-    constexpr int NTW = VS / 16;   // 16-wide value tiles per wave
-    constexpr int MT = D / 16;     // 16-row key tiles of S
-    constexpr int KS = D / 32;     // 32-deep key steps
-    constexpr int TS = C / 32;     // 32-deep token steps
-    constexpr int NTILE = NW * (NW + 1) / 2;   // causal 16x16 score tiles
+    constexpr int NW = Shape<D, C>::NW;    // waves
+    constexpr int RPW = Shape<D, C>::RPW;  // chunk rows per wave
+    constexpr int NB = C / 16;             // 16-row token tiles per chunk
+    constexpr int CPL = D / 64;            // key/value columns per lane in the row mapping
+    constexpr int VS = D / NW;             // value columns per wave
+    constexpr int NTW = VS / 16;           // 16-wide value tiles per wave
+    constexpr int MT = D / 16;             // 16-row key tiles of S
+    constexpr int KS = D / 32;             // 32-deep key steps
+    constexpr int TS = C / 32;             // 32-deep token steps
+    constexpr int NTILE = NB * (NB + 1) / 2;   // causal 16x16 score tiles
     static_assert(NTW >= 1 && TS >= 1 && CPL >= 1, "unsupported tile shape");
     constexpr bool kOut = MODE == MODE_OUT;
     constexpr bool kSeg = MODE == MODE_SEG;
@@ -262,20 +269,19 @@ chunk_kernel(const KernelParams p) {
     constexpr bool kCumsum = MODE == MODE_CUMSUM;
     constexpr bool kScores = kOut || kIntra;     // needs the score matrix
     constexpr bool kState = kOut || kSeg;        // carries S
-    using L = Layout<E, D, C>;
+    using L = Layout<E, D, C, MODE>;
     using lds_t = typename E::lds_t;
     using gmem_t = typename E::gmem_t;
     using frag_t = typename E::frag_t;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
-    lds_t *sQb = reinterpret_cast<lds_t *>(smem + L::qb);   // guarded: q, block-start reference
-    lds_t *sQh = reinterpret_cast<lds_t *>(smem + L::qh);   // scale q exp(Gc)
-    lds_t *sKb = reinterpret_cast<lds_t *>(smem + L::kb);   // fast: k exp(-Gc); guarded: block-end reference
-    lds_t *sKht = reinterpret_cast<lds_t *>(smem + L::kht); // (k exp(Gamma - Gc))^T
-    lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);   // v^T
-    lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);     // scaled scores, row-major
+    lds_t *sQh = reinterpret_cast<lds_t *>(smem + L::qh);    // scale q exp(Gc), permuted cols
+    lds_t *sKt = reinterpret_cast<lds_t *>(smem + L::kt);    // fast: k exp(-Gc) (permuted); exact: raw k
+    lds_t *sKht = reinterpret_cast<lds_t *>(smem + L::kht);  // (k exp(Gamma - Gc))^T
+    lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);    // v^T
+    lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);      // scaled scores, row-major
+    float *sDec = reinterpret_cast<float *>(smem + L::dec);  // exact path: exp(g) per token
     float *sBtot = reinterpret_cast<float *>(smem + L::btot);
-    float *sBb = reinterpret_cast<float *>(smem + L::bb);
     float *sEG = reinterpret_cast<float *>(smem + L::eg);
 
     const int tid = threadIdx.x;
@@ -290,6 +296,7 @@ chunk_kernel(const KernelParams p) {
     const int c_begin = seg * p.cps;
     const int c_end = min(p.N, c_begin + p.cps);
     const int vb = w * VS;                     // this wave's first value column
+    const int r0 = RPW * w;                    // this wave's first chunk row
 
     const gmem_t *gq = reinterpret_cast<const gmem_t *>(p.q) + bh * long(T) * D;
     const gmem_t *gk = reinterpret_cast<const gmem_t *>(p.k) + bh * long(T) * D;
@@ -312,48 +319,46 @@ chunk_kernel(const KernelParams p) {
                 for (int e = 0; e < 4; ++e)
                     S[mt][nt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] : 0.f;
     }
-    if constexpr (kOut) {  // tiles above the diagonal of A are never written: zero them once
+    if constexpr (kOut) {  // entries above the diagonal of A are never written: zero them once
         for (int i = tid; i < C * L::TP; i += NW * 64) sA[i] = E::f2l(0.f);
     }
     float seg_gamma[CPL];
 #pragma unroll
     for (int u = 0; u < CPL; ++u) seg_gamma[u] = 0.f;
 
-    // ---- raw rows of the current chunk (this wave's 16 rows, CPL columns) --
-    Raw<E, CPL> rq[16], rk[16], rv[16];
-    RawG<CPL> rg[16];
+    // ---- raw rows of the current chunk (this wave's RPW rows, CPL columns) --
+    Raw<E, CPL> rq[RPW], rk[RPW], rv[RPW];
+    RawG<CPL> rg[RPW];
     constexpr int es = sizeof(gmem_t);
     const rsrc_t bq = make_rsrc(gq, long(T) * D * es);
     const rsrc_t bk = make_rsrc(gk, long(T) * D * es);
     const rsrc_t bv = make_rsrc(gv, long(T) * D * es);
     const rsrc_t bg = make_rsrc(gg, long(T) * D * 4);
     auto load_chunk = [&](int c) {
-        const int row0 = c * C + 16 * w;           // rows past T read as zero
-        const int eoff = row0 * D + lane * CPL;    // element offset of row i = 0
+        const int eoff = (c * C + r0) * D + lane * CPL;   // rows past T read as zero
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            rg[i].load(bg, (eoff + i * D) * 4);
-            if constexpr (kScores) rq[i].load(bq, (eoff + i * D) * es);
-            if constexpr (!kCumsum) rk[i].load(bk, (eoff + i * D) * es);
-            if constexpr (kState) rv[i].load(bv, (eoff + i * D) * es);
+        for (int i = 0; i < RPW; ++i) {   // row offsets go in the uniform soffset
+            rg[i].load(bg, eoff * 4, i * D * 4);
+            if constexpr (kScores) rq[i].load(bq, eoff * es, i * D * es);
+            if constexpr (!kCumsum) rk[i].load(bk, eoff * es, i * D * es);
+            if constexpr (kState) rv[i].load(bv, eoff * es, i * D * es);
         }
     };
     if (c_begin < c_end) load_chunk(c_begin);
 
-    // 16 consecutive tokens of column `col` into a transposed tile (2 fragments)
-    auto store_col16 = [&](lds_t *tile, int col, const float *x16) {
-        E::st_frag(tile + col * L::TP + 16 * w, E::pack(x16));
-        E::st_frag(tile + col * L::TP + 16 * w + 8, E::pack(x16 + 8));
+    // RPW consecutive tokens of column `col` into a transposed tile
+    auto store_col = [&](lds_t *tile, int col, const float *x) {
+#pragma unroll
+        for (int h = 0; h < RPW / 8; ++h) E::st_frag(tile + col * L::TP + r0 + 8 * h, E::pack(x + 8 * h));
     };
     auto store_v_cols = [&]() {
 #pragma unroll
-        for (int u = 0; u < CPL; ++u) {
-            const int col = lane * CPL + u;
-            E::st_frag(sVt + col * L::TP + 16 * w, Raw<E, CPL>::col8(rv, u));
-            E::st_frag(sVt + col * L::TP + 16 * w + 8, Raw<E, CPL>::col8(rv + 8, u));
-        }
+        for (int u = 0; u < CPL; ++u)
+#pragma unroll
+            for (int h = 0; h < RPW / 8; ++h)
+                E::st_frag(sVt + (lane * CPL + u) * L::TP + r0 + 8 * h, Raw<E, CPL>::col8(rv + 8 * h, u));
     };
-    auto store_row_pair = [&](lds_t *tile, int row, const float *x) {
+    auto store_row = [&](lds_t *tile, int row, const float *x) {   // permuted columns
         const int pc = perm_col(lane * CPL);
         if constexpr (CPL == 2) {
             typedef lds_t l2_t __attribute__((ext_vector_type(2)));
@@ -383,26 +388,26 @@ chunk_kernel(const KernelParams p) {
     int buf = 0;
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
-        // ---- a1: gate cumsum (log2 units) inside this wave's 16-row block.
-        // Every exponent formed below is a sum of gates of one sign (a prefix,
-        // a suffix, a run of block totals), never a difference of two prefix
+        // ---- a1: gate cumsum (log2 units) over this wave's RPW rows.  Every
+        // exponent formed below is a sum of gates of one sign (a prefix, a
+        // suffix, a run of wave totals), never a difference of two prefix
         // sums, so huge gates cannot cancel into large exponent errors.
-        float Pf[16][CPL];   // inclusive prefix within the block
+        float Pf[RPW][CPL];   // inclusive prefix within the wave's rows
         float Bw[CPL];
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
             float run = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < RPW; ++i) {
                 run = __builtin_fmaf(rg[i].get(u), kLog2e, run);
                 Pf[i][u] = run;
             }
             Bw[u] = run;
             sBtot[(buf * NW + w) * D + lane * CPL + u] = run;
         }
-        __syncthreads();  // B1: block totals visible
+        __syncthreads();  // B1: wave totals visible
 
-        float rw[CPL], aw[CPL], gam[CPL];   // blocks before w, after w, all
+        float rw[CPL], aw[CPL], gam[CPL];   // rows before the wave's, after, all
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
             float before = 0.f, after = 0.f, tot = 0.f;
@@ -420,8 +425,8 @@ chunk_kernel(const KernelParams p) {
 
         if constexpr (kCumsum) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = t0 + 16 * w + i;
+            for (int i = 0; i < RPW; ++i) {
+                const int t = t0 + r0 + i;
                 if (t < T)
 #pragma unroll
                     for (int u = 0; u < CPL; ++u)
@@ -436,135 +441,92 @@ chunk_kernel(const KernelParams p) {
             continue;
         }
 
-        // chunk span, identical in every wave (each wave holds all columns)
-        float cspan = 0.f;
+        // fast path unless some key dim decays by more than 2^kSpanGuard
+        bool wide = false;
 #pragma unroll
-        for (int u = 0; u < CPL; ++u) cspan = fmaxf(cspan, -gam[u]);
-        cspan = wave_max(cspan);
-        const bool fast = cspan <= kSpanGuard;
-        float bspan = 0.f;   // this wave's block span (guarded path)
+        for (int u = 0; u < CPL; ++u) wide |= -gam[u] > kSpanGuard;
+        const bool fast = __ballot(wide) == 0;
 
         // ---- operand tiles into LDS -----------------------------------------
+        float eg[CPL];
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+            eg[u] = fexp2(gam[u]);
+            if constexpr (kState) if (w == 0) sEG[lane * CPL + u] = eg[u];
+        }
         if constexpr (kScores) {
-            float eg[CPL];
-#pragma unroll
-            for (int u = 0; u < CPL; ++u) {
-                eg[u] = fexp2(gam[u]);
-                if constexpr (kOut) if (w == 0) sEG[lane * CPL + u] = eg[u];
-            }
+            float kh[CPL][RPW];
             if (fast) {
-                float kh[CPL][16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
+                for (int i = 0; i < RPW; ++i) {
                     float qh[CPL], kt[CPL];
 #pragma unroll
                     for (int u = 0; u < CPL; ++u) {
-                        const float t = rw[u] + Pf[i][u];                   // Gc_i, in [-kSpanGuard, 0]
-                        qh[u] = rq[i].get(u) * (p.scale * fexp2(t));          // scale q exp(Gc)
-                        kt[u] = rk[i].get(u) * fexp2(-t);                     // k exp(-Gc)
-                        kh[u][i] = kt[u] * eg[u];                             // k exp(Gamma - Gc)
+                        const float t = rw[u] + Pf[i][u];           // Gc_i in [-kSpanGuard, 0]
+                        qh[u] = rq[i].get(u) * (p.scale * fexp2(t)); // scale q exp(Gc)
+                        kt[u] = rk[i].get(u) * fexp2(-t);            // k exp(-Gc)
+                        kh[u][i] = kt[u] * eg[u];                    // k exp(Gamma - Gc)
                     }
-                    store_row_pair(sQh, 16 * w + i, qh);
-                    store_row_pair(sKb, 16 * w + i, kt);
-                }
-                if constexpr (kOut) {
-#pragma unroll
-                    for (int u = 0; u < CPL; ++u) store_col16(sKht, lane * CPL + u, kh[u]);
+                    store_row(sQh, r0 + i, qh);
+                    store_row(sKt, r0 + i, kt);
                 }
             } else {
-                float Sf[16][CPL];   // exclusive suffix within the block
-                float ew[CPL], xk[CPL];
 #pragma unroll
                 for (int u = 0; u < CPL; ++u) {
-                    float suf = 0.f;
+                    float suf = aw[u];   // rows after i within the chunk: exponent <= 0
 #pragma unroll
-                    for (int i = 15; i >= 0; --i) {
-                        Sf[i][u] = suf;
+                    for (int i = RPW - 1; i >= 0; --i) {
+                        kh[u][i] = rk[i].get(u) * fexp2(suf);
                         suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
                     }
-                    ew[u] = fexp2(rw[u]);    // chunk start -> block start   <= 1
-                    xk[u] = fexp2(aw[u]);    // block end   -> chunk end     <= 1
-                    sBb[w * D + perm_col(lane * CPL + u)] = Bw[u];
-                    bspan = fmaxf(bspan, -Bw[u]);
                 }
-                bspan = wave_max(bspan);
-                float kh[CPL][16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float qb[CPL], qh[CPL], kb[CPL];
+                for (int i = 0; i < RPW; ++i) {
+                    float qh[CPL];
 #pragma unroll
                     for (int u = 0; u < CPL; ++u) {
-                        qb[u] = p.scale * rq[i].get(u) * fexp2(Pf[i][u]);  // block start -> row i
-                        qh[u] = qb[u] * ew[u];
-                        kb[u] = rk[i].get(u) * fexp2(Sf[i][u]);            // row i -> block end
-                        kh[u][i] = kb[u] * xk[u];
+                        const int col = lane * CPL + u;
+                        qh[u] = rq[i].get(u) * (p.scale * fexp2(rw[u] + Pf[i][u]));
+                        // raw k and the token's decay factors, natural column order
+                        sKt[(r0 + i) * L::QP + col] = E::f2l(rk[i].get(u));
+                        sDec[(r0 + i) * L::DP + col] = fexp2(rg[i].get(u) * kLog2e);
                     }
-                    store_row_pair(sQb, 16 * w + i, qb);
-                    store_row_pair(sQh, 16 * w + i, qh);
-                    store_row_pair(sKb, 16 * w + i, kb);
-                }
-                if constexpr (kOut) {
-#pragma unroll
-                    for (int u = 0; u < CPL; ++u) store_col16(sKht, lane * CPL + u, kh[u]);
-                }
-                // diagonal block with a large span: exact elementwise scores,
-                // A[i][j] = scale sum_d q_i k_j exp(g_{j+1} + ... + g_i)
-                if (bspan > kSpanGuard) {
-#pragma unroll 1
-                    for (int i = 0; i < 16; ++i) {
-                        float qi[CPL], ex[CPL];
-#pragma unroll
-                        for (int u = 0; u < CPL; ++u) {
-                            qi[u] = 0.f;
-                            ex[u] = 0.f;
-#pragma unroll
-                            for (int x = 0; x < 16; ++x)
-                                if (x == i) qi[u] = rq[x].get(u);
-                        }
-                        for (int j = i; j >= 0; --j) {
-                            float part = 0.f;
-#pragma unroll
-                            for (int u = 0; u < CPL; ++u) {
-                                float kj = 0.f, gj = 0.f;   // select register row j
-#pragma unroll
-                                for (int x = 0; x < 16; ++x)
-                                    if (x == j) { kj = rk[x].get(u); gj = rg[x].get(u) * kLog2e; }
-                                part += qi[u] * kj * fexp2(ex[u]);
-                                ex[u] += gj;   // exponent for j-1: g_j + ... + g_i
-                            }
-                            const float s = wave_sum(part) * p.scale;
-                            if (lane == 0) {
-                                if constexpr (kOut) sA[(16 * w + i) * L::TP + 16 * w + j] = E::f2l(s);
-                                else p.dump[((bh * long(p.N) + c) * C + 16 * w + i) * C + 16 * w + j] = s;
-                            }
-                        }
-                        if constexpr (kIntra) {  // zeros above the diagonal of this block
-                            if (lane < 16 && lane > i)
-                                p.dump[((bh * long(p.N) + c) * C + 16 * w + i) * C + 16 * w + lane] = 0.f;
-                        }
-                    }
+                    store_row(sQh, r0 + i, qh);
                 }
             }
-            if constexpr (kOut) store_v_cols();
+            if constexpr (kOut) {
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) store_col(sKht, lane * CPL + u, kh[u]);
+                store_v_cols();
+            }
         }
         if constexpr (kSeg) {
 #pragma unroll
             for (int u = 0; u < CPL; ++u) {
-                const int col = lane * CPL + u;
-                if (w == 0) sEG[col] = fexp2(gam[u]);
-                float kk[16];
-                float suf = aw[u];   // blocks after w, then rows after i: exponent <= 0
+                float kk[RPW];
+                float suf = aw[u];   // rows after i within the chunk: exponent <= 0
 #pragma unroll
-                for (int i = 15; i >= 0; --i) {
-                    kk[i] = rk[i].get(u) * fexp2(suf);     // k exp(Gamma - Gc_i)
+                for (int i = RPW - 1; i >= 0; --i) {
+                    kk[i] = rk[i].get(u) * fexp2(suf);   // k exp(Gamma - Gc_i)
                     suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
                 }
-                store_col16(sKht, col, kk);
+                store_col(sKht, lane * CPL + u, kk);
             }
             store_v_cols();
         }
 #pragma unroll
         for (int u = 0; u < CPL; ++u) seg_gamma[u] += gam[u];
+
+        // the exact path reads raw q rows of this wave after the prefetch below
+        float qx[RPW][CPL];
+        if constexpr (kScores) {
+            if (!fast) {
+#pragma unroll
+                for (int i = 0; i < RPW; ++i)
+#pragma unroll
+                    for (int u = 0; u < CPL; ++u) qx[i][u] = rq[i].get(u);
+            }
+        }
 
         // prefetch the next chunk; the loads fly during the matrix work below
         if (c + 1 < c_end) load_chunk(c + 1);
@@ -579,13 +541,13 @@ chunk_kernel(const KernelParams p) {
                     if (t % NW != w) continue;
                     int I = 0, J = t;
 #pragma unroll
-                    for (int r = 0; r < NW; ++r)
+                    for (int r = 0; r < NB; ++r)
                         if (J > r) { J -= r + 1; I = r + 1; }
                     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         const int pos = ks * 32 + 8 * q4;
-                        acc = E::mma(E::ld_frag(sKb + (16 * J + n16) * L::QP + pos),
+                        acc = E::mma(E::ld_frag(sKt + (16 * J + n16) * L::QP + pos),
                                      E::ld_frag(sQh + (16 * I + n16) * L::QP + pos), acc);
                     }
                     if (I == J) {
@@ -595,60 +557,45 @@ chunk_kernel(const KernelParams p) {
                     }
                     sink_tile(c, I, J, acc);
                 }
-            } else {
-                // row block I = w: tile (I, J) = Kb[J] Qb[I]^T with the k side
-                // moved from the end of block J to the start of block I, factor
-                // exp(B_{J+1} + ... + B_{I-1}) (<= 1); on the diagonal exp(-B_I)
-                const int I = w;
+                if constexpr (kIntra) {  // zero tiles above the diagonal
 #pragma unroll
-                for (int J = 0; J < NW; ++J) {
-                    if (J > I) continue;
-                    if (J == I && bspan > kSpanGuard) continue;  // formed elementwise
-                    const bool rescale = (J < I - 1) || (J == I);
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int I = 0; I < NB; ++I)
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int pos = ks * 32 + 8 * q4;
-                        frag_t a = E::ld_frag(sKb + (16 * J + n16) * L::QP + pos);
-                        if (rescale) {
-                            float x[8], ex[8];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) ex[e] = 0.f;
-                            if (J == I) {
-                                const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sBb + I * D + pos);
-                                const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sBb + I * D + pos + 4);
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) { ex[e] = -b0[e]; ex[4 + e] = -b1[e]; }
-                            } else {
-#pragma unroll
-                                for (int j = 0; j < NW; ++j) {
-                                    if (j <= J || j >= I) continue;
-                                    const f32x4_t b0 = *reinterpret_cast<const f32x4_t *>(sBb + j * D + pos);
-                                    const f32x4_t b1 = *reinterpret_cast<const f32x4_t *>(sBb + j * D + pos + 4);
-#pragma unroll
-                                    for (int e = 0; e < 4; ++e) { ex[e] += b0[e]; ex[4 + e] += b1[e]; }
-                                }
-                            }
-                            E::unpack(a, x);
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) x[e] *= fexp2(ex[e]);
-                            a = E::pack(x);
-                        }
-                        acc = E::mma(a, E::ld_frag(sQb + (16 * I + n16) * L::QP + pos), acc);
-                    }
-                    if (J == I) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * q4 + e > n16) acc[e] = 0.f;
-                    }
-                    sink_tile(c, I, J, acc);
+                        for (int J = I + 1; J < NB; ++J)
+                            if ((I * NB + J) % NW == w) sink_tile(c, I, J, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 }
-            }
-            if constexpr (kIntra) {  // zero tiles above the diagonal of row block w
+            } else {
+                // rows of this wave, elementwise: running product over j = i..0
+#pragma unroll 1
+                for (int il = 0; il < RPW; ++il) {
+                    const int i = r0 + il;
+                    float qi[CPL], pr[CPL];
 #pragma unroll
-                for (int J = 0; J < NW; ++J) {
-                    if (J <= w) continue;
-                    sink_tile(c, w, J, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                    for (int u = 0; u < CPL; ++u) {
+                        qi[u] = 0.f;
+                        pr[u] = 1.f;
+#pragma unroll
+                        for (int x = 0; x < RPW; ++x)
+                            if (x == il) qi[u] = qx[x][u];
+                    }
+                    for (int j = i; j >= 0; --j) {
+                        float part = 0.f;
+#pragma unroll
+                        for (int u = 0; u < CPL; ++u) {
+                            const int col = lane * CPL + u;
+                            part += qi[u] * E::l2f(sKt[j * L::QP + col]) * pr[u];
+                            pr[u] *= sDec[j * L::DP + col];   // exp(g_j + ... + g_i) for j-1
+                        }
+                        const float s = wave_sum(part) * p.scale;
+                        if (lane == 0) {
+                            if constexpr (kOut) sA[i * L::TP + j] = E::f2l(s);
+                            else p.dump[((bh * long(p.N) + c) * C + i) * C + j] = s;
+                        }
+                    }
+                    if constexpr (kIntra) {
+                        for (int j = i + 1 + lane; j < C; j += 64)
+                            p.dump[((bh * long(p.N) + c) * C + i) * C + j] = 0.f;
+                    }
                 }
             }
         }
@@ -678,15 +625,14 @@ chunk_kernel(const KernelParams p) {
                             dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
             }
             // ---- a4: O^T tiles (value tile nt, token tile m) ---------------------
-            f32x4_t O[NTW][NW];
+            f32x4_t O[NTW][NB];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                for (int m = 0; m < NW; ++m) O[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int m = 0; m < NB; ++m) O[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             // inter-chunk: O^T += S^T (scale q exp Gc)^T, S straight from its accumulators
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                __builtin_amdgcn_sched_barrier(0);  // bound the fragment loads in flight
                 frag_t sf[NTW];
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
@@ -696,16 +642,15 @@ chunk_kernel(const KernelParams p) {
                     sf[nt] = E::pack(x);
                 }
 #pragma unroll
-                for (int m = 0; m < NW; ++m) {
+                for (int m = 0; m < NB; ++m) {
                     const frag_t b = E::ld_frag(sQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) O[nt][m] = E::mma(sf[nt], b, O[nt][m]);
                 }
             }
             // intra-chunk: O^T += V^T A^T over causal token steps
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int m = 0; m < NW; ++m) {
+            for (int m = 0; m < NB; ++m) {
 #pragma unroll
                 for (int ts = 0; ts < TS; ++ts) {
                     if (ts * 32 > 16 * m + 15) continue;
@@ -716,7 +661,7 @@ chunk_kernel(const KernelParams p) {
             }
             const rsrc_t bo = make_rsrc(reinterpret_cast<gmem_t *>(p.o) + bh * long(T) * D, long(T) * D * es);
 #pragma unroll
-            for (int m = 0; m < NW; ++m) {
+            for (int m = 0; m < NB; ++m) {
                 const int row = t0 + 16 * m + n16;   // rows past T are dropped
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
@@ -735,7 +680,6 @@ chunk_kernel(const KernelParams p) {
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            if ((mt & 1) == 0) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ts = 0; ts < TS; ++ts) {
                 const frag_t a = E::ld_frag(sKht + (16 * mt + n16) * L::TP + ts * 32 + 8 * q4);
@@ -803,7 +747,7 @@ copy_state_kernel(float *__restrict__ dst, const float *__restrict__ src, long n
 template <typename E, int D, int C, int MODE>
 static hipError_t launch_one(const KernelParams &p, int grid_x, int grid_y, hipStream_t s) {
     if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_kernel<E, D, C, MODE>), dim3(grid_x, grid_y), dim3(C / 16 * 64), 0, s, p);
+    hipLaunchKernelGGL((chunk_kernel<E, D, C, MODE>), dim3(grid_x, grid_y), dim3(Shape<D, C>::NW * 64), 0, s, p);
     return hipGetLastError();
 }
 
