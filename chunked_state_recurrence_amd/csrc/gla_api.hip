@@ -147,15 +147,26 @@ int validate(Call &c) {
 }
 
 struct Plan {
-    int P, cps;
+    int P;      // output-pass segments along T
+    int cps;    // chunks per output segment
+    int sub;    // state-pass units per output segment (divides cps)
+    int slots;  // state-pass units before the last output segment: (P - 1) * sub
 };
 
+// Output pass: about `target` work-groups (one per CU).  State pass: finer
+// units, about twice as many work-groups, since it fits two per CU.
 Plan plan_segments(int nbh, int N, int target) {
     int P = std::max(1, (target + nbh - 1) / nbh);
     P = std::min(P, N);
     const int cps = (N + P - 1) / P;
     P = (N + cps - 1) / cps;
-    return {P, cps};
+    int sub = 1;
+    if (P > 1) {
+        const int want = std::max(1, (2 * target) / (nbh * (P - 1)));
+        for (int m = std::min(want, cps); m >= 1; --m)
+            if (cps % m == 0) { sub = m; break; }
+    }
+    return {P, cps, sub, (P - 1) * sub};
 }
 
 int run_forward(Call &c) {
@@ -187,7 +198,7 @@ int run_forward(Call &c) {
     for (long g0 = 0; g0 < BH; g0 += group) {
         const int nbh = int(std::min(group, BH - g0));
         const Plan pl = plan_segments(nbh, N, target);
-        need = std::max(need, size_t(nbh) * size_t(pl.P - 1) * size_t(D) * (D + 1) * 4);
+        need = std::max(need, size_t(nbh) * size_t(pl.slots) * size_t(D) * (D + 1) * 4);
     }
     float *ws = nullptr;
     if (need > 0 && (rc = ensure_workspace(dev, need, &ws)) != GLA_OK) return rc;
@@ -199,19 +210,25 @@ int run_forward(Call &c) {
         p.q = c.q; p.k = c.k; p.v = c.v; p.g = c.g; p.h0 = c.h0;
         p.o = c.o; p.h_final = c.h_final;
         p.ws_E = ws;
-        p.ws_G = ws ? ws + size_t(nbh) * (pl.P - 1) * D * D : nullptr;
+        p.ws_G = ws ? ws + size_t(nbh) * pl.slots * D * D : nullptr;
         p.dump = c.states; p.dump2 = nullptr;
-        p.T = c.T; p.N = N; p.cps = pl.cps; p.P = pl.P; p.bh0 = g0; p.scale = c.scale;
+        p.T = c.T; p.N = N; p.bh0 = g0; p.scale = c.scale;
+        p.ws_slots = pl.slots; p.sub = pl.sub;
         if (pl.P > 1) {
+            gla::KernelParams ps = p;   // state pass over the chunks before the last segment
+            ps.cps = pl.cps / pl.sub;
+            ps.P = pl.slots;
             if (traced(GLA_KERNEL_SEGMENT, c.stream, [&] {
-                    return gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_SEG, p, pl.P - 1, nbh, c.stream);
+                    return gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_SEG, ps, pl.slots, nbh, c.stream);
                 }) != hipSuccess)
                 return GLA_ERR_LAUNCH;
             if (traced(GLA_KERNEL_SCAN, c.stream, [&] {
-                    return gla::launch_scan(p.ws_E, p.ws_G, c.h0, g0, nbh, pl.P, D, c.stream);
+                    return gla::launch_scan(p.ws_E, p.ws_G, c.h0, g0, nbh, pl.slots, D, c.stream);
                 }) != hipSuccess)
                 return GLA_ERR_LAUNCH;
         }
+        p.cps = pl.cps;
+        p.P = pl.P;
         if (traced(GLA_KERNEL_OUTPUT, c.stream, [&] {
                 return gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_OUT, p, pl.P, nbh, c.stream);
             }) != hipSuccess)

@@ -19,14 +19,16 @@ struct KernelParams {
     const float *h0;
     void *o;
     float *h_final;
-    float *ws_E;   // [nbh][P-1][D][D]  segment end states, then segment start states
-    float *ws_G;   // [nbh][P-1][D]     segment total log2-decay
+    float *ws_E;   // [nbh][ws_slots][D][D]  state-pass end states, then start states
+    float *ws_G;   // [nbh][ws_slots][D]     state-pass total log2-decay
     float *dump;   // stage outputs
     float *dump2;
     int T;         // tokens per (batch, head)
     int N;         // chunks per (batch, head)
     int cps;       // chunks per segment
-    int P;         // segments
+    int P;         // work-groups along T in this launch
+    int ws_slots;  // state-pass units per (batch, head) in the workspace
+    int sub;       // state-pass units per output segment (output pass reads slot seg*sub - 1)
     long bh0;      // first (batch, head) row of this launch
     float scale;
 };
@@ -35,7 +37,7 @@ bool chunk_supported(int dtype, int D, int C);
 hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, const KernelParams &p,
                                int grid_x, int grid_y, hipStream_t s);
 hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,
-                       int P, int D, hipStream_t s);
+                       int slots, int D, hipStream_t s);
 hipError_t launch_copy_state(float *dst, const float *src, long n, hipStream_t s);
 
 }  // namespace gla

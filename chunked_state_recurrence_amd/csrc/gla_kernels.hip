@@ -309,7 +309,7 @@ chunk_kernel(const KernelParams p) {
         const float *src = nullptr;
         if constexpr (kOut) {
             if (seg == 0) src = p.h0 ? p.h0 + bh * D * D : nullptr;
-            else src = p.ws_E + (bhl * (p.P - 1) + seg - 1) * long(D) * D;
+            else src = p.ws_E + (bhl * p.ws_slots + seg * p.sub - 1) * long(D) * D;
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -696,11 +696,11 @@ chunk_kernel(const KernelParams p) {
         if constexpr (kOut) {
             if (seg == p.P - 1 && p.h_final) dst = p.h_final + bh * long(D) * D;
         } else {
-            dst = p.ws_E + (bhl * (p.P - 1) + seg) * long(D) * D;
+            dst = p.ws_E + (bhl * p.ws_slots + seg) * long(D) * D;
             if (w == 0)
 #pragma unroll
                 for (int u = 0; u < CPL; ++u)
-                    p.ws_G[(bhl * (p.P - 1) + seg) * D + lane * CPL + u] = seg_gamma[u];
+                    p.ws_G[(bhl * p.ws_slots + seg) * D + lane * CPL + u] = seg_gamma[u];
         }
         if (dst) {
 #pragma unroll
@@ -714,11 +714,11 @@ chunk_kernel(const KernelParams p) {
     }
 }
 
-// Exclusive scan of the segment maps: E_r <- S_start(r+1) in place.
+// Exclusive scan of the state-pass maps: E_j <- S_start(j+1) in place.
 // One thread per (head, key dim, value column).
 __global__ void __launch_bounds__(256)
 scan_kernel(float *__restrict__ ws_E, const float *__restrict__ ws_G,
-            const float *__restrict__ h0, long bh0, int nbh, int P, int D) {
+            const float *__restrict__ h0, long bh0, int nbh, int slots, int D) {
     const long idx = long(blockIdx.x) * 256 + threadIdx.x;
     const long DD = long(D) * D;
     if (idx >= long(nbh) * DD) return;
@@ -726,11 +726,25 @@ scan_kernel(float *__restrict__ ws_E, const float *__restrict__ ws_G,
     const long dv = idx - bhl * DD;
     const int d = int(dv / D);
     float s = h0 ? h0[(bh0 + bhl) * DD + dv] : 0.f;
-    float *e = ws_E + bhl * (P - 1) * DD + dv;
-    const float *gm = ws_G + bhl * (P - 1) * D + d;
-    for (int r = 0; r < P - 1; ++r) {
-        s = fexp2(gm[long(r) * D]) * s + e[long(r) * DD];
-        e[long(r) * DD] = s;
+    float *e = ws_E + bhl * (slots) * DD + dv;
+    const float *gm = ws_G + bhl * (slots) * D + d;
+    constexpr int U = 8;   // segment states loaded ahead of the dependent chain
+    for (int r0 = 0; r0 < slots; r0 += U) {
+        float ev[U], gv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (r0 + u < slots) {
+                ev[u] = e[long(r0 + u) * DD];
+                gv[u] = gm[long(r0 + u) * D];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (r0 + u < slots) {
+                s = fexp2(gv[u]) * s + ev[u];
+                e[long(r0 + u) * DD] = s;
+            }
+        }
     }
 }
 
@@ -784,10 +798,10 @@ bool chunk_supported(int dtype, int D, int C) {
 }
 
 hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,
-                       int P, int D, hipStream_t s) {
+                       int slots, int D, hipStream_t s) {
     const long n = long(nbh) * D * D;
     const long blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(scan_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, ws_E, ws_G, h0, bh0, nbh, P, D);
+    hipLaunchKernelGGL(scan_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, ws_E, ws_G, h0, bh0, nbh, slots, D);
     return hipGetLastError();
 }
 
