@@ -74,6 +74,20 @@ struct BF16 {
     __device__ static f32x4_t mma(frag_t a, frag_t b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
+    // 8 consecutive tokens of one value column from a row-major tile of
+    // pitch `pitch` bytes: two transposing reads of 4 tokens each.  Within
+    // each 16-lane group, lane j supplies row k0 + j/4, columns c0 + 4(j%4)..+3
+    // and receives column c0 + (its index) of rows k0..k0+3.
+    __device__ static frag_t ld_col8(const unsigned char *tile, int pitch, int k0, int c0, int n16) {
+        typedef short s4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s4_t *lds_s4_p;
+        const unsigned char *a = tile + (k0 + (n16 >> 2)) * pitch + (c0 + 4 * (n16 & 3)) * 2;
+        const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_p)(a));
+        const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_p)(a + 4 * pitch));
+        typedef short s8_t __attribute__((ext_vector_type(8)));
+        const s8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(frag_t, v);
+    }
     // store 4 consecutive outputs (8 bytes) at byte offset `off`
     __device__ static void st4(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
         typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -118,6 +132,13 @@ struct F32 {
         for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
         return c;
     }
+    __device__ static frag_t ld_col8(const unsigned char *tile, int pitch, int k0, int c0, int n16) {
+        const float *a = reinterpret_cast<const float *>(tile + k0 * pitch) + c0 + n16;
+        frag_t f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = a[e * (pitch / 4)];
+        return f;
+    }
     __device__ static void st4(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
         typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), r, off, 0, 0);
@@ -132,6 +153,39 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, long bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes), 0x00020000);
+}
+
+// Buffer loads that write LDS directly: lane l's `size` bytes land at
+// lds + l * size (lds must be uniform).  Loads past num_records write zeros.
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+template <int SIZE>
+__device__ __forceinline__ void dma(rsrc_t r, void *lds, int voff, int soff) {
+    static_assert(SIZE == 4 || SIZE == 16, "direct load size");
+    if constexpr (SIZE == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 4, voff, soff, 0, 0);
+    if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 16, voff, soff, 0, 0);
+}
+// Wait until at most n vector-memory operations of this wave are in flight
+// (operations retire in issue order).  The direct-to-LDS loads have no
+// register results, so the compiler inserts no wait for them by itself.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Keeps the compiler from moving memory operations across this point, so
+// the issue order the waits count on is the program order.
+__device__ __forceinline__ void mem_fence_compiler() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Work-group barrier for LDS traffic: this wave's LDS reads and writes are
+// complete, then every wave meets.  Unlike __syncthreads() it does not drain
+// the wave's in-flight global loads (the release fence there counts the
+// direct-to-LDS loads as pending LDS writes); those are waited for
+// explicitly, with wait_vmem, before the barrier that publishes them.
+__device__ __forceinline__ void block_sync() {
+    __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // CPL consecutive elements of one row of q, k or v, as loaded from HBM.
@@ -223,15 +277,22 @@ template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int QP = D + 16 / es;   // Qh / Kt row pitch (elements)
     static constexpr int TP = C + 16 / es;   // Kht / Vt / A row pitch (elements)
     static constexpr int DP = D + 4;         // decay tile row pitch (floats)
-    static constexpr int qh = 0;
+    // output pass: v rows staged row-major by direct loads; bf16 rows padded
+    // by 32 bytes so the transposing fragment reads hit distinct banks
+    static constexpr int VP = es == 2 ? D * 2 + 32 : D * 4;   // bytes
+    // the direct-load targets come first, at low LDS addresses
+    static constexpr int gs = 0;                                  // float [C][D] gates
+    static constexpr int vs = gs + C * D * 4;                     // output pass: v rows
+    static constexpr int qh = vs + (MODE == MODE_OUT ? C * VP : 0);
     static constexpr int kt = qh + (scores ? C * QP * es : 0);
     static constexpr int kht = kt + (scores ? C * QP * es : 0);
-    static constexpr int vt = kht + (state ? D * TP * es : 0);
-    static constexpr int a = vt + (state ? D * TP * es : 0);
+    static constexpr int vt = kht + (state ? D * TP * es : 0);             // state pass: v^T
+    static constexpr int a = vt + (MODE == MODE_SEG ? D * TP * es : 0);
     static constexpr int dec = a + (MODE == MODE_OUT ? C * TP * es : 0);
     static constexpr int btot = dec + (scores ? C * DP * 4 : 0);   // float [2][NW][D]
     static constexpr int eg = btot + 2 * NW * D * 4;              // float [D] exp2(Gamma)
     static constexpr int bytes = eg + D * 4;
+    static_assert(vs + (MODE == MODE_OUT ? C * VP : 0) <= 65536, "direct-load targets below 64 KB");
 };
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -278,7 +339,9 @@ chunk_kernel(const KernelParams p) {
     lds_t *sQh = reinterpret_cast<lds_t *>(smem + L::qh);    // scale q exp(Gc), permuted cols
     lds_t *sKt = reinterpret_cast<lds_t *>(smem + L::kt);    // fast: k exp(-Gc) (permuted); exact: raw k
     lds_t *sKht = reinterpret_cast<lds_t *>(smem + L::kht);  // (k exp(Gamma - Gc))^T
-    lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);    // v^T
+    lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);    // state pass: v^T
+    unsigned char *sV = smem + L::vs;                         // output pass: v rows (pitch L::VP)
+    float *sG = reinterpret_cast<float *>(smem + L::gs);      // gates of the chunk, row-major
     lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);      // scaled scores, row-major
     float *sDec = reinterpret_cast<float *>(smem + L::dec);  // exact path: exp(g) per token
     float *sBtot = reinterpret_cast<float *>(smem + L::btot);
@@ -327,24 +390,64 @@ chunk_kernel(const KernelParams p) {
     for (int u = 0; u < CPL; ++u) seg_gamma[u] = 0.f;
 
     // ---- raw rows of the current chunk (this wave's RPW rows, CPL columns) --
+    constexpr bool kVreg = kSeg;   // v through registers into v^T (state pass)
+    constexpr bool kVdma = kOut;   // v straight into LDS rows (output pass)
     Raw<E, CPL> rq[RPW], rk[RPW], rv[RPW];
-    RawG<CPL> rg[RPW];
     constexpr int es = sizeof(gmem_t);
     const rsrc_t bq = make_rsrc(gq, long(T) * D * es);
     const rsrc_t bk = make_rsrc(gk, long(T) * D * es);
     const rsrc_t bv = make_rsrc(gv, long(T) * D * es);
     const rsrc_t bg = make_rsrc(gg, long(T) * D * 4);
-    auto load_chunk = [&](int c) {
-        const int eoff = (c * C + r0) * D + lane * CPL;   // rows past T read as zero
+    // Issue counts per wave, for the explicit waits: gate rows (direct, 1 KB
+    // per load), register rows of q / k (/ v in the state pass), v rows.
+    constexpr int NG = RPW * D * 4 / 1024;
+    constexpr int NQK = (kScores ? RPW : 0) + (kCumsum ? 0 : RPW) + (kVreg ? RPW : 0);
+    constexpr int NV = !kVdma ? 0 : (es == 2 ? RPW : RPW * D * 4 / 1024);
+    static_assert(RPW * D * 4 % 1024 == 0, "gate rows per wave must fill whole loads");
+    // this wave's gate rows of chunk c into its rows of sG (rows past T read 0)
+    auto load_g = [&](int c) {
+        const int rbase = __builtin_amdgcn_readfirstlane((c * C + r0) * D * 4);
+        float *dst = sG + __builtin_amdgcn_readfirstlane(r0 * D);
+        mem_fence_compiler();
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {   // row offsets go in the uniform soffset
-            rg[i].load(bg, eoff * 4, i * D * 4);
+        for (int i = 0; i < NG; ++i) dma<16>(bg, reinterpret_cast<unsigned char *>(dst) + i * 1024, lane * 16, rbase + i * 1024);
+        mem_fence_compiler();
+    };
+    // rows past T read as zero; row offsets go in the uniform soffset
+    auto load_qkv = [&](int c) {
+        const int eoff = (c * C + r0) * D + lane * CPL;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
             if constexpr (kScores) rq[i].load(bq, eoff * es, i * D * es);
             if constexpr (!kCumsum) rk[i].load(bk, eoff * es, i * D * es);
-            if constexpr (kState) rv[i].load(bv, eoff * es, i * D * es);
+            if constexpr (kVreg) rv[i].load(bv, eoff * es, i * D * es);
+        }
+        mem_fence_compiler();
+    };
+    // this wave's v rows of chunk c into sV
+    auto load_v = [&](int c) {
+        if constexpr (kVdma) {
+            const int row0 = __builtin_amdgcn_readfirstlane(c * C + r0);
+            const int lr0 = __builtin_amdgcn_readfirstlane(r0);
+            if constexpr (es == 2) {   // one load per row, padded pitch; 4 bytes per lane
+                // (narrower direct loads still occupy 4 bytes of LDS per lane), so
+                // a 64-wide row takes lanes 0..31 only
+#pragma unroll
+                for (int i = 0; i < RPW; ++i)
+                    if (CPL == 2 || lane < 32) dma<4>(bv, sV + (lr0 + i) * L::VP, lane * 4, (row0 + i) * D * 2);
+            } else {                   // dense rows, 1 KB per load
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    dma<16>(bv, sV + lr0 * L::VP + i * 1024, lane * 16, row0 * D * 4 + i * 1024);
+            }
+            mem_fence_compiler();
         }
     };
-    if (c_begin < c_end) load_chunk(c_begin);
+    if (c_begin < c_end) {
+        load_g(c_begin);
+        load_qkv(c_begin);
+        load_v(c_begin);
+    }
 
     // RPW consecutive tokens of column `col` into a transposed tile
     auto store_col = [&](lds_t *tile, int col, const float *x) {
@@ -392,8 +495,17 @@ chunk_kernel(const KernelParams p) {
         // exponent formed below is a sum of gates of one sign (a prefix, a
         // suffix, a run of wave totals), never a difference of two prefix
         // sums, so huge gates cannot cancel into large exponent errors.
+        // The next chunk's loads are issued on every chunk (the last one
+        // reloads its own rows), so each wait below counts the same loads on
+        // every path.
+        const int cn = min(c + 1, c_end - 1);
+        // this wave's gate rows arrived (loads after them: q / k / v rows)
+        wait_vmem<NQK + NV>();
+        RawG<CPL> rg[RPW];   // each wave reads back only the rows it loaded itself
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) rg[i].x = *reinterpret_cast<const decltype(rg[i].x) *>(sG + (r0 + i) * D + lane * CPL);
         float Pf[RPW][CPL];   // inclusive prefix within the wave's rows
-        float Bw[CPL];
+        float Sw[RPW][CPL];   // state pass: suffix after the row within the wave's rows
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
             float run = 0.f;
@@ -402,10 +514,20 @@ chunk_kernel(const KernelParams p) {
                 run = __builtin_fmaf(rg[i].get(u), kLog2e, run);
                 Pf[i][u] = run;
             }
-            Bw[u] = run;
+            if constexpr (kSeg) {
+                float suf = 0.f;
+#pragma unroll
+                for (int i = RPW - 1; i >= 0; --i) {
+                    Sw[i][u] = suf;
+                    suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
+                }
+            }
             sBtot[(buf * NW + w) * D + lane * CPL + u] = run;
         }
-        __syncthreads();  // B1: wave totals visible
+        // the gates are in registers: the next chunk's gate rows load during
+        // the rest of this chunk
+        if constexpr (!kCumsum) load_g(cn);
+        block_sync();  // B1: wave totals visible
 
         float rw[CPL], aw[CPL], gam[CPL];   // rows before the wave's, after, all
 #pragma unroll
@@ -436,7 +558,7 @@ chunk_kernel(const KernelParams p) {
 #pragma unroll
                 for (int u = 0; u < CPL; ++u)
                     p.dump2[(bh * long(p.N) + c) * D + lane * CPL + u] = gam[u] * kLn2;
-            if (c + 1 < c_end) load_chunk(c + 1);
+            load_g(cn);
             buf ^= 1;
             continue;
         }
@@ -497,19 +619,15 @@ chunk_kernel(const KernelParams p) {
             if constexpr (kOut) {
 #pragma unroll
                 for (int u = 0; u < CPL; ++u) store_col(sKht, lane * CPL + u, kh[u]);
-                store_v_cols();
             }
         }
         if constexpr (kSeg) {
 #pragma unroll
             for (int u = 0; u < CPL; ++u) {
                 float kk[RPW];
-                float suf = aw[u];   // rows after i within the chunk: exponent <= 0
 #pragma unroll
-                for (int i = RPW - 1; i >= 0; --i) {
-                    kk[i] = rk[i].get(u) * fexp2(suf);   // k exp(Gamma - Gc_i)
-                    suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
-                }
+                for (int i = 0; i < RPW; ++i)   // k exp(Gamma - Gc_i): two sums of gates <= 0
+                    kk[i] = rk[i].get(u) * fexp2(aw[u] + Sw[i][u]);
                 store_col(sKht, lane * CPL + u, kk);
             }
             store_v_cols();
@@ -528,9 +646,11 @@ chunk_kernel(const KernelParams p) {
             }
         }
 
-        // prefetch the next chunk; the loads fly during the matrix work below
-        if (c + 1 < c_end) load_chunk(c + 1);
-        __syncthreads();  // B2: operand tiles visible
+        // prefetch the next chunk's gates (score modes) and q / k rows; the
+        // loads fly during the matrix work below
+        load_qkv(cn);
+        if constexpr (kVdma) wait_vmem<NG + NQK>();   // this chunk's v rows arrived (loads after them: next gates, q, k)
+        block_sync();  // B2: operand tiles visible
 
         // ---- a2: causal score tiles -------------------------------------------
         if constexpr (kScores) {
@@ -601,7 +721,7 @@ chunk_kernel(const KernelParams p) {
         }
         if constexpr (kIntra) {
             buf ^= 1;
-            __syncthreads();  // LDS reuse by the next chunk
+            block_sync();  // LDS reuse by the next chunk
             continue;
         }
 
@@ -610,10 +730,11 @@ chunk_kernel(const KernelParams p) {
         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
             for (int ts = 0; ts < TS; ++ts)
-                vf[nt][ts] = E::ld_frag(sVt + (vb + 16 * nt + n16) * L::TP + ts * 32 + 8 * q4);
+                if constexpr (kVdma) vf[nt][ts] = E::ld_col8(sV, L::VP, ts * 32 + 8 * q4, vb + 16 * nt, n16);
+                else vf[nt][ts] = E::ld_frag(sVt + (vb + 16 * nt + n16) * L::TP + ts * 32 + 8 * q4);
 
         if constexpr (kOut) {
-            __syncthreads();  // B3: score tiles visible
+            block_sync();  // B3: score tiles visible
             if (p.dump) {     // chunk-start states (stage test only)
                 float *dst = p.dump + (bh * long(p.N) + c) * long(D) * D;
 #pragma unroll
@@ -624,6 +745,8 @@ chunk_kernel(const KernelParams p) {
                         for (int e = 0; e < 4; ++e)
                             dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
             }
+            // every wave holds its v fragments: the next chunk's v rows may land
+            load_v(cn);
             // ---- a4: O^T tiles (value tile nt, token tile m) ---------------------
             f32x4_t O[NTW][NB];
 #pragma unroll
@@ -689,6 +812,7 @@ chunk_kernel(const KernelParams p) {
         }
         buf ^= 1;
     }
+    wait_vmem<0>();   // no direct load may land after the work-group ends
 
     // ---- segment end --------------------------------------------------------
     if constexpr (kState) {
