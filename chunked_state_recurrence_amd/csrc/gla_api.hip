@@ -155,14 +155,14 @@ struct Plan {
 
 // Output pass: about `target` work-groups (one per CU).  State pass: finer
 // units, about twice as many work-groups, since it fits two per CU.
-Plan plan_segments(int nbh, int N, int target) {
+Plan plan_segments(int nbh, int N, int target, int state_per_cu) {
     int P = std::max(1, (target + nbh - 1) / nbh);
     P = std::min(P, N);
     const int cps = (N + P - 1) / P;
     P = (N + cps - 1) / cps;
     int sub = 1;
-    if (P > 1) {
-        const int want = std::max(1, (2 * target) / (nbh * (P - 1)));
+    if (P > 1) {   // state units: about state_per_cu work-groups per CU target
+        const int want = std::max(1, (state_per_cu * target) / (nbh * (P - 1)));
         for (int m = std::min(want, cps); m >= 1; --m)
             if (cps % m == 0) { sub = m; break; }
     }
@@ -190,6 +190,10 @@ int run_forward(Call &c) {
         target = g_target_wgs;
         hg = g_head_group;
     }
+    // chunk length of the state pass (state units end on output-chunk
+    // boundaries, so it may differ from the output pass's; it is the same here)
+    const int cs = c.chunk;
+    const int spc = gla::state_units_per_cu(c.dtype, D, cs);
     long group = hg > 0 ? std::min<long>(hg, BH) : BH;
     group = std::min<long>(group, 65535);
 
@@ -197,7 +201,7 @@ int run_forward(Call &c) {
     size_t need = 0;
     for (long g0 = 0; g0 < BH; g0 += group) {
         const int nbh = int(std::min(group, BH - g0));
-        const Plan pl = plan_segments(nbh, N, target);
+        const Plan pl = plan_segments(nbh, N, target, spc);
         need = std::max(need, size_t(nbh) * size_t(pl.slots) * size_t(D) * (D + 1) * 4);
     }
     float *ws = nullptr;
@@ -205,7 +209,7 @@ int run_forward(Call &c) {
 
     for (long g0 = 0; g0 < BH; g0 += group) {
         const int nbh = int(std::min(group, BH - g0));
-        const Plan pl = plan_segments(nbh, N, target);
+        const Plan pl = plan_segments(nbh, N, target, spc);
         gla::KernelParams p{};
         p.q = c.q; p.k = c.k; p.v = c.v; p.g = c.g; p.h0 = c.h0;
         p.o = c.o; p.h_final = c.h_final;
@@ -216,10 +220,11 @@ int run_forward(Call &c) {
         p.ws_slots = pl.slots; p.sub = pl.sub;
         if (pl.P > 1) {
             gla::KernelParams ps = p;   // state pass over the chunks before the last segment
-            ps.cps = pl.cps / pl.sub;
+            ps.cps = pl.cps / pl.sub * (c.chunk / cs);
+            ps.N = (c.T + cs - 1) / cs;
             ps.P = pl.slots;
             if (traced(GLA_KERNEL_SEGMENT, c.stream, [&] {
-                    return gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_SEG, ps, pl.slots, nbh, c.stream);
+                    return gla::launch_chunk_kernel(c.dtype, D, cs, gla::MODE_SEG, ps, pl.slots, nbh, c.stream);
                 }) != hipSuccess)
                 return GLA_ERR_LAUNCH;
             if (traced(GLA_KERNEL_SCAN, c.stream, [&] {

@@ -34,6 +34,8 @@ struct KernelParams {
 };
 
 bool chunk_supported(int dtype, int D, int C);
+// work-groups of the state pass that fit on one CU (LDS bound), 1 or 2
+int state_units_per_cu(int dtype, int D, int C);
 hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, const KernelParams &p,
                                int grid_x, int grid_y, hipStream_t s);
 hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,

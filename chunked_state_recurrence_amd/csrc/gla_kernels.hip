@@ -31,6 +31,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "gla_internal.h"
 
 namespace gla {
@@ -74,14 +77,20 @@ struct BF16 {
     __device__ static f32x4_t mma(frag_t a, frag_t b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
-    // 8 consecutive tokens of one value column from a row-major tile of
-    // pitch `pitch` bytes: two transposing reads of 4 tokens each.  Within
-    // each 16-lane group, lane j supplies row k0 + j/4, columns c0 + 4(j%4)..+3
-    // and receives column c0 + (its index) of rows k0..k0+3.
+    // Row r of a padded row-major bf16 tile of pitch `pitch` bytes starts at
+    // r * pitch + 128 * (r / 8): with pitch = 32 mod 256 the four rows one
+    // transposing read touches cover distinct banks, and the extra shift puts
+    // rows eight apart (the next 16-lane group) on the other half of the banks.
+    __device__ static int rowoff(int r, int pitch) { return r * pitch + 128 * (r >> 3); }
+    static constexpr int tile_bytes(int rows, int pitch) { return rows * pitch + 128 * (rows / 8); }
+    // 8 consecutive tokens of one column from such a tile, k0 a multiple of 8:
+    // two transposing reads of 4 tokens each.  Within each 16-lane group,
+    // lane j supplies row k0 + j/4, columns c0 + 4(j%4)..+3 and receives
+    // column c0 + (its index) of rows k0..k0+3.
     __device__ static frag_t ld_col8(const unsigned char *tile, int pitch, int k0, int c0, int n16) {
         typedef short s4_t __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) s4_t *lds_s4_p;
-        const unsigned char *a = tile + (k0 + (n16 >> 2)) * pitch + (c0 + 4 * (n16 & 3)) * 2;
+        const unsigned char *a = tile + rowoff(k0, pitch) + (n16 >> 2) * pitch + (c0 + 4 * (n16 & 3)) * 2;
         const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_p)(a));
         const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_p)(a + 4 * pitch));
         typedef short s8_t __attribute__((ext_vector_type(8)));
@@ -132,6 +141,9 @@ struct F32 {
         for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
         return c;
     }
+    // dense rows (fp32 tiles are loaded 1 KB at a time)
+    __device__ static int rowoff(int r, int pitch) { return r * pitch; }
+    static constexpr int tile_bytes(int rows, int pitch) { return rows * pitch; }
     __device__ static frag_t ld_col8(const unsigned char *tile, int pitch, int k0, int c0, int n16) {
         const float *a = reinterpret_cast<const float *>(tile + k0 * pitch) + c0 + n16;
         frag_t f;
@@ -167,9 +179,11 @@ __device__ __forceinline__ void dma(rsrc_t r, void *lds, int voff, int soff) {
 // Wait until at most n vector-memory operations of this wave are in flight
 // (operations retire in issue order).  The direct-to-LDS loads have no
 // register results, so the compiler inserts no wait for them by itself.
-template <int N>
+// Counts above the counter's range (63) clamp down, which only waits longer.
+template <int N0>
 __device__ __forceinline__ void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
+    static_assert(N0 >= 0, "vmcnt range");
+    constexpr int N = N0 < 63 ? N0 : 63;
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 // Keeps the compiler from moving memory operations across this point, so
@@ -280,10 +294,9 @@ template <typename E, int D, int C, int MODE> struct Layout {
     // output pass: v rows staged row-major by direct loads; bf16 rows padded
     // by 32 bytes so the transposing fragment reads hit distinct banks
     static constexpr int VP = es == 2 ? D * 2 + 32 : D * 4;   // bytes
-    // the direct-load targets come first, at low LDS addresses
-    static constexpr int gs = 0;                                  // float [C][D] gates
-    static constexpr int vs = gs + C * D * 4;                     // output pass: v rows
-    static constexpr int qh = vs + (MODE == MODE_OUT ? C * VP : 0);
+    // (the direct-load targets, gate rows and output-pass value rows, are
+    // arrays of their own)
+    static constexpr int qh = 0;
     static constexpr int kt = qh + (scores ? C * QP * es : 0);
     static constexpr int kht = kt + (scores ? C * QP * es : 0);
     static constexpr int vt = kht + (state ? D * TP * es : 0);             // state pass: v^T
@@ -292,7 +305,9 @@ template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int btot = dec + (scores ? C * DP * 4 : 0);   // float [2][NW][D]
     static constexpr int eg = btot + 2 * NW * D * 4;              // float [D] exp2(Gamma)
     static constexpr int bytes = eg + D * 4;
-    static_assert(vs + (MODE == MODE_OUT ? C * VP : 0) <= 65536, "direct-load targets below 64 KB");
+    static constexpr int gbytes = C * D * 4;                        // gate rows
+    static constexpr int vbytes = MODE == MODE_OUT ? E::tile_bytes(C, VP) : 16;   // output pass: v rows
+    static_assert(bytes + gbytes + vbytes <= 163840, "LDS");
 };
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -340,8 +355,10 @@ chunk_kernel(const KernelParams p) {
     lds_t *sKt = reinterpret_cast<lds_t *>(smem + L::kt);    // fast: k exp(-Gc) (permuted); exact: raw k
     lds_t *sKht = reinterpret_cast<lds_t *>(smem + L::kht);  // (k exp(Gamma - Gc))^T
     lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);    // state pass: v^T
-    unsigned char *sV = smem + L::vs;                         // output pass: v rows (pitch L::VP)
-    float *sG = reinterpret_cast<float *>(smem + L::gs);      // gates of the chunk, row-major
+    // Direct-load targets in arrays of their own, so the compiler can tell
+    // that fragment reads elsewhere do not touch loads still landing here.
+    __shared__ __attribute__((aligned(16))) float sG[C * D];                   // gate rows
+    __shared__ __attribute__((aligned(16))) unsigned char sV[L::vbytes];       // v rows (pitch L::VP)
     lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);      // scaled scores, row-major
     float *sDec = reinterpret_cast<float *>(smem + L::dec);  // exact path: exp(g) per token
     float *sBtot = reinterpret_cast<float *>(smem + L::btot);
@@ -434,7 +451,7 @@ chunk_kernel(const KernelParams p) {
                 // a 64-wide row takes lanes 0..31 only
 #pragma unroll
                 for (int i = 0; i < RPW; ++i)
-                    if (CPL == 2 || lane < 32) dma<4>(bv, sV + (lr0 + i) * L::VP, lane * 4, (row0 + i) * D * 2);
+                    if (CPL == 2 || lane < 32) dma<4>(bv, sV + E::rowoff(lr0 + i, L::VP), lane * 4, (row0 + i) * D * 2);
             } else {                   // dense rows, 1 KB per load
 #pragma unroll
                 for (int i = 0; i < NV; ++i)
@@ -838,6 +855,215 @@ chunk_kernel(const KernelParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// State pass, bf16: the end state of each state unit (a run of chunks) from a
+// zero start, S <- diag(exp2 Gamma) S + (k exp2(Gamma - Gc))^T V per chunk,
+// and the unit's total log2-decay.  Three-stage pipeline, so that two
+// chunks' rows are always on their way from HBM while one is worked on: key
+// and value rows go straight into LDS (three buffers each), gate rows into
+// registers (three sets); chunk c + 2 is requested at the first barrier of
+// chunk c, once every wave is done with chunk c - 1's buffers.
+// Wave w owns the gate / key rows [r0, r0 + RPW) for the exponent sums and
+// value columns [w*D/NW, (w+1)*D/NW) of S.  The k~^T and V operands of the
+// update are read as MFMA fragments with transposing LDS reads.
+// ---------------------------------------------------------------------------
+template <int D, int C> struct StateLayout {
+    static constexpr int NW = Shape<D, C>::NW;
+    static constexpr int VP = D * 2 + 32;    // padded bf16 row pitch (bytes) of the v / k~ tiles
+    static constexpr int KB = C * D * 2;     // raw key tile, dense rows
+    static constexpr int VB = BF16::tile_bytes(C, VP);   // value tile / scaled key tile
+    static constexpr int bytes = 3 * (KB + VB) + VB + NW * D * 4 + D * 4;
+    static_assert(bytes <= 163840, "state pass LDS");
+};
+
+template <int D, int C>
+__global__ void __launch_bounds__((Shape<D, C>::NW * 64))
+state_kernel(const KernelParams p) {
+    using E = BF16;
+    using L = StateLayout<D, C>;
+    constexpr int NW = Shape<D, C>::NW;
+    constexpr int RPW = Shape<D, C>::RPW;
+    constexpr int CPL = D / 64;
+    constexpr int VS = D / NW;
+    constexpr int NTW = VS / 16;
+    constexpr int MT = D / 16;
+    constexpr int TS = C / 32;
+    constexpr int NKL = RPW * D * 2 / 1024;   // direct loads per wave and chunk: keys
+    constexpr int NVL = RPW;                  // values (one per row)
+    constexpr int NCH = RPW + NKL + NVL;      // vector-memory operations per wave and chunk
+    static_assert(RPW * D * 2 % 1024 == 0, "key rows per wave must fill whole loads");
+    typedef typename E::frag_t frag_t;
+
+    // Separate arrays per buffer: the compiler can then tell that fragment
+    // reads of one buffer do not touch the loads landing in another.
+    __shared__ __attribute__((aligned(16))) unsigned char sK0[L::KB], sK1[L::KB], sK2[L::KB];
+    __shared__ __attribute__((aligned(16))) unsigned char sV0[L::VB], sV1[L::VB], sV2[L::VB];
+    __shared__ __attribute__((aligned(16))) unsigned char sKK[L::VB];   // k exp2(Gamma - Gc), rows
+    __shared__ __attribute__((aligned(16))) float sBt[NW * D];          // wave totals
+    __shared__ __attribute__((aligned(16))) float sEG[D];               // exp2(Gamma)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int n16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int seg = blockIdx.x;
+    const long bhl = blockIdx.y;
+    const long bh = p.bh0 + bhl;
+    const int T = p.T;
+    const int c_begin = seg * p.cps;
+    const int c_end = min(p.N, c_begin + p.cps);
+    const int vb = w * VS;
+    const int r0 = RPW * w;
+
+    const rsrc_t bk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + bh * long(T) * D, long(T) * D * 2);
+    const rsrc_t bv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + bh * long(T) * D, long(T) * D * 2);
+    const rsrc_t bg = make_rsrc(p.g + bh * long(T) * D, long(T) * D * 4);
+
+    RawG<CPL> rg0[RPW], rg1[RPW], rg2[RPW];   // gate rows of the three stages
+
+    // this wave's gate rows (registers), key and value rows (LDS) of chunk c
+    // (rows past T read as zero).  Issue order g, k, v is what the waits count on.
+    auto issue = [&](int c, RawG<CPL> *tg, unsigned char *tk, unsigned char *tv) {
+        const int row0 = __builtin_amdgcn_readfirstlane(c * C + r0);
+        const int lr0 = __builtin_amdgcn_readfirstlane(r0);
+        mem_fence_compiler();
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) tg[i].load(bg, (row0 * D + lane * CPL) * 4, i * D * 4);
+#pragma unroll
+        for (int i = 0; i < NKL; ++i)
+            dma<16>(bk, tk + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
+#pragma unroll
+        for (int i = 0; i < NVL; ++i)   // 4 bytes per lane: a 64-wide row takes lanes 0..31
+            if (CPL == 2 || lane < 32) dma<4>(bv, tv + E::rowoff(lr0 + i, L::VP), lane * 4, (row0 + i) * D * 2);
+        mem_fence_compiler();
+    };
+
+    f32x4_t S[MT][NTW];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) S[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float seg_gamma[CPL];
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) seg_gamma[u] = 0.f;
+
+    // one chunk from stage B while the next two chunks load into the others
+    auto step = [&](int c, auto bsel) {
+        constexpr int B = decltype(bsel)::value;
+        RawG<CPL> *rg = B == 0 ? rg0 : B == 1 ? rg1 : rg2;
+        unsigned char *kt = B == 0 ? sK0 : B == 1 ? sK1 : sK2;
+        unsigned char *vt = B == 0 ? sV0 : B == 1 ? sV1 : sV2;
+        // this wave's key rows of chunk c arrived (after them: its value rows
+        // and all of chunk c + 1); the gate registers are waited for by the compiler
+        wait_vmem<NVL + NCH>();
+        Raw<E, CPL> rk[RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+            rk[i].x = *reinterpret_cast<const decltype(rk[i].x) *>(kt + ((r0 + i) * D + lane * CPL) * 2);
+        // gate sums in log2 units: suffix after each row and total, per wave
+        float Sw[RPW][CPL];
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+            float suf = 0.f;
+#pragma unroll
+            for (int i = RPW - 1; i >= 0; --i) {
+                Sw[i][u] = suf;
+                suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
+            }
+            sBt[w * D + lane * CPL + u] = suf;
+        }
+        block_sync();  // B1: wave totals visible; every wave is done with chunk c - 1
+        // chunk c - 1's stage is free: request chunk c + 2 (near the end the
+        // last chunk is requested again, so the waits count the same loads)
+        {
+            constexpr int N2 = (B + 2) % 3;
+            issue(min(c + 2, c_end - 1), N2 == 0 ? rg0 : N2 == 1 ? rg1 : rg2,
+                  N2 == 0 ? sK0 : N2 == 1 ? sK1 : sK2, N2 == 0 ? sV0 : N2 == 1 ? sV1 : sV2);
+        }
+
+        float aw[CPL];   // rows after the wave's
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+            float after = 0.f, tot = 0.f;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const float t = sBt[j * D + lane * CPL + u];
+                if (j > w) after += t;
+                tot += t;
+            }
+            aw[u] = after;
+            seg_gamma[u] += tot;
+            if (w == 0) sEG[lane * CPL + u] = fexp2(tot);
+        }
+        // k exp2(Gamma - Gc_i): two sums of gates <= 0, rows into the k~ tile
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            float kk[CPL];
+#pragma unroll
+            for (int u = 0; u < CPL; ++u) kk[u] = rk[i].get(u) * fexp2(aw[u] + Sw[i][u]);
+            __bf16 *dst = reinterpret_cast<__bf16 *>(sKK + E::rowoff(r0 + i, L::VP)) + lane * CPL;
+            if constexpr (CPL == 2) {
+                typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+                *reinterpret_cast<b2_t *>(dst) = b2_t{(__bf16)kk[0], (__bf16)kk[1]};
+            } else {
+                dst[0] = (__bf16)kk[0];
+            }
+        }
+        wait_vmem<2 * NCH>();   // this chunk's value rows arrived (after them: chunks c + 1, c + 2)
+        block_sync();  // B2: k~ tile, value rows and decays visible
+
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4_t egv = *reinterpret_cast<const f32x4_t *>(sEG + 16 * mt + 4 * q4);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[mt][nt][e] *= egv[e];
+        }
+        frag_t vf[NTW][TS];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int ts = 0; ts < TS; ++ts) vf[nt][ts] = E::ld_col8(vt, L::VP, ts * 32 + 8 * q4, vb + 16 * nt, n16);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ts = 0; ts < TS; ++ts) {
+                const frag_t a = E::ld_col8(sKK, L::VP, ts * 32 + 8 * q4, 16 * mt, n16);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) S[mt][nt] = E::mma(a, vf[nt][ts], S[mt][nt]);
+            }
+    };
+
+    if (c_begin < c_end) {   // prologue: the first two chunks
+        issue(c_begin, rg0, sK0, sV0);
+        issue(min(c_begin + 1, c_end - 1), rg1, sK1, sV1);
+    }
+    // whole rounds of three, then the remainder, so that every path into a
+    // step has issued the same loads (the waits stay tight)
+    int c = c_begin;
+    for (; c + 3 <= c_end; c += 3) {
+        step(c, std::integral_constant<int, 0>{});
+        step(c + 1, std::integral_constant<int, 1>{});
+        step(c + 2, std::integral_constant<int, 2>{});
+    }
+    if (c < c_end) step(c, std::integral_constant<int, 0>{});
+    if (c + 1 < c_end) step(c + 1, std::integral_constant<int, 1>{});
+    wait_vmem<0>();   // no direct load may land after the work-group ends
+
+    float *dst = p.ws_E + (bhl * p.ws_slots + seg) * long(D) * D;
+    if (w == 0)
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) p.ws_G[(bhl * p.ws_slots + seg) * D + lane * CPL + u] = seg_gamma[u];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
+}
+
 // Exclusive scan of the state-pass maps: E_j <- S_start(j+1) in place.
 // One thread per (head, key dim, value column).
 __global__ void __launch_bounds__(256)
@@ -889,11 +1115,20 @@ static hipError_t launch_one(const KernelParams &p, int grid_x, int grid_y, hipS
     return hipGetLastError();
 }
 
+template <int D, int C>
+static hipError_t launch_state(const KernelParams &p, int grid_x, int grid_y, hipStream_t s) {
+    if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
+    hipLaunchKernelGGL((state_kernel<D, C>), dim3(grid_x, grid_y), dim3(Shape<D, C>::NW * 64), 0, s, p);
+    return hipGetLastError();
+}
+
 template <typename E, int D, int C>
 static hipError_t dispatch_mode(int mode, const KernelParams &p, int gx, int gy, hipStream_t s) {
     switch (mode) {
         case MODE_OUT: return launch_one<E, D, C, MODE_OUT>(p, gx, gy, s);
-        case MODE_SEG: return launch_one<E, D, C, MODE_SEG>(p, gx, gy, s);
+        case MODE_SEG:
+            if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C>(p, gx, gy, s);
+            else return launch_one<E, D, C, MODE_SEG>(p, gx, gy, s);
         case MODE_INTRA: return launch_one<E, D, C, MODE_INTRA>(p, gx, gy, s);
         case MODE_CUMSUM: return launch_one<E, D, C, MODE_CUMSUM>(p, gx, gy, s);
         default: return hipErrorInvalidValue;
@@ -913,6 +1148,22 @@ hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, const KernelPa
         if (D == 128 && C == 32) return dispatch_mode<F32, 128, 32>(mode, p, gx, gy, s);
     }
     return hipErrorInvalidValue;
+}
+
+int state_units_per_cu(int dtype, int D, int C) {
+    int bytes = 0;
+    if (dtype == DTYPE_BF16) {
+        if (D == 128 && C == 64) bytes = StateLayout<128, 64>::bytes;
+        if (D == 128 && C == 32) bytes = StateLayout<128, 32>::bytes;
+        if (D == 64 && C == 64) bytes = StateLayout<64, 64>::bytes;
+        if (D == 64 && C == 32) bytes = StateLayout<64, 32>::bytes;
+    } else if (dtype == DTYPE_F32) {
+        if (D == 64 && C == 64) bytes = Layout<F32, 64, 64, MODE_SEG>::bytes;
+        if (D == 64 && C == 32) bytes = Layout<F32, 64, 32, MODE_SEG>::bytes;
+        if (D == 128 && C == 32) bytes = Layout<F32, 128, 32, MODE_SEG>::bytes;
+    }
+    if (bytes <= 0) return 1;
+    return std::max(1, std::min(2, 163840 / bytes));
 }
 
 bool chunk_supported(int dtype, int D, int C) {
