@@ -131,12 +131,14 @@ def summarize_counters(outdir: str, wl_name: str):
         with open(p) as f:
             rows = list(csv.DictReader(f))
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        last_chunk = max((int(r["Dispatch_Id"]) for r in rows if "chunk_kernel" in r["Kernel_Name"]),
-                         default=-1)
+        last_chunk = max((int(r["Dispatch_Id"]) for r in rows
+                          if "chunk_kernel" in r["Kernel_Name"] or "state_kernel" in r["Kernel_Name"]), default=-1)
         for r in rows:
             name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
             if "chunk_kernel" in name:
                 kind = {"0": "output", "1": "segment"}.get(name.split(",")[3].strip(" >")[:1])
+            elif "state_kernel" in name:
+                kind = "segment"
             elif "scan_kernel" in name:
                 kind = "scan"
             elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_chunk:
