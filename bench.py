@@ -19,6 +19,14 @@ algorithmic bytes of the workload (bf16 q, k, v, o + fp32 g per token-head,
 plus the fp32 final state); ``cpu_baseline`` is the fp64 oracle timed on the
 host cores over a bounded sample of the same workload.
 
+Decode (a separate line, not the headline):
+    python bench.py --workload decode_b256 [--steps K] [--warmup W]
+A step is one gla_decode call: one token for each of B sequences x H heads
+against a carried fp32 state, updated in place.  ``value`` is decode
+tokens/s = B / step time; ``roofline`` prices the decode kernel against HBM
+bandwidth with its algorithmic bytes (fp32 state read + written, bf16 q, k,
+v, o and fp32 g per (batch, head) row).
+
 Helpers for the counter runs (used under rocprofv3):
     --copy-calibration  also runs a plain device copy of known size, so
                         FETCH_SIZE / WRITE_SIZE can be scaled to bytes
@@ -45,6 +53,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "prefill tokens/s, chunk GLA fwd H=16 D=128 bf16; % MFMA peak / HBM BW"
+DECODE_METRIC = "decode tokens/s, GLA decode step H=16 D=128 bf16 q/k/v/o, fp32 state; % HBM BW"
 # The pages' number for this workload (FLA chunk_gla, RTX 4090, bf16, H=16,
 # D=128, B=1, T=16K: 2.17 ms) as tokens/s: another machine, context only.
 PAGES_TOKENS_PER_S = {"prefill_16k": 1 * 16384 / 2.17e-3, "prefill_4k": 1 * 4096 / 0.47e-3}
@@ -61,6 +70,12 @@ def algorithmic_bytes(wl) -> int:
     per_token_head = wl.D * (4 * es + 4)          # 1536 B at D=128, bf16
     state = wl.B * wl.H * wl.D * wl.D * 4
     return th * per_token_head + (state if wl.want_final else 0) + (state if wl.h0_std else 0)
+
+
+def decode_bytes(wl) -> int:
+    """Per (batch, head) row: the fp32 D x D state read and written, bf16 q, k,
+    v, o (2 B each) and fp32 g (4 B) of D elements."""
+    return wl.B * wl.H * (2 * wl.D * wl.D * 4 + wl.D * (4 * 2 + 4))
 
 
 def algorithmic_flops(wl, chunk: int) -> int:
@@ -113,6 +128,115 @@ def cpu_baseline(wl, x, budget_s: float = 20.0, min_s: float = 10.0):
             "seconds": round(sum(times), 3)}
 
 
+def cpu_baseline_decode(wl, x, min_s: float = 10.0):
+    """Time the fp64 oracle for one decode step (the recurrence over T = 1
+    from the carried state) on the host over the first sequences' rows,
+    repeated until min_s has passed; scaled to decode tokens/s of all rows."""
+    import numpy as np
+    import oracle
+    from chunked_state_recurrence_amd.workloads import to_f64_numpy
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    nb = min(wl.B, 64)
+    f = {n: np.ascontiguousarray(to_f64_numpy(x[n][:nb])) for n in ("q", "k", "v", "g", "h0")}
+    times = []
+    while sum(times) < min_s:
+        t0 = time.perf_counter()
+        oracle.token_recurrence(f["q"], f["k"], f["v"], f["g"], f["h0"], wl.scale, threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.mean(times) * wl.B / nb
+    return {"value": wl.B / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nb * wl.H} of {wl.B * wl.H} (batch, head) rows, one fp64 decode step "
+                      f"each, {len(times)} passes of {statistics.mean(times) * 1e3:.1f} ms; "
+                      "scaled to all rows",
+            "seconds": round(sum(times), 3)}
+
+
+def copy_calibration(dev):
+    """A plain device copy of COPY_BYTES, three times, for counter scaling."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def bench_decode(args, wl):
+    import torch
+
+    import chunked_state_recurrence_amd as gla
+    from chunked_state_recurrence_amd.workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    host = make_inputs(wl)
+    sets = []
+    for s in range(2):  # two independent sets (2 x 256 MiB of state) alternate
+        d = {n: host[n][:, :, 0].contiguous().to(dev) for n in ("q", "k", "v", "g")}
+        d["state"] = host["h0"].to(dev)
+        d["o"] = torch.empty(wl.B, wl.H, wl.D, dtype=torch.bfloat16, device=dev)
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        d = sets[i & 1]
+        gla.gla_decode(d["q"], d["k"], d["v"], d["g"], d["state"], scale=wl.scale, o=d["o"],
+                       stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+
+    gla.profile_start(args.steps + 8)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kms = [t for kind, t in gla.profile_stop() if kind == "decode"]
+    k_ms = statistics.mean(kms)
+    per_launch = decode_bytes(wl)
+    achieved = per_launch / (k_ms * 1e-3) / 1e9
+    if args.copy_calibration:
+        copy_calibration(dev)
+    traffic = None
+    c = read_counters(wl.name)
+    if c and "fetch_factor" in c:
+        m = c["median_per_dispatch_KiB"]
+        f, w = m.get("decode:FETCH_SIZE"), m.get("decode:WRITE_SIZE")
+        if f is not None and w is not None:
+            traffic = int(f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"])
+    res = {
+        "metric": DECODE_METRIC,
+        "value": wl.B / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "K": wl.D, "V": wl.D,
+                   "state": "fp32, updated in place", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "decode_kernel<BF16,128>", "kernel_ms": k_ms,
+                     "algorithmic_bytes_per_launch": per_launch},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_decode(wl, host)
+    print(json.dumps(res), flush=True)
+
+
 def read_counters(wl_name: str):
     path = os.path.join(ROOT, "profiles", f"counters_{wl_name}.json")
     if not os.path.exists(path):
@@ -136,7 +260,9 @@ def summarize_counters(outdir: str, wl_name: str):
             rows = list(csv.DictReader(f))
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         last_chunk = max((int(r["Dispatch_Id"]) for r in rows
-                          if "chunk_kernel" in r["Kernel_Name"] or "state_kernel" in r["Kernel_Name"]), default=-1)
+                          if any(s in r["Kernel_Name"]
+                                 for s in ("chunk_kernel", "state_kernel", "decode_kernel"))),
+                         default=-1)
         for r in rows:
             name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
             if "chunk_kernel" in name:
@@ -145,6 +271,8 @@ def summarize_counters(outdir: str, wl_name: str):
                 kind = "segment"
             elif "scan_kernel" in name:
                 kind = "scan"
+            elif "decode_kernel" in name:
+                kind = "decode"
             elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_chunk:
                 kind = "copy"
             else:
@@ -192,8 +320,11 @@ def main():
     import torch
 
     import chunked_state_recurrence_amd as gla
-    from chunked_state_recurrence_amd.workloads import WORKLOADS, make_inputs
+    from chunked_state_recurrence_amd.workloads import DECODE_WORKLOADS, WORKLOADS, make_inputs
 
+    if args.workload in DECODE_WORKLOADS:
+        bench_decode(args, DECODE_WORKLOADS[args.workload])
+        return
     wl = WORKLOADS[args.workload]
     if wl.dtype != "bf16":
         raise SystemExit("bench.py measures the bf16 workloads")
@@ -250,12 +381,8 @@ def main():
     per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     traced_ms = ev[0].elapsed_time(ev[-1]) / args.steps
 
-    if args.copy_calibration:  # a plain copy of known size for counter scaling
-        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(dev)
 
     by_kind = {}
     for kind, kms in kernels:

@@ -1,4 +1,5 @@
-"""ctypes binding of libgla.so (include/gla.h, include/gla_stages.h).
+"""ctypes binding of libgla.so (include/gla.h, include/gla_decode.h,
+include/gla_stages.h).
 
 Argument marshalling only: shape/dtype/device checks, output allocation with
 torch, and the call.  Every step of the computation runs in the HIP kernels
@@ -25,8 +26,8 @@ ERRORS = {
 # every symbol include/gla.h and include/gla_stages.h declare
 EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_version",
             "gla_release", "gla_profile_start", "gla_profile_stop", "gla_stage_cumsum",
-            "gla_stage_intra", "gla_stage_states")
-KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other"}
+            "gla_stage_intra", "gla_stage_states", "gla_decode", "gla_decode_f32")
+KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode"}
 
 
 class _KernelTime(ctypes.Structure):
@@ -62,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     lib.gla_stage_states.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_stage_cumsum.argtypes = [P, P, P, I, I, I, I, I, P]
     lib.gla_stage_intra.argtypes = [P, P, P, P, I, I, I, I, I, F, P]
+    lib.gla_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
+    lib.gla_decode_f32.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
     lib.gla_set_tuning.argtypes = [I, I]
     lib.gla_strerror.argtypes = [I]
     lib.gla_strerror.restype = ctypes.c_char_p
@@ -73,7 +76,7 @@ def load_library(path: str = LIB_PATH):
     lib.gla_profile_start.restype = ctypes.c_int
     lib.gla_profile_stop.restype = ctypes.c_int
     for name in ("gla_fwd", "gla_fwd_f32", "gla_stage_states", "gla_stage_cumsum",
-                 "gla_stage_intra", "gla_set_tuning", "gla_version"):
+                 "gla_stage_intra", "gla_set_tuning", "gla_version", "gla_decode", "gla_decode_f32"):
         getattr(lib, name).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -148,6 +151,37 @@ def gla_fwd_f32(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=False, o
     """fp32 forward: the same operation with fp32 q, k, v and o."""
     return _fwd(load_library().gla_fwd_f32, torch.float32, q, k, v, g, h0, chunk, scale,
                 want_final, o, h_final, stream)
+
+
+def _decode(fn, io_dtype, q, k, v, g, state, scale, o, stream):
+    B, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    for t, n, dt, shp in ((q, "q", io_dtype, (B, H, K)), (k, "k", io_dtype, (B, H, K)),
+                          (v, "v", io_dtype, (B, H, V)), (g, "g", torch.float32, (B, H, K)),
+                          (state, "state", torch.float32, (B, H, K, V))):
+        if t is None:
+            raise ValueError(f"{n} is required")
+        _need(t, n, dt, shp, dev)
+    if scale is None:
+        scale = K ** -0.5
+    if o is None:
+        o = torch.empty((B, H, V), dtype=io_dtype, device=dev)
+    _need(o, "o", io_dtype, (B, H, V), dev)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _ptr(o), B, H, K, V, float(scale),
+              _stream(stream)))
+    return o
+
+
+def gla_decode(q, k, v, g, state, *, scale=None, o=None, stream=None):
+    """One decode step, bf16: q, k bf16 [B,H,K], v bf16 [B,H,V], g fp32 [B,H,K];
+    state fp32 [B,H,K,V] is updated in place.  Returns o bf16 [B,H,V]."""
+    return _decode(load_library().gla_decode, torch.bfloat16, q, k, v, g, state, scale, o, stream)
+
+
+def gla_decode_f32(q, k, v, g, state, *, scale=None, o=None, stream=None):
+    """One decode step with fp32 q, k, v and o."""
+    return _decode(load_library().gla_decode_f32, torch.float32, q, k, v, g, state, scale, o, stream)
 
 
 def gla_stage_states(q, k, v, g, h0=None, *, chunk=64, scale=None, stream=None):

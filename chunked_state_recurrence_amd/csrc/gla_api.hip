@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "gla.h"
+#include "gla_decode.h"
 #include "gla_stages.h"
 #include "gla_internal.h"
 
@@ -153,8 +154,8 @@ struct Plan {
     int slots;  // state-pass units before the last output segment: (P - 1) * sub
 };
 
-// Output pass: about `target` work-groups (one per CU).  State pass: finer
-// units, about twice as many work-groups, since it fits two per CU.
+// Output pass: about `target` work-groups (one per CU).  State pass: units
+// that end on segment boundaries, about state_per_cu work-groups per CU.
 Plan plan_segments(int nbh, int N, int target, int state_per_cu) {
     int P = std::max(1, (target + nbh - 1) / nbh);
     P = std::min(P, N);
@@ -260,6 +261,47 @@ int gla_fwd_f32(const float *q, const float *k, const float *v, const float *g, 
     Call c{gla::DTYPE_F32, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
            static_cast<hipStream_t>(stream)};
     return run_forward(c);
+}
+
+// One decode step (include/gla_decode.h).
+static int decode_call(int dtype, const void *q, const void *k, const void *v, const float *g,
+                       float *state, void *o, int B, int H, int K, int V, float scale, hipStream_t stream) {
+    if (B <= 0 || H <= 0 || K <= 0 || V <= 0) return GLA_ERR_SHAPE;
+    if (long(B) * H > (1L << 30)) return GLA_ERR_SHAPE;
+    if (K != V || (K != 64 && K != 128)) return GLA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !g || !state || !o) return GLA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, state, o};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return GLA_ERR_ALIGN;
+    const size_t es = dtype == gla::DTYPE_BF16 ? 2 : 4;
+    const size_t bh = size_t(B) * H;
+    const size_t nvec = bh * K * es, ng = bh * K * 4, nst = bh * K * V * 4;
+    struct R { const void *p; size_t n; } ins[] = {{q, nvec}, {k, nvec}, {v, nvec}, {g, ng}};
+    for (const R &r : ins) {
+        if (overlaps(o, nvec, r.p, r.n)) return GLA_ERR_ALIAS;
+        if (overlaps(state, nst, r.p, r.n)) return GLA_ERR_ALIAS;
+    }
+    if (overlaps(state, nst, o, nvec)) return GLA_ERR_ALIAS;
+    DeviceState *dev = nullptr;
+    int rc = current_device(&dev);
+    if (rc != GLA_OK) return rc;
+    if (traced(GLA_KERNEL_DECODE, stream, [&] {
+            return gla::launch_decode(dtype, K, q, k, v, g, state, o, long(bh), scale, stream);
+        }) != hipSuccess)
+        return GLA_ERR_LAUNCH;
+    return GLA_OK;
+}
+
+int gla_decode(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g, float *state,
+               gla_bf16 *o, int B, int H, int K, int V, float scale, void *stream) {
+    return decode_call(gla::DTYPE_BF16, q, k, v, g, state, o, B, H, K, V, scale,
+                       static_cast<hipStream_t>(stream));
+}
+
+int gla_decode_f32(const float *q, const float *k, const float *v, const float *g, float *state,
+                   float *o, int B, int H, int K, int V, float scale, void *stream) {
+    return decode_call(gla::DTYPE_F32, q, k, v, g, state, o, B, H, K, V, scale,
+                       static_cast<hipStream_t>(stream));
 }
 
 int gla_stage_states(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g,

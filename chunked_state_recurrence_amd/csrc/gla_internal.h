@@ -41,5 +41,8 @@ hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, const KernelPa
 hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,
                        int slots, int D, hipStream_t s);
 hipError_t launch_copy_state(float *dst, const float *src, long n, hipStream_t s);
+// one decode step for nbh (batch, head) rows, state [nbh][D][D] updated in place
+hipError_t launch_decode(int dtype, int D, const void *q, const void *k, const void *v, const float *g,
+                         float *state, void *o, long nbh, float scale, hipStream_t s);
 
 }  // namespace gla

@@ -1098,6 +1098,68 @@ scan_kernel(float *__restrict__ ws_E, const float *__restrict__ ws_G,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode step: one new token per (batch, head), the state updated in place,
+//   S <- diag(exp g) S + k^T v,   o = scale q S   (update, then read out)
+// the same recurrence one token at a time (blog "Linear Attention 在 GPU 上到底
+// 慢在哪", section 学长的反馈; "线性注意力GPU算子库的定义与技术解析", section 四).
+// Bound by the state traffic: each (batch, head) reads and writes D*D fp32.
+// Work-group = 32 value columns of one (batch, head); thread t owns columns
+// c0 + 4 (t % 8) .. +3 and rows t / 8 + 32 i.
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+__global__ void __launch_bounds__(256)
+decode_kernel(const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
+              const float *__restrict__ g, float *__restrict__ state, void *__restrict__ o, float scale) {
+    using gmem_t = typename E::gmem_t;
+    constexpr int CB = 32;   // value columns per work-group
+    constexpr int RB = 32;   // row groups (256 threads = 32 row groups x 8 column quads)
+    const long bh = blockIdx.x;
+    const int c0 = blockIdx.y * CB;
+    const int t = threadIdx.x;
+    const int cq = t & 7;
+    const int rb = t >> 3;
+    const gmem_t *qp = reinterpret_cast<const gmem_t *>(q) + bh * D;
+    const gmem_t *kp = reinterpret_cast<const gmem_t *>(k) + bh * D;
+    const gmem_t *vp = reinterpret_cast<const gmem_t *>(v) + bh * D;
+    const float *gp = g + bh * D;
+    float *S = state + bh * D * D + c0 + 4 * cq;
+    float vv[4], acc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        vv[e] = E::g2f(vp[c0 + 4 * cq + e]);
+        acc[e] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < D / RB; ++i) {
+        const int r = rb + RB * i;
+        const float dec = fexp2(gp[r] * kLog2e);
+        const float kr = E::g2f(kp[r]), qr = E::g2f(qp[r]);
+        f32x4_t sv = *reinterpret_cast<const f32x4_t *>(S + r * D);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = __builtin_fmaf(kr, vv[e], dec * sv[e]);
+            acc[e] = __builtin_fmaf(qr, sv[e], acc[e]);
+        }
+        *reinterpret_cast<f32x4_t *>(S + r * D) = sv;
+    }
+    // sum over the row groups: 8 per wave (lane / 8), then over the 4 waves
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int m = 8; m <= 32; m <<= 1) acc[e] += __shfl_xor(acc[e], m, 64);
+    __shared__ float red[4][CB];
+    if ((t & 63) < 8)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[t >> 6][4 * cq + e] = acc[e];
+    __syncthreads();
+    if (t < CB) {
+        const float x = scale * (red[0][t] + red[1][t] + red[2][t] + red[3][t]);
+        if constexpr (sizeof(gmem_t) == 2) reinterpret_cast<__bf16 *>(o)[bh * D + c0 + t] = (__bf16)x;
+        else reinterpret_cast<float *>(o)[bh * D + c0 + t] = x;
+    }
+}
+
 // T == 0: h_final <- h0 (or 0).
 __global__ void __launch_bounds__(256)
 copy_state_kernel(float *__restrict__ dst, const float *__restrict__ src, long n) {
@@ -1177,6 +1239,22 @@ hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0
     const long n = long(nbh) * D * D;
     const long blocks = (n + 255) / 256;
     hipLaunchKernelGGL(scan_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, ws_E, ws_G, h0, bh0, nbh, slots, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(int dtype, int D, const void *q, const void *k, const void *v, const float *g,
+                         float *state, void *o, long nbh, float scale, hipStream_t s) {
+    if (nbh <= 0) return hipSuccess;
+    const dim3 grid(unsigned(nbh), unsigned(D / 32));
+    if (dtype == DTYPE_BF16) {
+        if (D == 128) hipLaunchKernelGGL((decode_kernel<BF16, 128>), grid, dim3(256), 0, s, q, k, v, g, state, o, scale);
+        else if (D == 64) hipLaunchKernelGGL((decode_kernel<BF16, 64>), grid, dim3(256), 0, s, q, k, v, g, state, o, scale);
+        else return hipErrorInvalidValue;
+    } else {
+        if (D == 128) hipLaunchKernelGGL((decode_kernel<F32, 128>), grid, dim3(256), 0, s, q, k, v, g, state, o, scale);
+        else if (D == 64) hipLaunchKernelGGL((decode_kernel<F32, 64>), grid, dim3(256), 0, s, q, k, v, g, state, o, scale);
+        else return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -21,6 +21,12 @@ normal, h0; values drawn in float32):
 
 The pages measure on synthetic shapes only (B, H, T, D sweeps); no dataset
 stands behind these numbers, and none is used here.
+
+Decode workloads (DECODE_WORKLOADS) draw the same way with T = 1: one new
+token per (batch, head) and a carried fp32 state drawn as h0.  The pages do
+not measure decode; the batch is sized so that the state of one step
+(B*H*D*D*4 bytes, 256 MiB at B=256, H=16, D=128) is as large as the MI355X
+Infinity Cache, and two such sets alternate in the benchmark.
 """
 
 from __future__ import annotations
@@ -64,6 +70,12 @@ WORKLOADS = {
     "prefill_16k": Workload("prefill_16k", 1, 16, 16384, 128, "bf16", "l2", "ls16", None, True, None, 2),
     "batch16_4k": Workload("batch16_4k", 16, 16, 4096, 128, "bf16", "l2", "ls16", None, False, None, 3),
     "long_128k": Workload("long_128k", 1, 16, 131072, 128, "bf16", "l2", "ls41", 0.02, True, None, 4),
+}
+
+
+# Decode: B sequences x H heads each take one step against a carried state.
+DECODE_WORKLOADS = {
+    "decode_b256": Workload("decode_b256", 256, 16, 1, 128, "bf16", "l2", "ls16", 0.05, True, None, 5),
 }
 
 

@@ -3,6 +3,7 @@ headers declare, and rejects bad arguments with the documented codes before
 anything is enqueued (fake device pointers are never dereferenced)."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -11,7 +12,7 @@ import pytest
 import chunked_state_recurrence_amd as gla
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("gla.h", "gla_stages.h")]
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(gla.LIB_PATH),
                                 reason="libgla.so not built (run __graft_entry__.build())")
@@ -72,6 +73,31 @@ def _call(lib, **kw):
 def test_argument_errors(kw, code):
     lib = gla.load_library()
     assert _call(lib, **kw) == code
+
+
+def _decode(lib, f32=False, **kw):
+    a = dict(q=FAKE, k=FAKE + STEP, v=FAKE + 2 * STEP, g=FAKE + 3 * STEP, state=FAKE + 4 * STEP,
+             o=FAKE + 5 * STEP, B=2, H=3, K=128, V=128, scale=0.1)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    fn = lib.gla_decode_f32 if f32 else lib.gla_decode
+    return fn(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["state"]), vp(a["o"]),
+              a["B"], a["H"], a["K"], a["V"], a["scale"], None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(H=-1), -2), (dict(K=0, V=0), -2), (dict(B=1 << 16, H=1 << 15), -2),
+    (dict(K=128, V=64), -3), (dict(K=32, V=32), -3), (dict(K=256, V=256), -3),
+    (dict(q=None), -1), (dict(g=None), -1), (dict(state=None), -1), (dict(o=None), -1),
+    (dict(v=FAKE + 2 * STEP + 8), -4), (dict(state=FAKE + 4 * STEP + 4), -4),
+    (dict(o=FAKE + 64), -7),                      # o overlaps q
+    (dict(state=FAKE + 3 * STEP + 16), -7),       # state overlaps g
+    (dict(o=FAKE + 4 * STEP + 4096), -7),         # o inside state
+])
+def test_decode_argument_errors(kw, code, f32):
+    lib = gla.load_library()
+    assert _decode(lib, f32, **kw) == code
 
 
 def test_fp32_chunk_support_table():
