@@ -19,6 +19,11 @@ algorithmic bytes of the workload (bf16 q, k, v, o + fp32 g per token-head,
 plus the fp32 final state); ``cpu_baseline`` is the fp64 oracle timed on the
 host cores over a bounded sample of the same workload.
 
+Scalar gate (a separate line, not the headline):
+    python bench.py --workload prefill_16k_scalar
+the same step through gla_fwd_scalar (g [B,H,T]); its algorithmic bytes
+per token-head are 1028 at D=128 (bf16 q, k, v, o + one fp32 gate).
+
 Decode (a separate line, not the headline):
     python bench.py --workload decode_b256 [--steps K] [--warmup W]
 A step is one gla_decode call: one token for each of B sequences x H heads
@@ -53,6 +58,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "prefill tokens/s, chunk GLA fwd H=16 D=128 bf16; % MFMA peak / HBM BW"
+SCALAR_METRIC = "prefill tokens/s, chunk scalar-gate linear attention fwd H=16 D=128 bf16; % HBM BW"
 DECODE_METRIC = "decode tokens/s, GLA decode step H=16 D=128 bf16 q/k/v/o, fp32 state; % HBM BW"
 # The pages' number for this workload (FLA chunk_gla, RTX 4090, bf16, H=16,
 # D=128, B=1, T=16K: 2.17 ms) as tokens/s: another machine, context only.
@@ -63,11 +69,13 @@ COPY_BYTES = 1 << 30
 
 
 def algorithmic_bytes(wl) -> int:
-    """bf16 q, k, v, o (2 B each) + fp32 g (4 B) per token-head element row,
-    plus the fp32 h0 read and h_final write when present."""
+    """bf16 q, k, v, o (2 B each) + fp32 g (4 B; one per token for the scalar
+    gate) per token-head element row, plus the fp32 h0 read and h_final write
+    when present."""
     th = wl.B * wl.H * wl.T
     es = 2 if wl.dtype == "bf16" else 4
-    per_token_head = wl.D * (4 * es + 4)          # 1536 B at D=128, bf16
+    gate = 4 if wl.scalar_gate else wl.D * 4
+    per_token_head = wl.D * 4 * es + gate         # 1536 B at D=128, bf16 (scalar gate: 1028)
     state = wl.B * wl.H * wl.D * wl.D * 4
     return th * per_token_head + (state if wl.want_final else 0) + (state if wl.h0_std else 0)
 
@@ -110,8 +118,12 @@ def cpu_baseline(wl, x, budget_s: float = 20.0, min_s: float = 10.0):
                  np.stack([to_f64_numpy(x[n][b, h]) for (b, h) in sel])[None])
              for n in ("q", "k", "v", "g", "h0")}
         t0 = time.perf_counter()
-        oracle.token_recurrence(f["q"], f["k"], f["v"], f["g"], f["h0"], wl.scale,
-                                threads=threads)
+        if wl.scalar_gate:
+            oracle.scalar_gate_recurrence(f["q"], f["k"], f["v"], f["g"], f["h0"], wl.scale,
+                                          threads=threads)
+        else:
+            oracle.token_recurrence(f["q"], f["k"], f["v"], f["g"], f["h0"], wl.scale,
+                                    threads=threads)
         return time.perf_counter() - t0
 
     t1 = run(pairs[:1])
@@ -320,12 +332,14 @@ def main():
     import torch
 
     import chunked_state_recurrence_amd as gla
-    from chunked_state_recurrence_amd.workloads import DECODE_WORKLOADS, WORKLOADS, make_inputs
+    from chunked_state_recurrence_amd.workloads import (DECODE_WORKLOADS, SCALAR_WORKLOADS,
+                                                        WORKLOADS, make_inputs)
 
     if args.workload in DECODE_WORKLOADS:
         bench_decode(args, DECODE_WORKLOADS[args.workload])
         return
-    wl = WORKLOADS[args.workload]
+    wl = {**WORKLOADS, **SCALAR_WORKLOADS}[args.workload]
+    fwd = gla.gla_fwd_scalar if wl.scalar_gate else gla.gla_fwd
     if wl.dtype != "bf16":
         raise SystemExit("bench.py measures the bf16 workloads")
     dev = torch.device("cuda:0")
@@ -346,8 +360,8 @@ def main():
 
     def step(i):
         d = sets[i & 1]
-        gla.gla_fwd(d["q"], d["k"], d["v"], d["g"], d["h0"], chunk=chunk, scale=wl.scale,
-                    o=d["o"], h_final=d["hf"], want_final=wl.want_final, stream=stream)
+        fwd(d["q"], d["k"], d["v"], d["g"], d["h0"], chunk=chunk, scale=wl.scale,
+            o=d["o"], h_final=d["hf"], want_final=wl.want_final, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -401,7 +415,7 @@ def main():
             traffic = int(f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"])
 
     res = {
-        "metric": METRIC,
+        "metric": SCALAR_METRIC if wl.scalar_gate else METRIC,
         "value": wl.B * wl.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -415,6 +429,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.D, "V": wl.D,
                    "chunk": chunk, "h_final": wl.want_final, "h0": wl.h0_std is not None,
+                   "gate": "scalar [B,H,T]" if wl.scalar_gate else "per key dim [B,H,T,K]",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

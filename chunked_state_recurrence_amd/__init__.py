@@ -1,7 +1,8 @@
 """MI355X-native chunked gated linear attention (GLA) prefill forward.
 
 The computation lives in libgla.so (hand-written HIP kernels for gfx950 behind
-the C ABI in include/gla.h and include/gla_decode.h); this package is its thin Python binding.  Build
+the C ABI in include/gla.h, include/gla_scalar.h and
+include/gla_decode.h); this package is its thin Python binding.  Build
 the library with ``python -m chunked_state_recurrence_amd.build``.
 """
 
@@ -14,6 +15,8 @@ from ._binding import (  # noqa: F401
     gla_decode_f32,
     gla_fwd,
     gla_fwd_f32,
+    gla_fwd_scalar,
+    gla_fwd_scalar_f32,
     gla_stage_cumsum,
     gla_stage_intra,
     gla_stage_states,

@@ -1,5 +1,5 @@
-"""ctypes binding of libgla.so (include/gla.h, include/gla_decode.h,
-include/gla_stages.h).
+"""ctypes binding of libgla.so (include/gla.h, include/gla_scalar.h,
+include/gla_decode.h, include/gla_stages.h).
 
 Argument marshalling only: shape/dtype/device checks, output allocation with
 torch, and the call.  Every step of the computation runs in the HIP kernels
@@ -26,7 +26,8 @@ ERRORS = {
 # every symbol include/gla.h and include/gla_stages.h declare
 EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_version",
             "gla_release", "gla_profile_start", "gla_profile_stop", "gla_stage_cumsum",
-            "gla_stage_intra", "gla_stage_states", "gla_decode", "gla_decode_f32")
+            "gla_stage_intra", "gla_stage_states", "gla_decode", "gla_decode_f32",
+            "gla_fwd_scalar", "gla_fwd_scalar_f32")
 KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode"}
 
 
@@ -60,6 +61,8 @@ def load_library(path: str = LIB_PATH):
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.gla_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_fwd_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
+    lib.gla_fwd_scalar.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
+    lib.gla_fwd_scalar_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_stage_states.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_stage_cumsum.argtypes = [P, P, P, I, I, I, I, I, P]
     lib.gla_stage_intra.argtypes = [P, P, P, P, I, I, I, I, I, F, P]
@@ -76,7 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.gla_profile_start.restype = ctypes.c_int
     lib.gla_profile_stop.restype = ctypes.c_int
     for name in ("gla_fwd", "gla_fwd_f32", "gla_stage_states", "gla_stage_cumsum",
-                 "gla_stage_intra", "gla_set_tuning", "gla_version", "gla_decode", "gla_decode_f32"):
+                 "gla_stage_intra", "gla_set_tuning", "gla_version", "gla_decode", "gla_decode_f32",
+                 "gla_fwd_scalar", "gla_fwd_scalar_f32"):
         getattr(lib, name).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -112,12 +116,13 @@ def _need(t, name, dtype, shape, device):
 
 
 def _fwd(fn, io_dtype, q, k, v, g, h0, chunk, scale, want_final, o, h_final, stream,
-         states=None):
+         states=None, scalar_gate=False):
     B, H, T, K = q.shape
     V = v.shape[-1]
     dev = q.device
+    gshape = (B, H, T) if scalar_gate else (B, H, T, K)
     for t, n, dt, shp in ((q, "q", io_dtype, (B, H, T, K)), (k, "k", io_dtype, (B, H, T, K)),
-                          (v, "v", io_dtype, (B, H, T, V)), (g, "g", torch.float32, (B, H, T, K)),
+                          (v, "v", io_dtype, (B, H, T, V)), (g, "g", torch.float32, gshape),
                           (h0, "h0", torch.float32, (B, H, K, V))):
         _need(t, n, dt, shp, dev)
     if scale is None:
@@ -151,6 +156,21 @@ def gla_fwd_f32(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=False, o
     """fp32 forward: the same operation with fp32 q, k, v and o."""
     return _fwd(load_library().gla_fwd_f32, torch.float32, q, k, v, g, h0, chunk, scale,
                 want_final, o, h_final, stream)
+
+
+def gla_fwd_scalar(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=False, o=None,
+                   h_final=None, stream=None):
+    """Scalar-gate bf16 forward: as gla_fwd, with g fp32 [B,H,T] (one log-decay
+    per token and head, shared by every key dim)."""
+    return _fwd(load_library().gla_fwd_scalar, torch.bfloat16, q, k, v, g, h0, chunk, scale,
+                want_final, o, h_final, stream, scalar_gate=True)
+
+
+def gla_fwd_scalar_f32(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=False, o=None,
+                       h_final=None, stream=None):
+    """Scalar-gate fp32 forward: fp32 q, k, v, o; g fp32 [B,H,T]."""
+    return _fwd(load_library().gla_fwd_scalar_f32, torch.float32, q, k, v, g, h0, chunk, scale,
+                want_final, o, h_final, stream, scalar_gate=True)
 
 
 def _decode(fn, io_dtype, q, k, v, g, state, scale, o, stream):

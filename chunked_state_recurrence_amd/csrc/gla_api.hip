@@ -1,6 +1,6 @@
 // gla_api.hip — C ABI of libgla.so: argument validation, segment scheduling,
-// workspace, launches.  Declarations and contracts: include/gla.h and
-// include/gla_stages.h.
+// workspace, launches.  Declarations and contracts: include/gla.h,
+// include/gla_scalar.h, include/gla_decode.h and include/gla_stages.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -11,6 +11,7 @@
 
 #include "gla.h"
 #include "gla_decode.h"
+#include "gla_scalar.h"
 #include "gla_stages.h"
 #include "gla_internal.h"
 
@@ -111,6 +112,7 @@ struct Call {
     int B, H, T, K, V, chunk;
     float scale;
     hipStream_t stream;
+    bool scalar_gate = false;  // g is [B,H,T] instead of [B,H,T,K]
 };
 
 int default_chunk(int dtype, int D) {
@@ -131,7 +133,7 @@ int validate(Call &c) {
         if (misaligned(p)) return GLA_ERR_ALIGN;
     const size_t es = c.dtype == gla::DTYPE_BF16 ? 2 : 4;
     const size_t bht = size_t(c.B) * c.H * c.T;
-    const size_t nqk = bht * c.K * es, nv = bht * c.V * es, ng = bht * c.K * 4;
+    const size_t nqk = bht * c.K * es, nv = bht * c.V * es, ng = bht * (c.scalar_gate ? 1 : c.K) * 4;
     const size_t nst = size_t(c.B) * c.H * c.K * c.V * 4;
     const size_t nchunks = c.T > 0 ? size_t((c.T + c.chunk - 1) / c.chunk) : 0;
     const size_t nstates = size_t(c.B) * c.H * nchunks * c.K * c.V * 4;
@@ -225,7 +227,8 @@ int run_forward(Call &c) {
             ps.N = (c.T + cs - 1) / cs;
             ps.P = pl.slots;
             if (traced(GLA_KERNEL_SEGMENT, c.stream, [&] {
-                    return gla::launch_chunk_kernel(c.dtype, D, cs, gla::MODE_SEG, ps, pl.slots, nbh, c.stream);
+                    return gla::launch_chunk_kernel(c.dtype, D, cs, gla::MODE_SEG, c.scalar_gate, ps, pl.slots,
+                                                    nbh, c.stream);
                 }) != hipSuccess)
                 return GLA_ERR_LAUNCH;
             if (traced(GLA_KERNEL_SCAN, c.stream, [&] {
@@ -236,7 +239,8 @@ int run_forward(Call &c) {
         p.cps = pl.cps;
         p.P = pl.P;
         if (traced(GLA_KERNEL_OUTPUT, c.stream, [&] {
-                return gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_OUT, p, pl.P, nbh, c.stream);
+                return gla::launch_chunk_kernel(c.dtype, D, c.chunk, gla::MODE_OUT, c.scalar_gate, p, pl.P, nbh,
+                                                c.stream);
             }) != hipSuccess)
             return GLA_ERR_LAUNCH;
     }
@@ -260,6 +264,23 @@ int gla_fwd_f32(const float *q, const float *k, const float *v, const float *g, 
                 void *stream) {
     Call c{gla::DTYPE_F32, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
            static_cast<hipStream_t>(stream)};
+    return run_forward(c);
+}
+
+// Scalar-gate forward (include/gla_scalar.h): g is [B,H,T].
+int gla_fwd_scalar(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g,
+                   const float *h0, gla_bf16 *o, float *h_final, int B, int H, int T, int K, int V,
+                   int chunk, float scale, void *stream) {
+    Call c{gla::DTYPE_BF16, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
+           static_cast<hipStream_t>(stream), true};
+    return run_forward(c);
+}
+
+int gla_fwd_scalar_f32(const float *q, const float *k, const float *v, const float *g, const float *h0,
+                       float *o, float *h_final, int B, int H, int T, int K, int V, int chunk, float scale,
+                       void *stream) {
+    Call c{gla::DTYPE_F32, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
+           static_cast<hipStream_t>(stream), true};
     return run_forward(c);
 }
 
@@ -341,7 +362,7 @@ static int run_stage(int mode, const void *q, const void *k, const float *g, flo
         p.bh0 = g0;
         const int nbh = int(std::min<long>(65535, BH - g0));
         if (traced(GLA_KERNEL_OTHER, c.stream, [&] {
-                return gla::launch_chunk_kernel(c.dtype, K, c.chunk, mode, p, N, nbh, c.stream);
+                return gla::launch_chunk_kernel(c.dtype, K, c.chunk, mode, false, p, N, nbh, c.stream);
             }) != hipSuccess)
             return GLA_ERR_LAUNCH;
     }

@@ -36,8 +36,9 @@ struct KernelParams {
 bool chunk_supported(int dtype, int D, int C);
 // work-groups of the state pass that fit on one CU (LDS bound), 1 or 2
 int state_units_per_cu(int dtype, int D, int C);
-hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, const KernelParams &p,
-                               int grid_x, int grid_y, hipStream_t s);
+// scalar_gate: g is [B,H,T] (one log-decay per token), MODE_OUT / MODE_SEG only
+hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, bool scalar_gate,
+                               const KernelParams &p, int grid_x, int grid_y, hipStream_t s);
 hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,
                        int slots, int D, hipStream_t s);
 hipError_t launch_copy_state(float *dst, const float *src, long n, hipStream_t s);

@@ -251,14 +251,23 @@ template <> struct Raw<F32, 1> {
     }
 };
 template <int CPL> struct RawG;
+// Scalar gates (one per token) use the same registers: load_one / fill put
+// the token's gate in every column slot.
 template <> struct RawG<2> {
     u32x2_t x;
     __device__ void load(rsrc_t r, int off, int soff) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0); }
+    __device__ void load_one(rsrc_t r, int off, int soff) {
+        const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+        x = u32x2_t{u, u};
+    }
+    __device__ void fill(float f) { x = u32x2_t{__float_as_uint(f), __float_as_uint(f)}; }
     __device__ float get(int u) const { return __uint_as_float(u ? x.y : x.x); }
 };
 template <> struct RawG<1> {
     uint32_t x;
     __device__ void load(rsrc_t r, int off, int soff) { x = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
+    __device__ void load_one(rsrc_t r, int off, int soff) { load(r, off, soff); }
+    __device__ void fill(float f) { x = __float_as_uint(f); }
     __device__ float get(int) const { return __uint_as_float(x); }
 };
 
@@ -325,7 +334,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 //    formed elementwise from running products of per-token decays (factors
 //    in (0, 1], so nothing overflows and underflow is the true value).
 // Q and the state-update operand are bounded (exponents <= 0) on both paths.
-template <typename E, int D, int C, int MODE>
+// SG: scalar gate, g [B,H,T] (one log-decay per token, shared by every key
+// dim); each wave stages its rows' gates and reads them back broadcast over
+// the key dims, after which the arithmetic is the per-key-dim one.
+template <typename E, int D, int C, int MODE, bool SG>
 __global__ void __launch_bounds__((Shape<D, C>::NW * 64))
 chunk_kernel(const KernelParams p) {
     constexpr int NW = Shape<D, C>::NW;    // waves
@@ -357,7 +369,7 @@ chunk_kernel(const KernelParams p) {
     lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);    // state pass: v^T
     // Direct-load targets in arrays of their own, so the compiler can tell
     // that fragment reads elsewhere do not touch loads still landing here.
-    __shared__ __attribute__((aligned(16))) float sG[C * D];                   // gate rows
+    __shared__ __attribute__((aligned(16))) float sG[SG ? C : C * D];          // gate rows
     __shared__ __attribute__((aligned(16))) unsigned char sV[L::vbytes];       // v rows (pitch L::VP)
     lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);      // scaled scores, row-major
     float *sDec = reinterpret_cast<float *>(smem + L::dec);  // exact path: exp(g) per token
@@ -381,7 +393,8 @@ chunk_kernel(const KernelParams p) {
     const gmem_t *gq = reinterpret_cast<const gmem_t *>(p.q) + bh * long(T) * D;
     const gmem_t *gk = reinterpret_cast<const gmem_t *>(p.k) + bh * long(T) * D;
     const gmem_t *gv = reinterpret_cast<const gmem_t *>(p.v) + bh * long(T) * D;
-    const float *gg = p.g + bh * long(T) * D;
+    constexpr int GD = SG ? 1 : D;            // gates per token
+    const float *gg = p.g + bh * long(T) * GD;
 
     // ---- state init ---------------------------------------------------------
     f32x4_t S[MT][NTW];
@@ -414,20 +427,25 @@ chunk_kernel(const KernelParams p) {
     const rsrc_t bq = make_rsrc(gq, long(T) * D * es);
     const rsrc_t bk = make_rsrc(gk, long(T) * D * es);
     const rsrc_t bv = make_rsrc(gv, long(T) * D * es);
-    const rsrc_t bg = make_rsrc(gg, long(T) * D * 4);
+    const rsrc_t bg = make_rsrc(gg, long(T) * GD * 4);
     // Issue counts per wave, for the explicit waits: gate rows (direct, 1 KB
-    // per load), register rows of q / k (/ v in the state pass), v rows.
-    constexpr int NG = RPW * D * 4 / 1024;
+    // per load; one load of RPW floats for scalar gates), register rows of
+    // q / k (/ v in the state pass), v rows.
+    constexpr int NG = SG ? 1 : RPW * D * 4 / 1024;
     constexpr int NQK = (kScores ? RPW : 0) + (kCumsum ? 0 : RPW) + (kVreg ? RPW : 0);
     constexpr int NV = !kVdma ? 0 : (es == 2 ? RPW : RPW * D * 4 / 1024);
     static_assert(RPW * D * 4 % 1024 == 0, "gate rows per wave must fill whole loads");
     // this wave's gate rows of chunk c into its rows of sG (rows past T read 0)
     auto load_g = [&](int c) {
-        const int rbase = __builtin_amdgcn_readfirstlane((c * C + r0) * D * 4);
-        float *dst = sG + __builtin_amdgcn_readfirstlane(r0 * D);
+        const int rbase = __builtin_amdgcn_readfirstlane((c * C + r0) * GD * 4);
+        float *dst = sG + __builtin_amdgcn_readfirstlane(r0 * GD);
         mem_fence_compiler();
+        if constexpr (SG) {
+            if (lane < RPW) dma<4>(bg, reinterpret_cast<unsigned char *>(dst), lane * 4, rbase);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NG; ++i) dma<16>(bg, reinterpret_cast<unsigned char *>(dst) + i * 1024, lane * 16, rbase + i * 1024);
+            for (int i = 0; i < NG; ++i) dma<16>(bg, reinterpret_cast<unsigned char *>(dst) + i * 1024, lane * 16, rbase + i * 1024);
+        }
         mem_fence_compiler();
     };
     // rows past T read as zero; row offsets go in the uniform soffset
@@ -520,7 +538,10 @@ chunk_kernel(const KernelParams p) {
         wait_vmem<NQK + NV>();
         RawG<CPL> rg[RPW];   // each wave reads back only the rows it loaded itself
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) rg[i].x = *reinterpret_cast<const decltype(rg[i].x) *>(sG + (r0 + i) * D + lane * CPL);
+        for (int i = 0; i < RPW; ++i) {
+            if constexpr (SG) rg[i].fill(sG[r0 + i]);
+            else rg[i].x = *reinterpret_cast<const decltype(rg[i].x) *>(sG + (r0 + i) * D + lane * CPL);
+        }
         float Pf[RPW][CPL];   // inclusive prefix within the wave's rows
         float Sw[RPW][CPL];   // state pass: suffix after the row within the wave's rows
 #pragma unroll
@@ -876,7 +897,7 @@ template <int D, int C> struct StateLayout {
     static_assert(bytes <= 163840, "state pass LDS");
 };
 
-template <int D, int C>
+template <int D, int C, bool SG>
 __global__ void __launch_bounds__((Shape<D, C>::NW * 64))
 state_kernel(const KernelParams p) {
     using E = BF16;
@@ -918,7 +939,8 @@ state_kernel(const KernelParams p) {
 
     const rsrc_t bk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + bh * long(T) * D, long(T) * D * 2);
     const rsrc_t bv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + bh * long(T) * D, long(T) * D * 2);
-    const rsrc_t bg = make_rsrc(p.g + bh * long(T) * D, long(T) * D * 4);
+    constexpr int GD = SG ? 1 : D;   // gates per token (SG: one scalar gate per token)
+    const rsrc_t bg = make_rsrc(p.g + bh * long(T) * GD, long(T) * GD * 4);
 
     RawG<CPL> rg0[RPW], rg1[RPW], rg2[RPW];   // gate rows of the three stages
 
@@ -929,7 +951,10 @@ state_kernel(const KernelParams p) {
         const int lr0 = __builtin_amdgcn_readfirstlane(r0);
         mem_fence_compiler();
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) tg[i].load(bg, (row0 * D + lane * CPL) * 4, i * D * 4);
+        for (int i = 0; i < RPW; ++i) {
+            if constexpr (SG) tg[i].load_one(bg, row0 * 4, i * 4);   // same address in every lane
+            else tg[i].load(bg, (row0 * D + lane * CPL) * 4, i * D * 4);
+        }
 #pragma unroll
         for (int i = 0; i < NKL; ++i)
             dma<16>(bk, tk + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
@@ -1170,44 +1195,54 @@ copy_state_kernel(float *__restrict__ dst, const float *__restrict__ src, long n
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C, int MODE>
+template <typename E, int D, int C, int MODE, bool SG>
 static hipError_t launch_one(const KernelParams &p, int grid_x, int grid_y, hipStream_t s) {
     if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_kernel<E, D, C, MODE>), dim3(grid_x, grid_y), dim3(Shape<D, C>::NW * 64), 0, s, p);
+    hipLaunchKernelGGL((chunk_kernel<E, D, C, MODE, SG>), dim3(grid_x, grid_y), dim3(Shape<D, C>::NW * 64), 0, s, p);
     return hipGetLastError();
 }
 
-template <int D, int C>
+template <int D, int C, bool SG>
 static hipError_t launch_state(const KernelParams &p, int grid_x, int grid_y, hipStream_t s) {
     if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
-    hipLaunchKernelGGL((state_kernel<D, C>), dim3(grid_x, grid_y), dim3(Shape<D, C>::NW * 64), 0, s, p);
+    hipLaunchKernelGGL((state_kernel<D, C, SG>), dim3(grid_x, grid_y), dim3(Shape<D, C>::NW * 64), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename E, int D, int C>
-static hipError_t dispatch_mode(int mode, const KernelParams &p, int gx, int gy, hipStream_t s) {
+static hipError_t dispatch_mode(int mode, bool sg, const KernelParams &p, int gx, int gy, hipStream_t s) {
+    if (sg) {   // scalar gates: the fused output pass and the state pass only
+        switch (mode) {
+            case MODE_OUT: return launch_one<E, D, C, MODE_OUT, true>(p, gx, gy, s);
+            case MODE_SEG:
+                if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C, true>(p, gx, gy, s);
+                else return launch_one<E, D, C, MODE_SEG, true>(p, gx, gy, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (mode) {
-        case MODE_OUT: return launch_one<E, D, C, MODE_OUT>(p, gx, gy, s);
+        case MODE_OUT: return launch_one<E, D, C, MODE_OUT, false>(p, gx, gy, s);
         case MODE_SEG:
-            if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C>(p, gx, gy, s);
-            else return launch_one<E, D, C, MODE_SEG>(p, gx, gy, s);
-        case MODE_INTRA: return launch_one<E, D, C, MODE_INTRA>(p, gx, gy, s);
-        case MODE_CUMSUM: return launch_one<E, D, C, MODE_CUMSUM>(p, gx, gy, s);
+            if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C, false>(p, gx, gy, s);
+            else return launch_one<E, D, C, MODE_SEG, false>(p, gx, gy, s);
+        case MODE_INTRA: return launch_one<E, D, C, MODE_INTRA, false>(p, gx, gy, s);
+        case MODE_CUMSUM: return launch_one<E, D, C, MODE_CUMSUM, false>(p, gx, gy, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, const KernelParams &p,
-                               int gx, int gy, hipStream_t s) {
+hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, bool scalar_gate,
+                               const KernelParams &p, int gx, int gy, hipStream_t s) {
+    const bool sg = scalar_gate;
     if (dtype == DTYPE_BF16) {
-        if (D == 128 && C == 64) return dispatch_mode<BF16, 128, 64>(mode, p, gx, gy, s);
-        if (D == 128 && C == 32) return dispatch_mode<BF16, 128, 32>(mode, p, gx, gy, s);
-        if (D == 64 && C == 64) return dispatch_mode<BF16, 64, 64>(mode, p, gx, gy, s);
-        if (D == 64 && C == 32) return dispatch_mode<BF16, 64, 32>(mode, p, gx, gy, s);
+        if (D == 128 && C == 64) return dispatch_mode<BF16, 128, 64>(mode, sg, p, gx, gy, s);
+        if (D == 128 && C == 32) return dispatch_mode<BF16, 128, 32>(mode, sg, p, gx, gy, s);
+        if (D == 64 && C == 64) return dispatch_mode<BF16, 64, 64>(mode, sg, p, gx, gy, s);
+        if (D == 64 && C == 32) return dispatch_mode<BF16, 64, 32>(mode, sg, p, gx, gy, s);
     } else if (dtype == DTYPE_F32) {
-        if (D == 64 && C == 64) return dispatch_mode<F32, 64, 64>(mode, p, gx, gy, s);
-        if (D == 64 && C == 32) return dispatch_mode<F32, 64, 32>(mode, p, gx, gy, s);
-        if (D == 128 && C == 32) return dispatch_mode<F32, 128, 32>(mode, p, gx, gy, s);
+        if (D == 64 && C == 64) return dispatch_mode<F32, 64, 64>(mode, sg, p, gx, gy, s);
+        if (D == 64 && C == 32) return dispatch_mode<F32, 64, 32>(mode, sg, p, gx, gy, s);
+        if (D == 128 && C == 32) return dispatch_mode<F32, 128, 32>(mode, sg, p, gx, gy, s);
     }
     return hipErrorInvalidValue;
 }

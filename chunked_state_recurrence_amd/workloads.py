@@ -22,6 +22,10 @@ normal, h0; values drawn in float32):
 The pages measure on synthetic shapes only (B, H, T, D sweeps); no dataset
 stands behind these numbers, and none is used here.
 
+Scalar-gate workloads (SCALAR_WORKLOADS) draw g with shape [B,H,T], one
+log-decay per token and head (same distributions), for the scalar-gate
+variant of the forward.
+
 Decode workloads (DECODE_WORKLOADS) draw the same way with T = 1: one new
 token per (batch, head) and a carried fp32 state drawn as h0.  The pages do
 not measure decode; the batch is sized so that the state of one step
@@ -52,6 +56,7 @@ class Workload:
     want_final: bool
     chunk: int | None  # None: the library's default chunk
     seed: int
+    scalar_gate: bool = False   # g is [B,H,T]: one log-decay per token and head
 
     @property
     def scale(self) -> float:
@@ -72,6 +77,12 @@ WORKLOADS = {
     "long_128k": Workload("long_128k", 1, 16, 131072, 128, "bf16", "l2", "ls41", 0.02, True, None, 4),
 }
 
+
+# Scalar gate: the prefill_16k shape with one gate per token and head.
+SCALAR_WORKLOADS = {
+    "prefill_16k_scalar": Workload("prefill_16k_scalar", 1, 16, 16384, 128, "bf16", "l2", "ls16",
+                                   None, True, None, 6, scalar_gate=True),
+}
 
 # Decode: B sequences x H heads each take one step against a carried state.
 DECODE_WORKLOADS = {
@@ -114,7 +125,7 @@ def make_inputs(wl: Workload, *, B=None, H=None, T=None, gate=None, seed=None,
     q = torch.randn(shape, generator=gen)
     k = torch.randn(shape, generator=gen)
     v = torch.randn(shape, generator=gen)
-    g = _gate(gate, shape, gen)
+    g = _gate(gate, (B, H, T) if wl.scalar_gate else shape, gen)
     if wl.k_mode == "l2":
         k = F.normalize(k, dim=-1, eps=1e-6)
     elif wl.k_mode == "scaled":

@@ -17,6 +17,10 @@ Parity status of each function (what pins it is in ``tests/test_oracle.py``):
   the output) and against a direct O(C^2 K) loop on tiny inputs.
 * ``chunked_reference``: pinned against ``token_recurrence`` at several chunk
   sizes (chunking is a reordering of the same sums).
+* ``scalar_gate_recurrence`` (scalar gate g [B,H,T], through
+  ``token_recurrence``) and ``scalar_gate_quadratic`` (the masked quadratic
+  form): pinned against each other, a hand-derived golden fixture
+  (``tests/golden/scalar/``), the g == 0 closed form and the T == 1 case.
 """
 
 from .reference import (  # noqa: F401
@@ -27,5 +31,7 @@ from .reference import (  # noqa: F401
     closed_form_zero_gate,
     intra_scores,
     oracle_threads,
+    scalar_gate_quadratic,
+    scalar_gate_recurrence,
     token_recurrence,
 )

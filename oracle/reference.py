@@ -232,3 +232,52 @@ def chunked_reference(q, k, v, g, h0=None, scale=1.0, chunk=64):
                 S = np.exp(Gam[b, h, c])[:, None] * S + Kh.T @ v[b, h, lo:hi]
             hf[b, h] = S
     return o, hf, states
+
+
+# --- scalar-gate variant (one log-decay per token and head) -------------------
+#
+# The pages name Mamba-2's SSD / semiseparable block and Lightning Attention
+# next to GLA (blog "Linear Attention 在 GPU 上到底慢在哪", section 正确的
+# baseline 和下一步) but print no formula for them.  Reading taken here: the
+# same recurrence with one gate per token shared by every key dim,
+#     S_t = exp(g_t) S_{t-1} + k_t^T v_t,   o_t = scale * q_t S_t,
+# g of shape [B,H,T].
+
+
+def scalar_gate_recurrence(q, k, v, g, h0=None, scale=1.0, threads=0, want_final=True):
+    """Scalar-gate recurrence via the token recurrence with g broadcast over
+    the key dims (a per-token gate is the per-key-dim gate with equal
+    entries).  g is [B,H,T]; returns (o, h_final)."""
+    g = np.asarray(g, dtype=np.float64)
+    K = np.shape(q)[-1]
+    gk = np.ascontiguousarray(np.repeat(g[..., None], K, axis=-1))
+    o, hf, _ = token_recurrence(q, k, v, gk, h0, scale, threads=threads, want_final=want_final)
+    return o, hf
+
+
+def scalar_gate_quadratic(q, k, v, g, h0=None, scale=1.0):
+    """The masked quadratic (semiseparable-matrix) form of the scalar-gate
+    recurrence, from unrolling it: with G_t = sum_{r<=t} g_r,
+        o   = scale * [ ((Q K^T) * L) V + exp(G) * (Q h0) ],
+        L_ts = exp(G_t - G_s) for s <= t, else 0,
+        h_final = exp(G_{T-1}) h0 + sum_s exp(G_{T-1} - G_s) k_s^T v_s.
+    Plain numpy matrix products per (b, h); O(T^2) memory, small T only."""
+    q, k, v, g = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g))
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    o = np.zeros((B, H, T, V))
+    hf = np.zeros((B, H, K, V))
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    for b in range(B):
+        for h in range(H):
+            G = np.cumsum(g[b, h])
+            L = np.where(causal, np.exp(np.where(causal, G[:, None] - G[None, :], 0.0)), 0.0)
+            Q, Kk, Vv = q[b, h], k[b, h], v[b, h]
+            base = np.zeros((K, V)) if h0 is None else np.asarray(h0[b, h], np.float64)
+            o[b, h] = scale * (((Q @ Kk.T) * L) @ Vv + np.exp(G)[:, None] * (Q @ base))
+            if T > 0:
+                w = np.exp(G[T - 1] - G)
+                hf[b, h] = np.exp(G[T - 1]) * base + (Kk * w[:, None]).T @ Vv
+            else:
+                hf[b, h] = base
+    return o, hf

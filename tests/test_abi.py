@@ -52,14 +52,14 @@ FAKE = 1 << 40          # 16-byte aligned, never dereferenced
 STEP = 1 << 32          # far apart: no overlap between fake buffers
 
 
-def _call(lib, **kw):
+def _call(lib, fn="gla_fwd", **kw):
     a = dict(q=FAKE, k=FAKE + STEP, v=FAKE + 2 * STEP, g=FAKE + 3 * STEP, h0=None,
              o=FAKE + 4 * STEP, hf=None, B=1, H=2, T=100, K=128, V=128, chunk=64, scale=0.1)
     a.update(kw)
     vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
-    return lib.gla_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["h0"]), vp(a["o"]),
-                       vp(a["hf"]), a["B"], a["H"], a["T"], a["K"], a["V"], a["chunk"],
-                       a["scale"], None)
+    return getattr(lib, fn)(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["g"]), vp(a["h0"]),
+                            vp(a["o"]), vp(a["hf"]), a["B"], a["H"], a["T"], a["K"], a["V"],
+                            a["chunk"], a["scale"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -73,6 +73,20 @@ def _call(lib, **kw):
 def test_argument_errors(kw, code):
     lib = gla.load_library()
     assert _call(lib, **kw) == code
+
+
+# Scalar-gate entry points: g is [B,H,T] (800 bytes at B=1, H=2, T=100), so an
+# output that starts inside those bytes is an alias.  (Cases that would pass
+# validation are not called: fake pointers must never reach a launch.)
+@pytest.mark.parametrize("fn", ["gla_fwd_scalar", "gla_fwd_scalar_f32"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(T=1 << 24), -2), (dict(K=96, V=96), -3), (dict(chunk=48), -3),
+    (dict(g=None), -1), (dict(q=None), -1), (dict(g=FAKE + 3 * STEP + 4), -4),
+    (dict(o=FAKE + 3 * STEP + 784), -7), (dict(hf=FAKE + 3 * STEP + 512), -7),
+])
+def test_scalar_gate_argument_errors(fn, kw, code):
+    lib = gla.load_library()
+    assert _call(lib, fn, **{"chunk": 32, **kw}) == code   # chunk 32: valid for both dtypes
 
 
 def _decode(lib, f32=False, **kw):

@@ -285,3 +285,78 @@ def test_pins_catch_planted_mistakes(mistake):
         o, hf = _py_recurrence(case["q"], case["k"], case["v"], case["g"], case["h0"],
                                case["scale"], None)
         np.testing.assert_allclose(o, case["o"], atol=1e-12)
+
+
+# --- scalar-gate variant -------------------------------------------------------
+
+def _scalar_golden():
+    path = os.path.join(GOLDEN, "scalar", "three_tokens.json")
+    with open(path) as f:
+        c = json.load(f)
+    T, K, V = c["T"], c["K"], c["V"]
+    arr = lambda key, shape: np.array(c[key], dtype=np.float64).reshape(shape)  # noqa: E731
+    return dict(q=arr("q", (1, 1, T, K)), k=arr("k", (1, 1, T, K)), v=arr("v", (1, 1, T, V)),
+                g=np.log(arr("decay", (1, 1, T))), h0=arr("h0", (1, 1, K, V)), scale=c["scale"],
+                o=arr("o", (1, 1, T, V)), hf=arr("h_final", (1, 1, K, V)))
+
+
+@pytest.mark.parametrize("fn", ["scalar_gate_recurrence", "scalar_gate_quadratic"])
+def test_scalar_gate_matches_golden(fn):
+    c = _scalar_golden()
+    o, hf = getattr(oracle, fn)(c["q"], c["k"], c["v"], c["g"], c["h0"], c["scale"])
+    np.testing.assert_allclose(o, c["o"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(hf, c["hf"], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 3, 2), (2, 3, 17, 5, 4), (1, 2, 70, 8, 11),
+                                   (1, 1, 130, 16, 16)])
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_scalar_gate_recurrence_matches_quadratic_form(shape, with_h0):
+    rng = np.random.default_rng(hash(("sg", shape, with_h0)) % 2**32)
+    B, H, T, K, V = shape
+    q, k, v, _, h0 = _rand(rng, *shape, h0=with_h0)
+    g = -np.abs(rng.standard_normal((B, H, T))) * 0.3
+    o, hf = oracle.scalar_gate_recurrence(q, k, v, g, h0, scale=0.41)
+    oq, hfq = oracle.scalar_gate_quadratic(q, k, v, g, h0, scale=0.41)
+    assert _rel(o, oq) < 1e-12
+    assert _rel(hf, hfq) < 1e-12
+
+
+def test_scalar_gate_zero_gate_is_the_closed_form():
+    rng = np.random.default_rng(7)
+    q, k, v, _, h0 = _rand(rng, 1, 2, 50, 8, 8)
+    g = np.zeros((1, 2, 50))
+    o, hf = oracle.scalar_gate_recurrence(q, k, v, g, h0, scale=0.5)
+    oc, hfc = oracle.closed_form_zero_gate(q, k, v, h0, scale=0.5)
+    assert _rel(o, oc) < 1e-13 and _rel(hf, hfc) < 1e-13
+
+
+def test_scalar_gate_single_token():
+    """T = 1: o = scale (exp(g) q h0 + (q . k) v), h_final = exp(g) h0 + k^T v."""
+    rng = np.random.default_rng(8)
+    q, k, v, _, h0 = _rand(rng, 2, 3, 1, 6, 5)
+    g = -np.abs(rng.standard_normal((2, 3, 1)))
+    o, hf = oracle.scalar_gate_quadratic(q, k, v, g, h0, scale=0.3)
+    e = np.exp(g[..., 0])[..., None]
+    qh0 = np.einsum("bhk,bhkv->bhv", q[:, :, 0], h0)
+    ref = 0.3 * (e * qh0 + np.sum(q[:, :, 0] * k[:, :, 0], -1)[..., None] * v[:, :, 0])
+    np.testing.assert_allclose(o[:, :, 0], ref, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(hf, e[..., None] * h0 + k[:, :, 0, :, None] * v[:, :, 0, None, :],
+                               rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("mistake", ["inclusive_mask_off", "shifted_exponent", "no_h0_decay"])
+def test_scalar_pins_catch_planted_mistakes(mistake):
+    """Plausible slips in a copy of the quadratic form fail the golden fixture."""
+    c = _scalar_golden()
+    Q, Kk, Vv, g, h0 = c["q"][0, 0], c["k"][0, 0], c["v"][0, 0], c["g"][0, 0], c["h0"][0, 0]
+    T = Q.shape[0]
+    G = np.cumsum(g)
+    if mistake == "shifted_exponent":   # exp(G_t - G_{s-1}): one decay too many
+        Gs = np.concatenate([[0.0], G[:-1]])
+        L = np.tril(np.exp(G[:, None] - Gs[None, :]))
+    else:
+        L = np.tril(np.exp(G[:, None] - G[None, :]), -1 if mistake == "inclusive_mask_off" else 0)
+    d = np.ones(T) if mistake == "no_h0_decay" else np.exp(G)
+    o = c["scale"] * (((Q @ Kk.T) * L) @ Vv + d[:, None] * (Q @ h0))
+    assert not np.allclose(o, c["o"][0, 0], atol=1e-12)
