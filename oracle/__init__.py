@@ -1,4 +1,4 @@
-"""CPU oracle for the gated linear attention prefill forward.
+"""CPU oracle for the gated linear attention prefill forward and its backward.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import anything from this package.  It
@@ -17,6 +17,11 @@ Parity status of each function (what pins it is in ``tests/test_oracle.py``):
   the output) and against a direct O(C^2 K) loop on tiny inputs.
 * ``chunked_reference``: pinned against ``token_recurrence`` at several chunk
   sizes (chunking is a reordering of the same sums).
+* ``token_recurrence_backward`` (C, fp64): the reverse-mode chain rule of the
+  same recurrence; pinned against torch autograd through an independent
+  PyTorch forward, central finite differences, hand-derived golden fixtures
+  (``tests/golden/backward/``) and the identity that dg is the reverse cumsum
+  of q*dq - k*dk plus the final-state term.
 * ``scalar_gate_recurrence`` (scalar gate g [B,H,T], through
   ``token_recurrence``) and ``scalar_gate_quadratic`` (the masked quadratic
   form): pinned against each other, a hand-derived golden fixture
@@ -34,4 +39,5 @@ from .reference import (  # noqa: F401
     scalar_gate_quadratic,
     scalar_gate_recurrence,
     token_recurrence,
+    token_recurrence_backward,
 )

@@ -123,3 +123,127 @@ int gla_oracle_f64(const double *q, const double *k, const double *v,
     }
     return status;
 }
+
+/*
+ * fp64 backward of the same recurrence: reverse-mode chain rule, token by
+ * token.  TEST INFRASTRUCTURE ONLY, like the forward above.
+ *
+ * Given do = dL/do [B,H,T,V] and dh_final = dL/dh_final [B,H,K,V] (NULL:
+ * zero), for every (b, h):
+ *
+ *   R <- dh_final                          (dL/dS_t from tokens after t)
+ *   for t = T-1 .. 0
+ *     R        <- R + scale * q_t^T do_t   (now the full dL/dS_t)
+ *     dq[t, d] <- scale * sum_v S_t[d, v] do_t[v]
+ *     dk[t, d] <- sum_v R[d, v] v_t[v]
+ *     dv[t, v] <- sum_d k_t[d] R[d, v]
+ *     dg[t, d] <- exp(g[t, d]) * sum_v R[d, v] S_{t-1}[d, v]
+ *     R[d, :]  <- exp(g[t, d]) * R[d, :]   (dL/dS_{t-1})
+ *   dh0 <- R
+ *
+ * with S_t the forward state after token t and S_{-1} = h0 (or 0).  The
+ * forward states are kept at every `ckpt`-th token and recomputed block by
+ * block with the same forward steps as gla_oracle_f64 (a memory bound, not a
+ * change of arithmetic).  Layouts as above; do [B,H,T,V], dq, dk, dg
+ * [B,H,T,K], dv [B,H,T,V], dh0 [B,H,K,V] (NULL: not written).  Parallel over
+ * (b, h).
+ */
+int gla_oracle_bwd_f64(const double *q, const double *k, const double *v,
+                       const double *g, const double *h0, const double *dout,
+                       const double *dh_final, double *dq, double *dk,
+                       double *dv, double *dg, double *dh0, long B, long H,
+                       long T, long K, long V, double scale, long ckpt,
+                       int threads) {
+    if (B < 0 || H < 0 || T < 0 || K <= 0 || V <= 0 || ckpt <= 0) return -1;
+    const long BH = B * H;
+    const long KV = K * V;
+    const long nblk = T > 0 ? (T + ckpt - 1) / ckpt : 0;
+    int status = 0;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        /* cp: state before each block's first token; blk: states after each
+           token of one block; R: the running gradient */
+        double *cp = (double *)malloc(sizeof(double) * (size_t)((nblk > 0 ? nblk : 1) * KV));
+        double *blk = (double *)malloc(sizeof(double) * (size_t)(ckpt * KV));
+        double *R = (double *)malloc(sizeof(double) * (size_t)KV);
+        double *S = (double *)malloc(sizeof(double) * (size_t)KV);
+        if (!cp || !blk || !R || !S) {
+            free(cp); free(blk); free(R); free(S);
+#pragma omp atomic write
+            status = -2;
+            continue;
+        }
+        for (long i = 0; i < KV; ++i) S[i] = h0 ? h0[bh * KV + i] : 0.0;
+        /* forward, keeping the state before every block */
+        for (long t = 0; t < T; ++t) {
+            if (t % ckpt == 0) memcpy(cp + (t / ckpt) * KV, S, sizeof(double) * (size_t)KV);
+            const double *kt = k + (bh * T + t) * K;
+            const double *gt = g + (bh * T + t) * K;
+            const double *vt = v + (bh * T + t) * V;
+            for (long d = 0; d < K; ++d) {
+                const double a = exp(gt[d]), kd = kt[d];
+                for (long c = 0; c < V; ++c) S[d * V + c] = a * S[d * V + c] + kd * vt[c];
+            }
+        }
+        for (long i = 0; i < KV; ++i) R[i] = dh_final ? dh_final[bh * KV + i] : 0.0;
+
+        for (long b = nblk - 1; b >= 0; --b) {
+            const long t0 = b * ckpt;
+            const long t1 = (t0 + ckpt < T) ? t0 + ckpt : T;
+            /* recompute the block's states: blk[t - t0] = S_t */
+            memcpy(S, cp + b * KV, sizeof(double) * (size_t)KV);
+            for (long t = t0; t < t1; ++t) {
+                const double *kt = k + (bh * T + t) * K;
+                const double *gt = g + (bh * T + t) * K;
+                const double *vt = v + (bh * T + t) * V;
+                for (long d = 0; d < K; ++d) {
+                    const double a = exp(gt[d]), kd = kt[d];
+                    for (long c = 0; c < V; ++c) S[d * V + c] = a * S[d * V + c] + kd * vt[c];
+                }
+                memcpy(blk + (t - t0) * KV, S, sizeof(double) * (size_t)KV);
+            }
+            for (long t = t1 - 1; t >= t0; --t) {
+                const double *St = blk + (t - t0) * KV;
+                const double *Sp = t > t0 ? blk + (t - 1 - t0) * KV : cp + b * KV;
+                const double *qt = q + (bh * T + t) * K;
+                const double *kt = k + (bh * T + t) * K;
+                const double *gt = g + (bh * T + t) * K;
+                const double *vt = v + (bh * T + t) * V;
+                const double *dot = dout + (bh * T + t) * V;
+                for (long d = 0; d < K; ++d)
+                    for (long c = 0; c < V; ++c) R[d * V + c] += scale * qt[d] * dot[c];
+                for (long d = 0; d < K; ++d) {
+                    double sq = 0.0, sk = 0.0, sg = 0.0;
+                    for (long c = 0; c < V; ++c) {
+                        sq += St[d * V + c] * dot[c];
+                        sk += R[d * V + c] * vt[c];
+                        sg += R[d * V + c] * Sp[d * V + c];
+                    }
+                    const double a = exp(gt[d]);
+                    dq[(bh * T + t) * K + d] = scale * sq;
+                    dk[(bh * T + t) * K + d] = sk;
+                    dg[(bh * T + t) * K + d] = a * sg;
+                }
+                for (long c = 0; c < V; ++c) {
+                    double s = 0.0;
+                    for (long d = 0; d < K; ++d) s += kt[d] * R[d * V + c];
+                    dv[(bh * T + t) * V + c] = s;
+                }
+                for (long d = 0; d < K; ++d) {
+                    const double a = exp(gt[d]);
+                    for (long c = 0; c < V; ++c) R[d * V + c] *= a;
+                }
+            }
+        }
+        if (dh0)
+            for (long i = 0; i < KV; ++i) dh0[bh * KV + i] = R[i];
+        free(cp); free(blk); free(R); free(S);
+    }
+    return status;
+}

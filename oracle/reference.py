@@ -55,6 +55,9 @@ def _load():
                                        ctypes.c_long, ctypes.c_long, ctypes.c_double,
                                        ctypes.c_long, ctypes.c_int]
         lib.gla_oracle_f64.restype = ctypes.c_int
+        lib.gla_oracle_bwd_f64.argtypes = [dp] * 12 + [ctypes.c_long] * 5 + [
+            ctypes.c_double, ctypes.c_long, ctypes.c_int]
+        lib.gla_oracle_bwd_f64.restype = ctypes.c_int
         lib.gla_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -101,6 +104,32 @@ def token_recurrence(q, k, v, g, h0=None, scale=1.0, record_every=0, threads=0,
     if rc != 0:
         raise RuntimeError(f"gla_oracle_f64 failed with status {rc}")
     return o, hf, states
+
+
+def token_recurrence_backward(q, k, v, g, h0, do, dh_final, scale=1.0, threads=0, ckpt=64):
+    """The oracle's backward (C, fp64): reverse-mode chain rule of the token
+    recurrence, token by token (see gla_oracle.c).  ``h0`` and ``dh_final``
+    may be None (zero).  Returns ``(dq, dk, dv, dg, dh0)``."""
+    q, k, v, g, h0, do, dh_final = (_f64(x) for x in (q, k, v, g, h0, do, dh_final))
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    assert k.shape == (B, H, T, K) and g.shape == (B, H, T, K)
+    assert v.shape == (B, H, T, V) and do.shape == (B, H, T, V)
+    for x in (h0, dh_final):
+        if x is not None:
+            assert x.shape == (B, H, K, V)
+    dq = np.empty((B, H, T, K))
+    dk = np.empty((B, H, T, K))
+    dv = np.empty((B, H, T, V))
+    dg = np.empty((B, H, T, K))
+    dh0 = np.empty((B, H, K, V))
+    rc = _load().gla_oracle_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(do),
+                                    _ptr(dh_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                    _ptr(dh0), B, H, T, K, V, float(scale), int(ckpt),
+                                    int(threads))
+    if rc != 0:
+        raise RuntimeError(f"gla_oracle_bwd_f64 failed with status {rc}")
+    return dq, dk, dv, dg, dh0
 
 
 def brute_force(q, k, v, g, h0=None, scale=1.0):

@@ -360,3 +360,118 @@ def test_scalar_pins_catch_planted_mistakes(mistake):
     d = np.ones(T) if mistake == "no_h0_decay" else np.exp(G)
     o = c["scale"] * (((Q @ Kk.T) * L) @ Vv + d[:, None] * (Q @ h0))
     assert not np.allclose(o, c["o"][0, 0], atol=1e-12)
+
+
+# --- backward ------------------------------------------------------------------
+
+def _bwd_golden_cases():
+    out = []
+    for path in sorted(glob.glob(os.path.join(GOLDEN, "backward", "*.json"))):
+        with open(path) as f:
+            c = json.load(f)
+        T, K, V = c["T"], c["K"], c["V"]
+        arr = lambda key, shape: np.array(c[key], dtype=np.float64).reshape(shape)  # noqa: E731
+        out.append(dict(
+            name=os.path.basename(path), scale=c["scale"],
+            q=arr("q", (1, 1, T, K)), k=arr("k", (1, 1, T, K)), v=arr("v", (1, 1, T, V)),
+            g=np.log(arr("decay", (1, 1, T, K))), h0=arr("h0", (1, 1, K, V)),
+            do=arr("do", (1, 1, T, V)), dhf=arr("dh_final", (1, 1, K, V)),
+            dq=arr("dq", (1, 1, T, K)), dk=arr("dk", (1, 1, T, K)), dv=arr("dv", (1, 1, T, V)),
+            dg=arr("dg", (1, 1, T, K)), dh0=arr("dh0", (1, 1, K, V))))
+    return out
+
+
+BWD_GOLDEN = _bwd_golden_cases()
+
+
+@pytest.mark.parametrize("case", BWD_GOLDEN, ids=lambda c: c["name"])
+def test_backward_matches_golden(case):
+    assert len(BWD_GOLDEN) >= 2
+    got = oracle.token_recurrence_backward(case["q"], case["k"], case["v"], case["g"], case["h0"],
+                                           case["do"], case["dhf"], case["scale"], ckpt=1)
+    for name, x in zip(("dq", "dk", "dv", "dg", "dh0"), got):
+        np.testing.assert_allclose(x, case[name], rtol=0, atol=1e-14, err_msg=name)
+
+
+def _torch_forward(q, k, v, g, h0, scale):
+    """An independent forward in plain PyTorch ops (CPU, float64), for autograd."""
+    import torch
+    B, H, T, K = q.shape
+    S = h0 if h0 is not None else torch.zeros(B, H, K, v.shape[-1], dtype=torch.float64)
+    outs = []
+    for t in range(T):
+        S = torch.exp(g[:, :, t])[..., None] * S + k[:, :, t, :, None] * v[:, :, t, None, :]
+        outs.append(scale * torch.einsum("bhk,bhkv->bhv", q[:, :, t], S))
+    return torch.stack(outs, dim=2), S
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 3, 2), (2, 2, 9, 5, 4), (1, 2, 37, 8, 11)])
+@pytest.mark.parametrize("ckpt", [1, 4, 64])
+def test_backward_matches_autograd(shape, ckpt):
+    import torch
+    rng = np.random.default_rng(hash(("bwd", shape, ckpt)) % 2**32)
+    q, k, v, g, h0 = _rand(rng, *shape, h0=True)
+    B, H, T, K, V = shape
+    do = rng.standard_normal((B, H, T, V))
+    dhf = rng.standard_normal((B, H, K, V))
+    tq, tk, tv, tg, th0 = (torch.tensor(x, requires_grad=True) for x in (q, k, v, g, h0))
+    o, hf = _torch_forward(tq, tk, tv, tg, th0, 0.3)
+    loss = (o * torch.tensor(do)).sum() + (hf * torch.tensor(dhf)).sum()
+    loss.backward()
+    got = oracle.token_recurrence_backward(q, k, v, g, h0, do, dhf, 0.3, ckpt=ckpt)
+    for name, x, t in zip(("dq", "dk", "dv", "dg", "dh0"), got, (tq, tk, tv, tg, th0)):
+        assert _rel(x, t.grad.numpy()) < 1e-12, name
+
+
+def test_backward_finite_differences():
+    """Directional derivatives of L = <o, do> + <h_final, dh_final> by central
+    differences agree with the oracle's gradients."""
+    rng = np.random.default_rng(31)
+    q, k, v, g, h0 = _rand(rng, 1, 1, 12, 4, 3, h0=True)
+    do = rng.standard_normal(v.shape)
+    dhf = rng.standard_normal(h0.shape)
+    grads = oracle.token_recurrence_backward(q, k, v, g, h0, do, dhf, 0.7, ckpt=5)
+
+    def loss(q, k, v, g, h0):
+        o, hf, _ = oracle.token_recurrence(q, k, v, g, h0, 0.7)
+        return float(np.sum(o * do) + np.sum(hf * dhf))
+
+    base = [q, k, v, g, h0]
+    for idx, grad in zip(range(5), (grads[0], grads[1], grads[2], grads[3], grads[4])):
+        direction = rng.standard_normal(base[idx].shape)
+        eps = 1e-5
+        plus = list(base)
+        minus = list(base)
+        plus[idx] = base[idx] + eps * direction
+        minus[idx] = base[idx] - eps * direction
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        an = float(np.sum(grad * direction))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (idx, fd, an)
+
+
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_backward_gate_gradient_identity(with_h0):
+    """dg_t = sum_{t' >= t} (q_t' * dq_t' - k_t' * dk_t') + sum_v dh_final * h_final:
+    the gate gradient from the log-space cumsum, against the oracle's direct
+    per-token formula; and at every chunk start it equals sum_v U * S, the
+    chunk-start state times the gradient flowing into it."""
+    rng = np.random.default_rng(41 + with_h0)
+    B, H, T, K, V = 2, 2, 130, 6, 5
+    q, k, v, g, h0 = _rand(rng, B, H, T, K, V, h0=with_h0)
+    do = rng.standard_normal((B, H, T, V))
+    dhf = rng.standard_normal((B, H, K, V))
+    dq, dk, dv, dg, dh0 = oracle.token_recurrence_backward(q, k, v, g, h0, do, dhf, 0.5)
+    _, hf, states = oracle.token_recurrence(q, k, v, g, h0, 0.5, record_every=32)
+    w = q * dq - k * dk
+    tail = np.sum(dhf * hf, axis=-1)[:, :, None, :]
+    ident = np.flip(np.cumsum(np.flip(w, axis=2), axis=2), axis=2) + tail
+    assert _rel(dg, ident) < 1e-11
+    # U_n (gradient into the chunk-start state) from the backward over the
+    # tail of the sequence with its own start state
+    for n in range(states.shape[2]):
+        t0 = 32 * n
+        sl = slice(t0, T)
+        _, _, _, _, U = oracle.token_recurrence_backward(
+            q[:, :, sl], k[:, :, sl], v[:, :, sl], g[:, :, sl], states[:, :, n], do[:, :, sl],
+            dhf, 0.5)
+        assert _rel(dg[:, :, t0], np.sum(U * states[:, :, n], axis=-1)) < 1e-11
