@@ -1,5 +1,5 @@
 """ctypes binding of libgla.so (include/gla.h, include/gla_scalar.h,
-include/gla_decode.h, include/gla_stages.h).
+include/gla_bwd.h, include/gla_decode.h, include/gla_stages.h).
 
 Argument marshalling only: shape/dtype/device checks, output allocation with
 torch, and the call.  Every step of the computation runs in the HIP kernels
@@ -27,8 +27,9 @@ ERRORS = {
 EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_version",
             "gla_release", "gla_profile_start", "gla_profile_stop", "gla_stage_cumsum",
             "gla_stage_intra", "gla_stage_states", "gla_decode", "gla_decode_f32",
-            "gla_fwd_scalar", "gla_fwd_scalar_f32")
-KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode"}
+            "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32")
+KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode", 5: "bwd_segment",
+                6: "bwd"}
 
 
 class _KernelTime(ctypes.Structure):
@@ -62,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     lib.gla_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_fwd_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_fwd_scalar.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
+    lib.gla_bwd.argtypes = [P] * 12 + [I, I, I, I, I, I, F, P]
+    lib.gla_bwd_f32.argtypes = [P] * 12 + [I, I, I, I, I, I, F, P]
     lib.gla_fwd_scalar_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_stage_states.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_stage_cumsum.argtypes = [P, P, P, I, I, I, I, I, P]
@@ -80,7 +83,7 @@ def load_library(path: str = LIB_PATH):
     lib.gla_profile_stop.restype = ctypes.c_int
     for name in ("gla_fwd", "gla_fwd_f32", "gla_stage_states", "gla_stage_cumsum",
                  "gla_stage_intra", "gla_set_tuning", "gla_version", "gla_decode", "gla_decode_f32",
-                 "gla_fwd_scalar", "gla_fwd_scalar_f32"):
+                 "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32"):
         getattr(lib, name).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -171,6 +174,49 @@ def gla_fwd_scalar_f32(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=F
     """Scalar-gate fp32 forward: fp32 q, k, v, o; g fp32 [B,H,T]."""
     return _fwd(load_library().gla_fwd_scalar_f32, torch.float32, q, k, v, g, h0, chunk, scale,
                 want_final, o, h_final, stream, scalar_gate=True)
+
+
+def _bwd(fn, io_dtype, q, k, v, g, h0, do, dh_final, chunk, scale, want_dh0, out, stream):
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if do is None:
+        raise ValueError("do is required")
+    for t, n, dt, shp in ((q, "q", io_dtype, (B, H, T, K)), (k, "k", io_dtype, (B, H, T, K)),
+                          (v, "v", io_dtype, (B, H, T, V)), (g, "g", torch.float32, (B, H, T, K)),
+                          (do, "do", io_dtype, (B, H, T, V)),
+                          (h0, "h0", torch.float32, (B, H, K, V)),
+                          (dh_final, "dh_final", torch.float32, (B, H, K, V))):
+        _need(t, n, dt, shp, dev)
+    if scale is None:
+        scale = K ** -0.5
+    out = dict(out or {})
+    shapes = {"dq": ((B, H, T, K), io_dtype), "dk": ((B, H, T, K), io_dtype),
+              "dv": ((B, H, T, V), io_dtype), "dg": ((B, H, T, K), torch.float32),
+              "dh0": ((B, H, K, V), torch.float32)}
+    for n, (shp, dt) in shapes.items():
+        if out.get(n) is None and (n != "dh0" or want_dh0):
+            out[n] = torch.empty(shp, dtype=dt, device=dev)
+        _need(out.get(n), n, dt, shp, dev)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(do), _ptr(dh_final),
+              _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+              _ptr(out.get("dh0")), B, H, T, K, V, int(chunk), float(scale), _stream(stream)))
+    return out["dq"], out["dk"], out["dv"], out["dg"], out.get("dh0")
+
+
+def gla_bwd(q, k, v, g, h0, do, dh_final=None, *, chunk=0, scale=None, want_dh0=True, out=None,
+            stream=None):
+    """bf16 backward: returns (dq, dk, dv bf16; dg fp32 [B,H,T,K]; dh0 fp32 or None).
+    ``out`` may hold preallocated dq, dk, dv, dg, dh0 tensors."""
+    return _bwd(load_library().gla_bwd, torch.bfloat16, q, k, v, g, h0, do, dh_final, chunk,
+                scale, want_dh0, out, stream)
+
+
+def gla_bwd_f32(q, k, v, g, h0, do, dh_final=None, *, chunk=0, scale=None, want_dh0=True,
+                out=None, stream=None):
+    """fp32 backward: the same with fp32 q, k, v, do, dq, dk, dv."""
+    return _bwd(load_library().gla_bwd_f32, torch.float32, q, k, v, g, h0, do, dh_final, chunk,
+                scale, want_dh0, out, stream)
 
 
 def _decode(fn, io_dtype, q, k, v, g, state, scale, o, stream):

@@ -1,6 +1,7 @@
 // gla_api.hip — C ABI of libgla.so: argument validation, segment scheduling,
 // workspace, launches.  Declarations and contracts: include/gla.h,
-// include/gla_scalar.h, include/gla_decode.h and include/gla_stages.h.
+// include/gla_scalar.h, include/gla_bwd.h, include/gla_decode.h and
+// include/gla_stages.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -10,6 +11,7 @@
 #include <vector>
 
 #include "gla.h"
+#include "gla_bwd.h"
 #include "gla_decode.h"
 #include "gla_scalar.h"
 #include "gla_stages.h"
@@ -22,8 +24,10 @@ constexpr int kDefaultTargetWgs = 256;
 
 struct DeviceState {
     int arch_ok = -1;  // -1 unknown, 0 not gfx950, 1 gfx950
-    void *ws = nullptr;
+    void *ws = nullptr;    // forward: segment states
     size_t ws_bytes = 0;
+    void *bws = nullptr;   // backward: forward chunk-start states, final states, segment states
+    size_t bws_bytes = 0;
 };
 
 std::mutex g_mu;
@@ -74,24 +78,29 @@ int current_device(DeviceState **out) {
     return GLA_OK;
 }
 
-int ensure_workspace(DeviceState *d, size_t bytes, float **out) {
+int grow(void **buf, size_t *have, size_t bytes, float **out) {
     std::lock_guard<std::mutex> lk(g_mu);
-    if (d->ws_bytes < bytes) {
-        if (d->ws) {
-            (void)hipFree(d->ws);  // hipFree waits for work that may still use it
-            d->ws = nullptr;
-            d->ws_bytes = 0;
+    if (*have < bytes) {
+        if (*buf) {
+            (void)hipFree(*buf);  // hipFree waits for work that may still use it
+            *buf = nullptr;
+            *have = 0;
         }
         void *p = nullptr;
         if (hipMalloc(&p, bytes) != hipSuccess || !p) {
             (void)hipGetLastError();
             return GLA_ERR_ALLOC;
         }
-        d->ws = p;
-        d->ws_bytes = bytes;
+        *buf = p;
+        *have = bytes;
     }
-    *out = static_cast<float *>(d->ws);
+    *out = static_cast<float *>(*buf);
     return GLA_OK;
+}
+
+int ensure_workspace(DeviceState *d, size_t bytes, float **out) { return grow(&d->ws, &d->ws_bytes, bytes, out); }
+int ensure_bwd_workspace(DeviceState *d, size_t bytes, float **out) {
+    return grow(&d->bws, &d->bws_bytes, bytes, out);
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -113,6 +122,7 @@ struct Call {
     float scale;
     hipStream_t stream;
     bool scalar_gate = false;  // g is [B,H,T] instead of [B,H,T,K]
+    bool need_o = true;        // false: only states / h_final are wanted (backward)
 };
 
 int default_chunk(int dtype, int D) {
@@ -127,7 +137,7 @@ int validate(Call &c) {
     if (c.chunk < 0) return GLA_ERR_UNSUPPORTED;
     if (c.chunk == 0) c.chunk = default_chunk(c.dtype, c.K);
     if (!gla::chunk_supported(c.dtype, c.K, c.chunk)) return GLA_ERR_UNSUPPORTED;
-    if (c.T > 0 && (!c.q || !c.k || !c.v || !c.g || !c.o)) return GLA_ERR_NULL;
+    if (c.T > 0 && (!c.q || !c.k || !c.v || !c.g || (c.need_o && !c.o))) return GLA_ERR_NULL;
     const void *ptrs[] = {c.q, c.k, c.v, c.g, c.h0, c.o, c.h_final, c.states};
     for (const void *p : ptrs)
         if (misaligned(p)) return GLA_ERR_ALIGN;
@@ -247,9 +257,127 @@ int run_forward(Call &c) {
     return GLA_OK;
 }
 
+struct BwdCall {
+    int dtype;
+    const void *q, *k, *v;
+    const float *g, *h0;
+    const void *dout;
+    const float *dhf;
+    void *dq, *dk, *dv;
+    float *dg, *dh0;
+    int B, H, T, K, V, chunk;
+    float scale;
+    hipStream_t stream;
+};
+
+int run_backward(BwdCall &b) {
+    Call c{b.dtype, b.q, b.k, b.v, b.g, b.h0, nullptr, nullptr, nullptr, b.B, b.H, b.T, b.K, b.V,
+           b.chunk, b.scale, b.stream};
+    c.need_o = false;
+    int rc = validate(c);   // shapes, chunk, input pointers and alignment
+    if (rc != GLA_OK) return rc;
+    b.chunk = c.chunk;
+    if (b.T > 0 && (!b.dout || !b.dq || !b.dk || !b.dv || !b.dg)) return GLA_ERR_NULL;
+    const void *ptrs[] = {b.dout, b.dhf, b.dq, b.dk, b.dv, b.dg, b.dh0};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return GLA_ERR_ALIGN;
+    const size_t es = b.dtype == gla::DTYPE_BF16 ? 2 : 4;
+    const size_t bht = size_t(b.B) * b.H * b.T;
+    const size_t nqk = bht * b.K * es, nv = bht * b.V * es, ng = bht * b.K * 4;
+    const size_t nst = size_t(b.B) * b.H * b.K * b.V * 4;
+    struct R { const void *p; size_t n; };
+    const R ins[] = {{b.q, nqk}, {b.k, nqk}, {b.v, nv}, {b.g, ng}, {b.h0, nst}, {b.dout, nv}, {b.dhf, nst}};
+    const R outs[] = {{b.dq, nqk}, {b.dk, nqk}, {b.dv, nv}, {b.dg, ng}, {b.dh0, nst}};
+    for (const R &o : outs) {
+        for (const R &i : ins)
+            if (overlaps(o.p, o.n, i.p, i.n)) return GLA_ERR_ALIAS;
+        for (const R &o2 : outs)
+            if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return GLA_ERR_ALIAS;
+    }
+    DeviceState *dev = nullptr;
+    if ((rc = current_device(&dev)) != GLA_OK) return rc;
+    const int D = b.K;
+    const long BH = long(b.B) * b.H;
+    if (b.T == 0) {   // dh0 = dh_final
+        if (b.dh0 && traced(GLA_KERNEL_OTHER, b.stream, [&] {
+                return gla::launch_copy_state(b.dh0, b.dhf, BH * D * D, b.stream);
+            }) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+        return GLA_OK;
+    }
+    const int N = (b.T + b.chunk - 1) / b.chunk;
+    int target;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        target = g_target_wgs;
+    }
+    const long group = std::min<long>(BH, 65535);
+    // workspace: chunk-start states, then the largest group's segment states
+    size_t seg_need = 0;
+    for (long g0 = 0; g0 < BH; g0 += group) {
+        const int nbh = int(std::min(group, BH - g0));
+        const Plan pl = plan_segments(nbh, N, target, 1);
+        seg_need = std::max(seg_need, size_t(nbh) * size_t(pl.P - 1) * size_t(D) * (D + 1) * 4);
+    }
+    const size_t n_states = size_t(BH) * N * D * D;
+    float *bws = nullptr;
+    if ((rc = ensure_bwd_workspace(dev, n_states * 4 + seg_need, &bws)) != GLA_OK) return rc;
+    float *states = bws, *segws = bws + n_states;
+
+    // forward chunk-start states (no o, no final state)
+    c.states = states;
+    if ((rc = run_forward(c)) != GLA_OK) return rc;
+
+    for (long g0 = 0; g0 < BH; g0 += group) {
+        const int nbh = int(std::min(group, BH - g0));
+        const Plan pl = plan_segments(nbh, N, target, 1);
+        gla::BwdParams p{};
+        p.q = b.q; p.k = b.k; p.v = b.v; p.dout = b.dout; p.g = b.g;
+        p.states = states; p.dhf = b.dhf;
+        p.dq = b.dq; p.dk = b.dk; p.dv = b.dv; p.dg = b.dg; p.dh0 = b.dh0;
+        p.ws_E = segws;
+        p.ws_G = segws + size_t(nbh) * (pl.P - 1) * D * D;
+        p.T = b.T; p.N = N; p.cps = pl.cps; p.P = pl.P; p.ws_slots = pl.P - 1;
+        p.bh0 = g0; p.scale = b.scale;
+        if (pl.P > 1) {
+            if (traced(GLA_KERNEL_BWD_SEGMENT, b.stream, [&] {
+                    return gla::launch_bwd(b.dtype, D, b.chunk, false, p, pl.P - 1, nbh, b.stream);
+                }) != hipSuccess)
+                return GLA_ERR_LAUNCH;
+            if (traced(GLA_KERNEL_SCAN, b.stream, [&] {
+                    return gla::launch_scan(p.ws_E, p.ws_G, b.dhf, g0, nbh, pl.P - 1, D, b.stream);
+                }) != hipSuccess)
+                return GLA_ERR_LAUNCH;
+        }
+        if (traced(GLA_KERNEL_BWD, b.stream, [&] {
+                return gla::launch_bwd(b.dtype, D, b.chunk, true, p, pl.P, nbh, b.stream);
+            }) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+    }
+    return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gla_bwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g, const float *h0,
+            const gla_bf16 *dout, const float *dh_final, gla_bf16 *dq, gla_bf16 *dk, gla_bf16 *dv,
+            float *dg, float *dh0, int B, int H, int T, int K, int V, int chunk, float scale,
+            void *stream) {
+    BwdCall b{gla::DTYPE_BF16, q, k, v, g, h0, dout, dh_final, dq, dk, dv, dg, dh0, B, H, T, K, V,
+              chunk, scale, static_cast<hipStream_t>(stream)};
+    return run_backward(b);
+}
+
+int gla_bwd_f32(const float *q, const float *k, const float *v, const float *g, const float *h0,
+                const float *dout, const float *dh_final, float *dq, float *dk, float *dv, float *dg,
+                float *dh0, int B, int H, int T, int K, int V, int chunk, float scale, void *stream) {
+    BwdCall b{gla::DTYPE_F32, q, k, v, g, h0, dout, dh_final, dq, dk, dv, dg, dh0, B, H, T, K, V,
+              chunk, scale, static_cast<hipStream_t>(stream)};
+    return run_backward(b);
+}
+
 
 int gla_fwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g,
             const float *h0, gla_bf16 *o, float *h_final, int B, int H, int T, int K, int V,
@@ -453,11 +581,14 @@ void gla_release(void) {
     int cur = -1;
     (void)hipGetDevice(&cur);
     for (size_t i = 0; i < g_dev.size(); ++i) {
-        if (g_dev[i].ws) {
+        if (g_dev[i].ws || g_dev[i].bws) {
             (void)hipSetDevice(int(i));
-            (void)hipFree(g_dev[i].ws);
+            if (g_dev[i].ws) (void)hipFree(g_dev[i].ws);
+            if (g_dev[i].bws) (void)hipFree(g_dev[i].bws);
             g_dev[i].ws = nullptr;
             g_dev[i].ws_bytes = 0;
+            g_dev[i].bws = nullptr;
+            g_dev[i].bws_bytes = 0;
         }
     }
     if (cur >= 0) (void)hipSetDevice(cur);

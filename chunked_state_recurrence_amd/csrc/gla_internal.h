@@ -33,6 +33,22 @@ struct KernelParams {
     float scale;
 };
 
+// backward chunk kernel (gla_bwd.hip)
+struct BwdParams {
+    const void *q, *k, *v, *dout;
+    const float *g;
+    const float *states;   // forward chunk-start states [heads][N][D][D]
+    const float *dhf;      // dL/dh_final [heads][D][D] or null (zero)
+    void *dq, *dk, *dv;
+    float *dg;
+    float *dh0;            // or null
+    float *ws_E;           // [nbh][ws_slots][D][D]  segment contributions, then U at segment ends
+    float *ws_G;           // [nbh][ws_slots][D]     segment total log2-decays
+    int T, N, cps, P, ws_slots;
+    long bh0;              // first (batch, head) row of this launch
+    float scale;
+};
+
 bool chunk_supported(int dtype, int D, int C);
 // work-groups of the state pass that fit on one CU (LDS bound), 1 or 2
 int state_units_per_cu(int dtype, int D, int C);
@@ -42,6 +58,10 @@ hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, bool scalar_ga
 hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,
                        int slots, int D, hipStream_t s);
 hipError_t launch_copy_state(float *dst, const float *src, long n, hipStream_t s);
+// backward: full = false, the segment contributions (grid: P - 1 slots x
+// heads); full = true, the per-segment chunk walk (grid: P segments x heads)
+hipError_t launch_bwd(int dtype, int D, int C, bool full, const BwdParams &p, int gx, int gy,
+                      hipStream_t s);
 // one decode step for nbh (batch, head) rows, state [nbh][D][D] updated in place
 hipError_t launch_decode(int dtype, int D, const void *q, const void *k, const void *v, const float *g,
                          float *state, void *o, long nbh, float scale, hipStream_t s);

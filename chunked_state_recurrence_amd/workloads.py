@@ -26,6 +26,10 @@ Scalar-gate workloads (SCALAR_WORKLOADS) draw g with shape [B,H,T], one
 log-decay per token and head (same distributions), for the scalar-gate
 variant of the forward.
 
+Backward inputs (make_grad_inputs): the loss gradients do ~ N(0, 1) (in the
+workload's dtype) and dh_final ~ N(0, 0.1) (fp32), from a generator of their
+own seeded with the workload seed + 1000.
+
 Decode workloads (DECODE_WORKLOADS) draw the same way with T = 1: one new
 token per (batch, head) and a carried fp32 state drawn as h0.  The pages do
 not measure decode; the batch is sized so that the state of one step
@@ -139,6 +143,21 @@ def make_inputs(wl: Workload, *, B=None, H=None, T=None, gate=None, seed=None,
         q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
     return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(),
             "g": g.float().contiguous(), "h0": None if h0 is None else h0.contiguous()}
+
+
+def make_grad_inputs(wl: Workload, *, B=None, H=None, T=None, seed=None, dh_final=True):
+    """Draw the loss gradients (do, dh_final) for a backward of workload ``wl``."""
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    T = wl.T if T is None else T
+    seed = (wl.seed if seed is None else seed) + 1000
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    do = torch.randn((B, H, T, wl.D), generator=gen)
+    dhf = torch.randn((B, H, wl.D, wl.D), generator=gen) * 0.1 if dh_final else None
+    if wl.dtype == "bf16":
+        do = do.to(torch.bfloat16)
+    return {"do": do.contiguous(), "dh_final": None if dhf is None else dhf.contiguous()}
 
 
 def to_f64_numpy(t):

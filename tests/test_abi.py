@@ -114,6 +114,33 @@ def test_decode_argument_errors(kw, code, f32):
     assert _decode(lib, f32, **kw) == code
 
 
+def _bwd(lib, fn="gla_bwd", **kw):
+    a = dict(q=FAKE, k=FAKE + STEP, v=FAKE + 2 * STEP, g=FAKE + 3 * STEP, h0=None,
+             do=FAKE + 4 * STEP, dhf=None, dq=FAKE + 5 * STEP, dk=FAKE + 6 * STEP,
+             dv=FAKE + 7 * STEP, dg=FAKE + 8 * STEP, dh0=None,
+             B=1, H=2, T=100, K=128, V=128, chunk=32, scale=0.1)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return getattr(lib, fn)(*(vp(a[n]) for n in ("q", "k", "v", "g", "h0", "do", "dhf", "dq", "dk",
+                                                   "dv", "dg", "dh0")),
+                            a["B"], a["H"], a["T"], a["K"], a["V"], a["chunk"], a["scale"], None)
+
+
+@pytest.mark.parametrize("fn", ["gla_bwd", "gla_bwd_f32"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(T=-1), -2), (dict(K=96, V=96), -3), (dict(chunk=48), -3),
+    (dict(do=None), -1), (dict(dq=None), -1), (dict(dg=None), -1), (dict(g=None), -1),
+    (dict(dk=FAKE + 6 * STEP + 8), -4), (dict(dh0=FAKE + 9 * STEP + 4), -4),
+    (dict(dq=FAKE + 64), -7),                    # dq overlaps q
+    (dict(dv=FAKE + 4 * STEP + 32), -7),         # dv overlaps do
+    (dict(dk=FAKE + 5 * STEP + 64), -7),         # dk overlaps dq
+    (dict(dh0=FAKE + 8 * STEP + 64), -7),        # dh0 overlaps dg
+])
+def test_backward_argument_errors(fn, kw, code):
+    lib = gla.load_library()
+    assert _bwd(lib, fn, **kw) == code
+
+
 def test_fp32_chunk_support_table():
     lib = gla.load_library()
     vp = ctypes.c_void_p
