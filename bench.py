@@ -24,6 +24,15 @@ Scalar gate (a separate line, not the headline):
 the same step through gla_fwd_scalar (g [B,H,T]); its algorithmic bytes
 per token-head are 1028 at D=128 (bf16 q, k, v, o + one fp32 gate).
 
+Backward (a separate line, not the headline):
+    python bench.py --workload prefill_16k --backward
+A step is one gla_bwd call: the forward's chunk-start states recomputed,
+the reverse segment pass and scan, and the backward chunk pass writing dq,
+dk, dv, dg.  ``value`` is B*T / step time; ``roofline`` prices the backward
+chunk pass against HBM bandwidth with its algorithmic bytes (bf16 q, k, v,
+do read and dq, dk, dv written, fp32 g read and dg written, and the fp32
+chunk-start state read once per chunk).
+
 Decode (a separate line, not the headline):
     python bench.py --workload decode_b256 [--steps K] [--warmup W]
 A step is one gla_decode call: one token for each of B sequences x H heads
@@ -59,6 +68,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "prefill tokens/s, chunk GLA fwd H=16 D=128 bf16; % MFMA peak / HBM BW"
 SCALAR_METRIC = "prefill tokens/s, chunk scalar-gate linear attention fwd H=16 D=128 bf16; % HBM BW"
+BWD_METRIC = ("backward tokens/s, chunk GLA bwd H=16 D=128 bf16 (forward states recomputed); "
+              "% HBM BW")
 DECODE_METRIC = "decode tokens/s, GLA decode step H=16 D=128 bf16 q/k/v/o, fp32 state; % HBM BW"
 # The pages' number for this workload (FLA chunk_gla, RTX 4090, bf16, H=16,
 # D=128, B=1, T=16K: 2.17 ms) as tokens/s: another machine, context only.
@@ -79,6 +90,16 @@ def algorithmic_bytes(wl) -> int:
     per_token_head = wl.D * 4 * es + gate         # 1536 B at D=128, bf16 (scalar gate: 1028)
     state = wl.B * wl.H * wl.D * wl.D * 4
     return th * per_token_head + (state if wl.want_final else 0) + (state if wl.h0_std else 0)
+
+
+def backward_bytes(wl, chunk: int) -> int:
+    """Backward chunk pass, per token-head: bf16 q, k, v, do read and dq, dk,
+    dv written (2 B each), fp32 g read and dg written, plus one fp32 D x D
+    chunk-start state read per chunk."""
+    th = wl.B * wl.H * wl.T
+    es = 2 if wl.dtype == "bf16" else 4
+    n_chunks = wl.B * wl.H * ((wl.T + chunk - 1) // chunk)
+    return th * wl.D * (7 * es + 8) + n_chunks * wl.D * wl.D * 4
 
 
 def decode_bytes(wl) -> int:
@@ -250,6 +271,129 @@ def bench_decode(args, wl):
     print(json.dumps(res), flush=True)
 
 
+def cpu_baseline_backward(wl, x, gr, min_s: float = 10.0):
+    """Time the fp64 oracle backward on the host over whole heads of the
+    workload (as many as fit about min_s, at least one), repeated until min_s
+    has passed; scaled to tokens/s of all heads."""
+    import numpy as np
+    import oracle
+    from chunked_state_recurrence_amd.workloads import to_f64_numpy
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    src = dict(x)
+    src["do"], src["dhf"] = gr["do"], gr["dh_final"]
+
+    def run(sel):
+        f = {n: (None if src[n] is None else
+                 np.stack([to_f64_numpy(src[n][b, h]) for (b, h) in sel])[None])
+             for n in ("q", "k", "v", "g", "h0", "do", "dhf")}
+        t0 = time.perf_counter()
+        oracle.token_recurrence_backward(f["q"], f["k"], f["v"], f["g"], f["h0"], f["do"],
+                                         f["dhf"], wl.scale, threads=threads)
+        return time.perf_counter() - t0
+
+    n = min(len(pairs), threads)
+    times = [run(pairs[:n])]
+    while sum(times) < min_s:
+        times.append(run(pairs[:n]))
+    t = statistics.mean(times) * len(pairs) / n
+    return {"value": wl.B * wl.T / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {len(pairs)} (batch, head) sequences, full T={wl.T}, fp64 token "
+                      f"backward, {len(times)} passes of {statistics.mean(times):.2f} s; "
+                      "scaled to all heads",
+            "seconds": round(sum(times), 3)}
+
+
+def bench_backward(args, wl):
+    import torch
+
+    import chunked_state_recurrence_amd as gla
+    from chunked_state_recurrence_amd.workloads import make_grad_inputs, make_inputs
+
+    dev = torch.device("cuda:0")
+    chunk = args.chunk or 64
+    host = make_inputs(wl)
+    gr = make_grad_inputs(wl)
+    sets = []
+    for s in range(2):   # two independent input sets alternate
+        d = {n: (None if host[n] is None else host[n].to(dev)) for n in ("q", "k", "v", "g", "h0")}
+        d["do"] = gr["do"].to(dev)
+        d["dhf"] = None if gr["dh_final"] is None else gr["dh_final"].to(dev)
+        if s == 1:
+            d = {n: (None if t is None else t.clone()) for n, t in d.items()}
+        shp = (wl.B, wl.H, wl.T, wl.D)
+        d["out"] = {"dq": torch.empty(shp, dtype=torch.bfloat16, device=dev),
+                    "dk": torch.empty(shp, dtype=torch.bfloat16, device=dev),
+                    "dv": torch.empty(shp, dtype=torch.bfloat16, device=dev),
+                    "dg": torch.empty(shp, dtype=torch.float32, device=dev),
+                    "dh0": torch.empty((wl.B, wl.H, wl.D, wl.D), dtype=torch.float32, device=dev)}
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        d = sets[i & 1]
+        gla.gla_bwd(d["q"], d["k"], d["v"], d["g"], d["h0"], d["do"], d["dhf"], chunk=chunk,
+                    scale=wl.scale, out=d["out"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+
+    gla.profile_start(16 * args.steps + 16)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    by_kind = {}
+    for kind, kms in gla.profile_stop():
+        by_kind.setdefault(kind, []).append(kms)
+    if args.copy_calibration:
+        copy_calibration(dev)
+    k_ms = statistics.mean(by_kind["bwd"])
+    per_launch = backward_bytes(wl, chunk)
+    achieved = per_launch / (k_ms * 1e-3) / 1e9
+    traffic = None
+    c = read_counters(wl.name + "_bwd")
+    if c and "fetch_factor" in c:
+        m = c["median_per_dispatch_KiB"]
+        f, w = m.get("bwd:FETCH_SIZE"), m.get("bwd:WRITE_SIZE")
+        if f is not None and w is not None:
+            traffic = int(f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"])
+    res = {
+        "metric": BWD_METRIC,
+        "value": wl.B * wl.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name + " backward", "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.D,
+                   "V": wl.D, "chunk": chunk, "h0": wl.h0_std is not None, "dh_final": True,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "backward chunk pass (bwd_kernel<BF16,128,64,BM_FULL>)",
+                     "kernel_ms": k_ms, "algorithmic_bytes_per_launch": per_launch},
+        "kernels_ms": {k: statistics.mean(v) for k, v in by_kind.items()},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_backward(wl, host, gr)
+    print(json.dumps(res), flush=True)
+
+
 def read_counters(wl_name: str):
     path = os.path.join(ROOT, "profiles", f"counters_{wl_name}.json")
     if not os.path.exists(path):
@@ -274,7 +418,8 @@ def summarize_counters(outdir: str, wl_name: str):
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         last_chunk = max((int(r["Dispatch_Id"]) for r in rows
                           if any(s in r["Kernel_Name"]
-                                 for s in ("chunk_kernel", "state_kernel", "decode_kernel"))),
+                                 for s in ("chunk_kernel", "state_kernel", "decode_kernel",
+                                           "bwd_kernel"))),
                          default=-1)
         for r in rows:
             name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
@@ -286,6 +431,8 @@ def summarize_counters(outdir: str, wl_name: str):
                 kind = "scan"
             elif "decode_kernel" in name:
                 kind = "decode"
+            elif "bwd_kernel" in name:
+                kind = "bwd" if name.split(",")[3].strip(" >)(")[:1] == "1" else "bwd_segment"
             elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_chunk:
                 kind = "copy"
             else:
@@ -319,10 +466,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--backward", action="store_true", help="time gla_bwd on the workload")
     args = ap.parse_args()
 
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.workload)
+        summarize_counters(args.summarize_counters,
+                           args.workload + ("_bwd" if args.backward else ""))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -340,6 +489,11 @@ def main():
         bench_decode(args, DECODE_WORKLOADS[args.workload])
         return
     wl = {**WORKLOADS, **SCALAR_WORKLOADS}[args.workload]
+    if args.backward:
+        if wl.scalar_gate or wl.dtype != "bf16":
+            raise SystemExit("--backward measures the bf16 per-key-dim workloads")
+        bench_backward(args, wl)
+        return
     fwd = gla.gla_fwd_scalar if wl.scalar_gate else gla.gla_fwd
     if wl.dtype != "bf16":
         raise SystemExit("bench.py measures the bf16 workloads")

@@ -76,37 +76,22 @@ template <typename E, int D, int C> struct BwdLayout {
     // e^Gamma U), then scale A and do v^T (rows i, columns j <= i)
     static constexpr int q = 0, k = q + TD, v = k + TD, o = v + TD, u = o + TD, a = u + TU, da = a + TA;
     static constexpr int bytes = da + TA;
-    // dq, dk1, dk2 before their row factors, fp32 [C][RP], over the q .. U tiles
+    // epilogue: Gc as an fp32 tile [C][RP] over the q .. U tiles
     static constexpr int RP = D + 4;
-    static_assert(3 * C * RP * 4 <= a, "result tiles must not reach the score tiles");
+    static_assert(C * RP * 4 <= a, "the Gc tile must not reach the score tiles");
 };
 
-// CPL consecutive values of one row, stored in the element type / fp32
-template <typename E, int CPL>
-__device__ __forceinline__ void store_row(rsrc_t r, int off, const float *x) {
+// four consecutive values of one row as fp32 (rows past the range read 0)
+template <typename E>
+__device__ __forceinline__ f32x4_t load4(rsrc_t r, int off) {
     if constexpr (std::is_same<E, BF16>::value) {
-        if constexpr (CPL == 2) {
-            const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)x[0]);
-            const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)x[1]);
-            __builtin_amdgcn_raw_buffer_store_b32(lo | (hi << 16), r, off, 0, 0);
-        } else {
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)x[0]), r, off, 0, 0);
-        }
+        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
     } else {
-        if constexpr (CPL == 2)
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(x[0]), __float_as_uint(x[1])}, r, off, 0, 0);
-        else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[0]), r, off, 0, 0);
+        return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
 }
-template <int CPL>
-__device__ __forceinline__ void store_row_f32(rsrc_t r, int off, const float *x) {
-    if constexpr (CPL == 2)
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(x[0]), __float_as_uint(x[1])}, r, off, 0, 0);
-    else
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[0]), r, off, 0, 0);
-}
-
 template <typename E, int D, int C, int BM>
 __global__ void __launch_bounds__((Shape<D, C>::NW * 64))
 bwd_kernel(const BwdParams p) {
@@ -127,12 +112,12 @@ bwd_kernel(const BwdParams p) {
     using gmem_t = typename E::gmem_t;
     using frag_t = typename E::frag_t;
     constexpr int es = sizeof(gmem_t);
-    static_assert(L::bytes + (3 * NW * D + D + C) * 4 <= 163840, "LDS");
+    static_assert(L::bytes + (2 * NW * D + 2 * D + C) * 4 <= 163840, "LDS");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
-    __shared__ __attribute__((aligned(16))) float sBt[NW * D];    // wave totals: gates, then q dq - k dk1
-    __shared__ __attribute__((aligned(16))) float sXt[NW * D];    // wave totals of k dk2
+    __shared__ __attribute__((aligned(16))) float sBt[NW * D];    // wave totals of the gates
     __shared__ __attribute__((aligned(16))) float sEG[D];         // exp2(Gamma)
+    __shared__ __attribute__((aligned(16))) float sGam[D];        // Gamma (log2)
     __shared__ __attribute__((aligned(16))) float sDot[NW * D];   // per-wave parts of e^Gamma sum_v U_{n+1} S_n
     __shared__ __attribute__((aligned(16))) float sDiag[C];       // do_i . v_i
     unsigned char *tQ = smem + L::q;
@@ -142,9 +127,7 @@ bwd_kernel(const BwdParams p) {
     unsigned char *tU = smem + L::u;
     unsigned char *tA = smem + L::a;
     unsigned char *tdA = smem + L::da;
-    float *rDq = reinterpret_cast<float *>(smem);
-    float *rDk1 = rDq + C * L::RP;
-    float *rDk2 = rDk1 + C * L::RP;
+    float *rGc = reinterpret_cast<float *>(smem);   // epilogue only
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -248,8 +231,11 @@ bwd_kernel(const BwdParams p) {
         }
 
         // ---- gate sums (log2 units) over this wave's rows --------------------
+        // The suffix after row i within the wave's rows is wt - Pf[i]; it only
+        // enters the exact path, where it is either exactly 0 (last row) or
+        // far below the exponent range, or small next to fp32 resolution.
         float Pf[RPW][CPL];   // inclusive prefix within the wave's rows
-        float Sw[RPW][CPL];   // suffix after the row within the wave's rows
+        float wt[CPL];        // the wave's total
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
             float run = 0.f;
@@ -258,12 +244,7 @@ bwd_kernel(const BwdParams p) {
                 run = __builtin_fmaf(rg[i].get(u), kLog2e, run);
                 Pf[i][u] = run;
             }
-            float suf = 0.f;
-#pragma unroll
-            for (int i = RPW - 1; i >= 0; --i) {
-                Sw[i][u] = suf;
-                suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
-            }
+            wt[u] = run;
             sBt[w * D + lane * CPL + u] = run;
         }
         block_sync();  // B1: wave totals and the v / do rows visible
@@ -301,7 +282,7 @@ bwd_kernel(const BwdParams p) {
                 qrow[u] = E::f2l(rq[i].get(u) * (p.scale * fexp2(gc)));  // scale q e^Gc
                 if constexpr (kFull) {
                     if (fast) krow[u] = E::f2l(rk[i].get(u) * fexp2(-gc));               // k e^-Gc
-                    else krow[u] = E::f2l(rk[i].get(u) * fexp2(aw[u] + Sw[i][u]));     // k e^{Gamma-Gc}
+                    else krow[u] = E::f2l(rk[i].get(u) * fexp2(aw[u] + (wt[u] - Pf[i][u])));   // k e^{Gamma-Gc}
                 }
             }
         }
@@ -325,7 +306,6 @@ bwd_kernel(const BwdParams p) {
         if constexpr (kFull) dot_us(c, sDot);   // e^Gamma sum_v U_{n+1} S_n
         block_sync();  // B3: operand tiles complete
 
-        float dq2x[RPW][CPL], dk1x[RPW][CPL];   // exact path: the decayed intra-chunk sums
         if constexpr (kFull) {
             // ---- do v^T and (fast path) scale A, causal 16x16 tiles -------------
 #pragma unroll
@@ -371,14 +351,9 @@ bwd_kernel(const BwdParams p) {
             block_sync();  // B4: do v^T tiles visible
 
             if (!fast) {
-                // exact path, this wave's rows: running products of per-token
-                // decays, A_ij = scale sum_d q_i k_j prod_{r=j+1..i} e^{g_r},
-                // dq2_i = sum_{j<i} (do_i.v_j) k_j prod(..), dk1_j = sum_{i>j} (do_i.v_j) q_i prod(..)
-                // (the do v^T tile is zero on its diagonal)
-#pragma unroll
-                for (int il = 0; il < RPW; ++il)
-#pragma unroll
-                    for (int u = 0; u < CPL; ++u) { dq2x[il][u] = 0.f; dk1x[il][u] = 0.f; }
+                // exact path, this wave's rows: A_ij = scale sum_d q_i k_j
+                // prod_{r=j+1..i} e^{g_r}, from running products of per-token
+                // decays (other rows' k and g re-read from the cache)
                 const int col0 = lane * CPL;
 #pragma unroll
                 for (int il = 0; il < RPW; ++il) {
@@ -391,52 +366,84 @@ bwd_kernel(const BwdParams p) {
                         RawG<CPL> gj;
                         kj.load(bk, ((t0 + j) * D + col0) * es, 0);
                         gj.load(bg, ((t0 + j) * D + col0) * 4, 0);
-                        const float dav = E::l2f(row_ptr(tdA, i, L::PC)[j]);
                         float part = 0.f;
 #pragma unroll
                         for (int u = 0; u < CPL; ++u) {
-                            const float kd = kj.get(u) * pr[u];
-                            part += rq[il].get(u) * kd;
-                            dq2x[il][u] += dav * kd;
+                            part += rq[il].get(u) * kj.get(u) * pr[u];
                             pr[u] *= fexp2(gj.get(u) * kLog2e);
                         }
                         const float s = wave_sum(part) * p.scale;
                         if (lane == 0) row_ptr(tA, i, L::PC)[j] = E::f2l(s);
                     }
-#pragma unroll
-                    for (int u = 0; u < CPL; ++u) pr[u] = 1.f;
-                    for (int i2 = i; i2 < C; ++i2) {   // rows of the chunk at or after row i
-                        Raw<E, CPL> qi;
-                        qi.load(bq, ((t0 + i2) * D + col0) * es, 0);
-                        const float dav = E::l2f(row_ptr(tdA, i2, L::PC)[i]);
-#pragma unroll
-                        for (int u = 0; u < CPL; ++u) dk1x[il][u] += dav * qi.get(u) * pr[u];
-                        if (i2 + 1 < C) {
-                            RawG<CPL> gn;
-                            gn.load(bg, ((t0 + i2 + 1) * D + col0) * 4, 0);
-#pragma unroll
-                            for (int u = 0; u < CPL; ++u) pr[u] *= fexp2(gn.get(u) * kLog2e);
-                        }
-                    }
                 }
                 block_sync();  // B5: exact scores visible
             }
 
-            // ---- dq, dk, dv column slices of this wave ----------------------------
-            f32x4_t Dq[NTW][NB], Dk1[NTW][NB], Dk2[NTW][NB], Dv[NTW][NB];
+            // ---- dv, dk2, U, dq, dk1 column slices of this wave --------------------
+            // each product's accumulators retire before the next group starts
+            const rsrc_t bdv = make_rsrc(reinterpret_cast<gmem_t *>(p.dv) + bh * long(T) * D, long(T) * D * es);
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
+            for (int nt = 0; nt < NTW; ++nt) {
+                f32x4_t Dv[NB];
+#pragma unroll
+                for (int m = 0; m < NB; ++m) Dv[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                // k~ U~ (or k^ U): this wave's U tile columns along d
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const frag_t uf = E::ld_col8(tU, L::PD, ks * 32 + 8 * q4, cb + 16 * nt, n16);
+#pragma unroll
+                    for (int m = 0; m < NB; ++m)
+                        Dv[m] = E::mma(uf, E::ld_frag(row_ptr(tK, 16 * m + n16, L::PD) + ks * 32 + 8 * q4), Dv[m]);
+                }
+                // (scale A)^T do over the causal token steps (rows i >= j)
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+                    const frag_t of = E::ld_col8(tO, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16);
+#pragma unroll
+                    for (int m = 0; m < NB; ++m)
+                        if (ts * 32 + 31 >= 16 * m)
+                            Dv[m] = E::mma(of, E::ld_col8(tA, L::PC, ts * 32 + 8 * q4, 16 * m, n16), Dv[m]);
+                }
+                // dv rows straight to HBM (rows past T are dropped)
+#pragma unroll
+                for (int m = 0; m < NB; ++m)
+                    E::st4(bdv, ((t0 + 16 * m + n16) * D + cb + 16 * nt + 4 * q4) * es, Dv[m]);
+            }
+            // v U~^T (or v U^T): U tile rows d of this wave along v
+            f32x4_t Dk2[NTW][NB];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+                for (int m = 0; m < NB; ++m) Dk2[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const frag_t uf = E::ld_frag(row_ptr(tU, cb + 16 * nt + n16, L::PD) + ks * 32 + 8 * q4);
+#pragma unroll
+                    for (int m = 0; m < NB; ++m)
+                        Dk2[nt][m] = E::mma(uf, E::ld_frag(row_ptr(tV, 16 * m + n16, L::PD) + ks * 32 + 8 * q4), Dk2[nt][m]);
+                }
+            }
+            // U_n = e^Gamma U_{n+1} + (scale q e^Gc)^T do
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+                    const frag_t a = E::ld_col8(tQ, L::PD, ts * 32 + 8 * q4, 16 * mt, n16);
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+                        U[mt][nt] = E::mma(a, E::ld_col8(tO, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16), U[mt][nt]);
+                }
+            // do S_n^T (S_n rows d of this wave, straight from HBM) and, on the
+            // fast path, (do v^T) k e^-Gc
+            const float *Sn = p.states + (bh * long(N) + c) * long(D) * D;
+            f32x4_t Dq[NTW][NB], Dk1[NTW][NB];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {
                     Dq[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                     Dk1[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    Dk2[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    Dv[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
-            // do S_n^T: S_n rows d of this wave's slice, straight from HBM
-            const float *Sn = p.states + (bh * long(N) + c) * long(D) * D;
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const float *src = Sn + (cb + 16 * nt + n16) * D + ks * 32 + 8 * q4;
@@ -448,159 +455,152 @@ bwd_kernel(const BwdParams p) {
                     for (int m = 0; m < NB; ++m)
                         Dq[nt][m] = E::mma(sf, E::ld_frag(row_ptr(tO, 16 * m + n16, L::PD) + ks * 32 + 8 * q4), Dq[nt][m]);
                 }
-            // v U^T (U tile rows d along v)
+                if (fast) {
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
+                    for (int ts = 0; ts < TS; ++ts) {
+                        // dq: rows i, tokens j <= i;  dk1: rows j, tokens i >= j
+                        const frag_t kf = E::ld_col8(tK, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16);
+                        const frag_t qf = E::ld_col8(tQ, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const frag_t uf = E::ld_frag(row_ptr(tU, cb + 16 * nt + n16, L::PD) + ks * 32 + 8 * q4);
-#pragma unroll
-                    for (int m = 0; m < NB; ++m)
-                        Dk2[nt][m] = E::mma(uf, E::ld_frag(row_ptr(tV, 16 * m + n16, L::PD) + ks * 32 + 8 * q4), Dk2[nt][m]);
-                }
-            // k~ U~ (or k^ U): U tile columns of this wave along d
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const frag_t uf = E::ld_col8(tU, L::PD, ks * 32 + 8 * q4, cb + 16 * nt, n16);
-#pragma unroll
-                    for (int m = 0; m < NB; ++m)
-                        Dv[nt][m] = E::mma(uf, E::ld_frag(row_ptr(tK, 16 * m + n16, L::PD) + ks * 32 + 8 * q4), Dv[nt][m]);
-                }
-            // causal intra-chunk terms over 32-deep token steps
-#pragma unroll
-            for (int m = 0; m < NB; ++m)
-#pragma unroll
-                for (int ts = 0; ts < TS; ++ts) {
-                    const bool lower = ts * 32 <= 16 * m + 15;   // some j <= i in the step (dq)
-                    const bool upper = ts * 32 + 31 >= 16 * m;   // some i >= j in the step (dk, dv)
-                    if (fast && lower) {   // dq += (do v^T) k e^-Gc
-                        const frag_t af = E::ld_frag(row_ptr(tdA, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
-#pragma unroll
-                        for (int nt = 0; nt < NTW; ++nt)
-                            Dq[nt][m] = E::mma(E::ld_col8(tK, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16), af, Dq[nt][m]);
-                    }
-                    if (upper) {
-                        const frag_t at = E::ld_col8(tA, L::PC, ts * 32 + 8 * q4, 16 * m, n16);
-                        const frag_t dat = E::ld_col8(tdA, L::PC, ts * 32 + 8 * q4, 16 * m, n16);
-#pragma unroll
-                        for (int nt = 0; nt < NTW; ++nt) {
-                            // dv += (scale A)^T do
-                            Dv[nt][m] = E::mma(E::ld_col8(tO, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16), at, Dv[nt][m]);
-                            // dk += (do v^T)^T scale q e^Gc   (fast path)
-                            if (fast)
-                                Dk1[nt][m] = E::mma(E::ld_col8(tQ, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16), dat, Dk1[nt][m]);
+                        for (int m = 0; m < NB; ++m) {
+                            if (ts * 32 <= 16 * m + 15)
+                                Dq[nt][m] = E::mma(kf, E::ld_frag(row_ptr(tdA, 16 * m + n16, L::PC) + ts * 32 + 8 * q4), Dq[nt][m]);
+                            if (ts * 32 + 31 >= 16 * m)
+                                Dk1[nt][m] = E::mma(qf, E::ld_col8(tdA, L::PC, ts * 32 + 8 * q4, 16 * m, n16), Dk1[nt][m]);
                         }
                     }
                 }
-            // dv rows straight to HBM (rows past T are dropped)
-            const rsrc_t bdv = make_rsrc(reinterpret_cast<gmem_t *>(p.dv) + bh * long(T) * D, long(T) * D * es);
-#pragma unroll
-            for (int m = 0; m < NB; ++m)
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    E::st4(bdv, ((t0 + 16 * m + n16) * D + cb + 16 * nt + 4 * q4) * es, Dv[nt][m]);
-
-            // ---- U_n = e^Gamma U_{n+1} + (scale q e^Gc)^T do ------------------------
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int ts = 0; ts < TS; ++ts) {
-                    const frag_t a = E::ld_col8(tQ, L::PD, ts * 32 + 8 * q4, 16 * mt, n16);
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt)
-                        U[mt][nt] = E::mma(a, E::ld_col8(tO, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16), U[mt][nt]);
-                }
+            }
             block_sync();  // B6: every wave is done with the operand tiles
 
-            // dq, dk1, dk2 (before their row factors) over the operand tiles
+            // Gc (log2, chunk-local inclusive cumsum) as an fp32 tile over the q, k tiles
 #pragma unroll
-            for (int m = 0; m < NB; ++m)
+            for (int i = 0; i < RPW; ++i)
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    const int off = (16 * m + n16) * L::RP + cb + 16 * nt + 4 * q4;
-                    *reinterpret_cast<f32x4_t *>(rDq + off) = Dq[nt][m];
-                    *reinterpret_cast<f32x4_t *>(rDk1 + off) = Dk1[nt][m];
-                    *reinterpret_cast<f32x4_t *>(rDk2 + off) = Dk2[nt][m];
-                }
-            block_sync();  // B7: results visible
+                for (int u = 0; u < CPL; ++u) rGc[(r0 + i) * L::RP + lane * CPL + u] = rw[u] + Pf[i][u];
+            if (w == 0)
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) sGam[lane * CPL + u] = gam[u];
+            block_sync();  // B7: Gc visible
 
-            // ---- epilogue on this wave's rows: dq, dk, then dg -------------------
-            float dqo[RPW][CPL], dko[RPW][CPL], w1[RPW][CPL], xk[RPW][CPL];
-#pragma unroll
-            for (int il = 0; il < RPW; ++il) {
-                const int i = r0 + il;
-                const float dgl = p.scale * sDiag[i];   // scale do_i . v_i
-#pragma unroll
-                for (int u = 0; u < CPL; ++u) {
-                    const int col = lane * CPL + u;
-                    const float gc = rw[u] + Pf[il][u];
-                    const float dqv = rDq[i * L::RP + col];
-                    const float k1v = rDk1[i * L::RP + col], k2v = rDk2[i * L::RP + col];
-                    float dk1, dk2;
-                    if (fast) {
-                        const float ek = fexp2(-gc);
-                        dqo[il][u] = p.scale * fexp2(gc) * dqv;
-                        dk1 = ek * k1v;
-                        dk2 = ek * k2v;
-                    } else {
-                        dqo[il][u] = p.scale * (fexp2(gc) * dqv + dq2x[il][u]);
-                        dk1 = p.scale * dk1x[il][u];
-                        dk2 = fexp2(aw[u] + Sw[il][u]) * k2v;
-                    }
-                    const float qv = rq[il].get(u), kv = rk[il].get(u);
-                    w1[il][u] = qv * dqo[il][u] - kv * dk1;
-                    xk[il][u] = kv * dk2;
-                    // the j = i terms, which cancel in q dq - k dk, added after
-                    dqo[il][u] += dgl * kv;
-                    dko[il][u] = dk1 + dk2 + dgl * qv;
-                }
-            }
-            // within the wave: rows t' >= t of w1 (inclusive), rows j < t of k dk2
-            float dgo[RPW][CPL];
-#pragma unroll
-            for (int u = 0; u < CPL; ++u) {
-                float suf = 0.f, pre = 0.f;
-#pragma unroll
-                for (int il = RPW - 1; il >= 0; --il) {
-                    suf += w1[il][u];
-                    dgo[il][u] = suf;
-                }
-#pragma unroll
-                for (int il = 0; il < RPW; ++il) {
-                    dgo[il][u] += pre;
-                    pre += xk[il][u];
-                }
-                sBt[w * D + lane * CPL + u] = suf;
-                sXt[w * D + lane * CPL + u] = pre;
-            }
-            block_sync();  // B8: wave totals visible
-            float later[CPL];   // later waves' w1, earlier waves' k dk2, the state term
-#pragma unroll
-            for (int u = 0; u < CPL; ++u) {
-                const int col = lane * CPL + u;
-                float x = 0.f;
-#pragma unroll
-                for (int j = 0; j < NW; ++j) {
-                    if (j > w) x += sBt[j * D + col];
-                    if (j < w) x += sXt[j * D + col];
-                    x += sDot[j * D + col];
-                }
-                later[u] = x;
-            }
+            // ---- epilogue in the accumulator layout: lane (n16, q4) holds rows
+            // 16m + n16, columns cb + 16nt + 4q4 .. +3 of dq, dk1, dk2 ---------------
             const rsrc_t bdq = make_rsrc(reinterpret_cast<gmem_t *>(p.dq) + bh * long(T) * D, long(T) * D * es);
             const rsrc_t bdk = make_rsrc(reinterpret_cast<gmem_t *>(p.dk) + bh * long(T) * D, long(T) * D * es);
             const rsrc_t bdg = make_rsrc(p.dg + bh * long(T) * D, long(T) * D * 4);
 #pragma unroll
-            for (int il = 0; il < RPW; ++il) {
-                const int e0 = (t0 + r0 + il) * D + lane * CPL;
-                float dgv[CPL];
+            for (int nt = 0; nt < NTW; ++nt) {
+                const int d0 = cb + 16 * nt + 4 * q4;   // this lane's four columns
+                f32x4_t w1[NB], xk[NB];
 #pragma unroll
-                for (int u = 0; u < CPL; ++u) dgv[u] = dgo[il][u] + later[u];
-                store_row<E, CPL>(bdq, e0 * es, dqo[il]);
-                store_row<E, CPL>(bdk, e0 * es, dko[il]);
-                store_row_f32<CPL>(bdg, e0 * 4, dgv);
+                for (int m = 0; m < NB; ++m) {
+                    const int i = 16 * m + n16;
+                    const int eoff = (t0 + i) * D + d0;
+                    const f32x4_t qv = load4<E>(bq, eoff * es), kv = load4<E>(bk, eoff * es);
+                    const f32x4_t gc = *reinterpret_cast<const f32x4_t *>(rGc + i * L::RP + d0);
+                    const float dgl = p.scale * sDiag[i];   // scale do_i . v_i
+                    f32x4_t dq2 = {0.f, 0.f, 0.f, 0.f}, dk1s = {0.f, 0.f, 0.f, 0.f};
+                    if (!fast) {
+                        // exact path: dq2_i = sum_{j<i} (do_i.v_j) k_j prod_{r=j+1..i} e^{g_r},
+                        // dk1_i = sum_{i2>i} (do_i2.v_i) q_i2 prod_{r=i+1..i2} e^{g_r}
+                        // (the do v^T tile is zero on its diagonal)
+                        f32x4_t pr = {1.f, 1.f, 1.f, 1.f};
+                        for (int j = i; j >= 0; --j) {
+                            const f32x4_t kj = load4<E>(bk, ((t0 + j) * D + d0) * es);
+                            const f32x4_t gj = load4<F32>(bg, ((t0 + j) * D + d0) * 4);
+                            const float dav = E::l2f(row_ptr(tdA, i, L::PC)[j]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                dq2[e] += dav * kj[e] * pr[e];
+                                pr[e] *= fexp2(gj[e] * kLog2e);
+                            }
+                        }
+                        pr = f32x4_t{1.f, 1.f, 1.f, 1.f};
+                        for (int i2 = i; i2 < C; ++i2) {
+                            const f32x4_t qi = load4<E>(bq, ((t0 + i2) * D + d0) * es);
+                            const float dav = E::l2f(row_ptr(tdA, i2, L::PC)[i]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) dk1s[e] += dav * qi[e] * pr[e];
+                            if (i2 + 1 < C) {
+                                const f32x4_t gn = load4<F32>(bg, ((t0 + i2 + 1) * D + d0) * 4);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) pr[e] *= fexp2(gn[e] * kLog2e);
+                            }
+                        }
+                    }
+                    f32x4_t dqo, dko;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float dq1, dk1, dk2;
+                        if (fast) {
+                            const float ek = fexp2(-gc[e]);
+                            dq1 = p.scale * fexp2(gc[e]) * Dq[nt][m][e];
+                            dk1 = ek * Dk1[nt][m][e];
+                            dk2 = ek * Dk2[nt][m][e];
+                        } else {
+                            dq1 = p.scale * (fexp2(gc[e]) * Dq[nt][m][e] + dq2[e]);
+                            dk1 = p.scale * dk1s[e];
+                            dk2 = fexp2(sGam[d0 + e] - gc[e]) * Dk2[nt][m][e];
+                        }
+                        w1[m][e] = qv[e] * dq1 - kv[e] * dk1;
+                        xk[m][e] = kv[e] * dk2;
+                        // the j = i terms, which cancel in q dq - k dk, added after
+                        dqo[e] = dq1 + dgl * kv[e];
+                        dko[e] = dk1 + dk2 + dgl * qv[e];
+                    }
+                    E::st4(bdq, eoff * es, dqo);
+                    E::st4(bdk, eoff * es, dko);
+                }
+                // dg_i = sum_{t>=i} w1_t + sum_{j<i} k_j dk2_j + e^Gamma sum_v U_{n+1} S_n,
+                // rows along the 16 lanes of a group and the NB row tiles
+                f32x4_t carry_w = {0.f, 0.f, 0.f, 0.f}, carry_x = {0.f, 0.f, 0.f, 0.f};
+                f32x4_t dgv[NB];
+#pragma unroll
+                for (int m = NB - 1; m >= 0; --m) {   // suffix of w1
+                    f32x4_t x = w1[m];
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float y = __shfl_down(x[e], off, 16);
+                            if (n16 + off < 16) x[e] += y;
+                        }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dgv[m][e] = x[e] + carry_w[e];
+                        carry_w[e] += __shfl(x[e], 0, 16);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {   // exclusive prefix of k dk2
+                    f32x4_t x = xk[m];
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float y = __shfl_up(x[e], off, 16);
+                            if (n16 >= off) x[e] += y;
+                        }
+                    // the previous row's inclusive sum, not x - xk: the row's own
+                    // term can be the large one that must not enter dg
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float ex = __shfl_up(x[e], 1, 16);
+                        dgv[m][e] += carry_x[e] + (n16 > 0 ? ex : 0.f);
+                        carry_x[e] += __shfl(x[e], 15, 16);
+                    }
+                }
+                f32x4_t dot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < NW; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dot[e] += sDot[j * D + d0 + e];
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dgv[m][e] += dot[e];
+                    F32::st4(bdg, ((t0 + 16 * m + n16) * D + d0) * 4, dgv[m]);
+                }
             }
         } else {
             // state units: only U_n = e^Gamma U_{n+1} + (scale q e^Gc)^T do
