@@ -63,6 +63,7 @@ namespace gla {
 
 enum { BM_SEG = 0, BM_FULL = 1 };
 
+
 template <typename E, int D, int C> struct BwdLayout {
     static constexpr int es = sizeof(typename E::lds_t);
     // row pitches (bytes): bf16 rows padded by 32 bytes for the transposing
@@ -79,6 +80,23 @@ template <typename E, int D, int C> struct BwdLayout {
     // epilogue: Gc as an fp32 tile [C][RP] over the q .. U tiles
     static constexpr int RP = D + 4;
     static_assert(C * RP * 4 <= a, "the Gc tile must not reach the score tiles");
+};
+
+// four consecutive values of one row, kept as loaded until get() decodes
+// them (so that issuing the load does not wait for it)
+template <typename E> struct Raw4;
+template <> struct Raw4<BF16> {
+    u32x2_t x;
+    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
+    __device__ f32x4_t get() const {
+        return f32x4_t{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                       __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+    }
+};
+template <> struct Raw4<F32> {
+    u32x4_t x;
+    __device__ void load(rsrc_t r, int off) { x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+    __device__ f32x4_t get() const { return __builtin_bit_cast(f32x4_t, x); }
 };
 
 // four consecutive values of one row as fp32 (rows past the range read 0)
@@ -118,7 +136,7 @@ bwd_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sBt[NW * D];    // wave totals of the gates
     __shared__ __attribute__((aligned(16))) float sEG[D];         // exp2(Gamma)
     __shared__ __attribute__((aligned(16))) float sGam[D];        // Gamma (log2)
-    __shared__ __attribute__((aligned(16))) float sDot[NW * D];   // per-wave parts of e^Gamma sum_v U_{n+1} S_n
+    __shared__ __attribute__((aligned(16))) float sDot[NW * D];   // per-wave parts of sum_v U_{n+1} S_n
     __shared__ __attribute__((aligned(16))) float sDiag[C];       // do_i . v_i
     unsigned char *tQ = smem + L::q;
     unsigned char *tK = smem + L::k;
@@ -168,17 +186,16 @@ bwd_kernel(const BwdParams p) {
                 for (int e = 0; e < 4; ++e)
                     U[mt][nt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + cb + 16 * nt + n16] : 0.f;
     }
-    // per-wave parts of sum_v U S_c over this wave's columns
-    auto dot_us = [&](int c, float *dst) {
-        const float *S = p.states + (bh * long(N) + c) * long(D) * D;
+    // per-wave parts of sum_v U S_n over this wave's columns, S_n prefetched
+    // in the accumulator layout
+    auto dot_us = [&](const float (&sacc)[MT][NTW][4], float *dst) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float part = 0.f;
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    part += U[mt][nt][e] * S[(16 * mt + 4 * q4 + e) * D + cb + 16 * nt + n16];
+                for (int nt = 0; nt < NTW; ++nt) part += U[mt][nt][e] * sacc[mt][nt][e];
 #pragma unroll
                 for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m, 64);
                 if (n16 == 0) dst[w * D + 16 * mt + 4 * q4 + e] = part;
@@ -201,7 +218,20 @@ bwd_kernel(const BwdParams p) {
         // ---- this chunk's rows: gates, q, k into registers; v, do into LDS ----
         RawG<CPL> rg[RPW];
         Raw<E, CPL> rq[RPW], rk[RPW];
+        float sacc[MT][NTW][4];   // S_n in the accumulator layout (for the dg state term)
         {
+            if constexpr (kFull) {   // one lane offset, the row in the uniform offset
+                const rsrc_t bs = make_rsrc(p.states + (bh * long(N) + c) * long(D) * D, D * D * 4);
+                const int voff = ((4 * q4) * D + cb + n16) * 4;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sacc[mt][nt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                bs, voff, ((16 * mt + e) * D + 16 * nt) * 4, 0));
+            }
             const int eoff = (t0 + r0) * D + lane * CPL;
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
@@ -228,6 +258,7 @@ bwd_kernel(const BwdParams p) {
             }
             mem_fence_compiler();
             wait_vmem<0>();
+            if constexpr (kFull) dot_us(sacc, sDot);   // sum_v U_{n+1} S_n (e^Gamma applied in the epilogue)
         }
 
         // ---- gate sums (log2 units) over this wave's rows --------------------
@@ -303,7 +334,6 @@ bwd_kernel(const BwdParams p) {
                     U[mt][nt][e] *= egv[e];
                 }
         }
-        if constexpr (kFull) dot_us(c, sDot);   // e^Gamma sum_v U_{n+1} S_n
         block_sync();  // B3: operand tiles complete
 
         if constexpr (kFull) {
@@ -381,6 +411,7 @@ bwd_kernel(const BwdParams p) {
 
             // ---- dv, dk2, U, dq, dk1 column slices of this wave --------------------
             // each product's accumulators retire before the next group starts
+            const rsrc_t bs = make_rsrc(p.states + (bh * long(N) + c) * long(D) * D, D * D * 4);
             const rsrc_t bdv = make_rsrc(reinterpret_cast<gmem_t *>(p.dv) + bh * long(T) * D, long(T) * D * es);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
@@ -433,9 +464,7 @@ bwd_kernel(const BwdParams p) {
                     for (int nt = 0; nt < NTW; ++nt)
                         U[mt][nt] = E::mma(a, E::ld_col8(tO, L::PD, ts * 32 + 8 * q4, cb + 16 * nt, n16), U[mt][nt]);
                 }
-            // do S_n^T (S_n rows d of this wave, straight from HBM) and, on the
-            // fast path, (do v^T) k e^-Gc
-            const float *Sn = p.states + (bh * long(N) + c) * long(D) * D;
+            // do S_n^T (S_n rows d of this wave) and, on the fast path, (do v^T) k e^-Gc
             f32x4_t Dq[NTW][NB], Dk1[NTW][NB];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
@@ -446,9 +475,9 @@ bwd_kernel(const BwdParams p) {
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const float *src = Sn + (cb + 16 * nt + n16) * D + ks * 32 + 8 * q4;
-                    const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(src);
-                    const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(src + 4);
+                    const int voff = ((cb + n16) * D + 8 * q4) * 4, soff = (16 * nt * D + ks * 32) * 4;
+                    const f32x4_t lo = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff, soff, 0));
+                    const f32x4_t hi = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff + 16, soff, 0));
                     const float xs[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     const frag_t sf = E::pack(xs);
 #pragma unroll
@@ -496,7 +525,10 @@ bwd_kernel(const BwdParams p) {
                 for (int m = 0; m < NB; ++m) {
                     const int i = 16 * m + n16;
                     const int eoff = (t0 + i) * D + d0;
-                    const f32x4_t qv = load4<E>(bq, eoff * es), kv = load4<E>(bk, eoff * es);
+                    Raw4<E> eqr, ekr;
+                    eqr.load(bq, eoff * es);
+                    ekr.load(bk, eoff * es);
+                    const f32x4_t qv = eqr.get(), kv = ekr.get();
                     const f32x4_t gc = *reinterpret_cast<const f32x4_t *>(rGc + i * L::RP + d0);
                     const float dgl = p.scale * sDiag[i];   // scale do_i . v_i
                     f32x4_t dq2 = {0.f, 0.f, 0.f, 0.f}, dk1s = {0.f, 0.f, 0.f, 0.f};
@@ -595,6 +627,8 @@ bwd_kernel(const BwdParams p) {
                 for (int j = 0; j < NW; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) dot[e] += sDot[j * D + d0 + e];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dot[e] *= sEG[d0 + e];   // e^Gamma sum_v U_{n+1} S_n
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {
 #pragma unroll
