@@ -22,6 +22,12 @@ Parity status of each function (what pins it is in ``tests/test_oracle.py``):
   PyTorch forward, central finite differences, hand-derived golden fixtures
   (``tests/golden/backward/``) and the identity that dg is the reverse cumsum
   of q*dq - k*dk plus the final-state term.
+* ``gdn_recurrence`` (C, fp64: the gated delta rule token by token) and
+  ``gdn_chunked_reference`` (its chunk form with a triangular solve): pinned
+  against each other at several chunk sizes, a hand-derived fixture
+  (``tests/golden/gdn/``), the beta = 0 closed form (pure decay of h0), the
+  exact-overwrite behaviour for orthonormal keys with beta = 1, and split
+  invariance.
 * ``scalar_gate_recurrence`` (scalar gate g [B,H,T], through
   ``token_recurrence``) and ``scalar_gate_quadratic`` (the masked quadratic
   form): pinned against each other, a hand-derived golden fixture
@@ -34,6 +40,8 @@ from .reference import (  # noqa: F401
     chunk_cumsum,
     chunked_reference,
     closed_form_zero_gate,
+    gdn_chunked_reference,
+    gdn_recurrence,
     intra_scores,
     oracle_threads,
     scalar_gate_quadratic,

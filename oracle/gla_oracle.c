@@ -247,3 +247,78 @@ int gla_oracle_bwd_f64(const double *q, const double *k, const double *v,
     }
     return status;
 }
+
+/*
+ * fp64 token-by-token oracle for the gated delta rule (Gated DeltaNet
+ * forward).  TEST INFRASTRUCTURE ONLY, like the functions above.
+ *
+ * The evaluation page names the Gated Delta Network class as gating plus an
+ * incremental ("delta") update of the recurrent state ("面向长序列大模型的线性
+ * 注意力算子性能评测方法与优化实践", sections 一 and 三.3) and gives no formula;
+ * the reading taken is the published gated delta rule: per (b, h),
+ *
+ *   S <- h0 (or 0)                                   K x V
+ *   for t = 0 .. T-1
+ *     S <- exp(g[t]) * S                             (scalar gate per token)
+ *     S <- S + beta[t] * k_t^T (v_t - k_t S)         (delta update)
+ *     o[t, :] <- scale * q_t S
+ *   h_final <- S
+ *
+ * Layouts: q, k [B,H,T,K]; v, o [B,H,T,V]; g, beta [B,H,T]; h0, h_final
+ * [B,H,K,V].  Value columns of S are independent (the update of column c
+ * only reads column c), so the work is split over (b, h, block of 16
+ * columns) as in gla_oracle_f64.
+ */
+int gdn_oracle_f64(const double *q, const double *k, const double *v,
+                   const double *g, const double *beta, const double *h0,
+                   double *o, double *h_final, long B, long H, long T, long K,
+                   long V, double scale, int threads) {
+    if (B < 0 || H < 0 || T < 0 || K <= 0 || V <= 0) return -1;
+    const long BH = B * H;
+    const long nvb = (V + ORACLE_VBLK - 1) / ORACLE_VBLK;
+    int status = 0;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long job = 0; job < BH * nvb; ++job) {
+        const long bh = job / nvb;
+        const long c0 = (job % nvb) * ORACLE_VBLK;
+        const long nc = (V - c0) < ORACLE_VBLK ? (V - c0) : ORACLE_VBLK;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(K * nc));
+        if (!S) {
+#pragma omp atomic write
+            status = -2;
+            continue;
+        }
+        for (long d = 0; d < K; ++d)
+            for (long c = 0; c < nc; ++c) S[d * nc + c] = h0 ? h0[(bh * K + d) * V + c0 + c] : 0.0;
+        for (long t = 0; t < T; ++t) {
+            const double *qt = q + (bh * T + t) * K;
+            const double *kt = k + (bh * T + t) * K;
+            const double *vt = v + (bh * T + t) * V + c0;
+            const double a = exp(g[bh * T + t]), b = beta[bh * T + t];
+            for (long i = 0; i < K * nc; ++i) S[i] *= a;
+            for (long c = 0; c < nc; ++c) {
+                double ks = 0.0;   /* (k_t S)[c] */
+                for (long d = 0; d < K; ++d) ks += kt[d] * S[d * nc + c];
+                const double r = b * (vt[c] - ks);
+                for (long d = 0; d < K; ++d) S[d * nc + c] += kt[d] * r;
+            }
+            double *ot = o + (bh * T + t) * V + c0;
+            for (long c = 0; c < nc; ++c) {
+                double s = 0.0;
+                for (long d = 0; d < K; ++d) s += qt[d] * S[d * nc + c];
+                ot[c] = scale * s;
+            }
+        }
+        if (h_final)
+            for (long d = 0; d < K; ++d)
+                for (long c = 0; c < nc; ++c) h_final[(bh * K + d) * V + c0 + c] = S[d * nc + c];
+        free(S);
+    }
+    return status;
+}

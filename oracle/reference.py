@@ -58,6 +58,9 @@ def _load():
         lib.gla_oracle_bwd_f64.argtypes = [dp] * 12 + [ctypes.c_long] * 5 + [
             ctypes.c_double, ctypes.c_long, ctypes.c_int]
         lib.gla_oracle_bwd_f64.restype = ctypes.c_int
+        lib.gdn_oracle_f64.argtypes = [dp] * 8 + [ctypes.c_long] * 5 + [ctypes.c_double,
+                                                                     ctypes.c_int]
+        lib.gdn_oracle_f64.restype = ctypes.c_int
         lib.gla_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -309,4 +312,70 @@ def scalar_gate_quadratic(q, k, v, g, h0=None, scale=1.0):
                 hf[b, h] = np.exp(G[T - 1]) * base + (Kk * w[:, None]).T @ Vv
             else:
                 hf[b, h] = base
+    return o, hf
+
+
+# --- gated delta rule (Gated DeltaNet forward) ---------------------------------
+#
+# The evaluation page ("面向长序列大模型的线性注意力算子性能评测方法与优化实践",
+# sections 一 and 三.3) describes the GDN class only as gating plus an
+# incremental ("delta") state update.  Reading taken: the published gated
+# delta rule with a scalar gate and write strength per token and head,
+#     S_t = exp(g_t) (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t,
+#     o_t = scale q_t S_t.
+
+
+def gdn_recurrence(q, k, v, g, beta, h0=None, scale=1.0, threads=0, want_final=True):
+    """The oracle for the gated delta rule (C, fp64, token by token).
+
+    q, k [B,H,T,K]; v [B,H,T,V]; g, beta [B,H,T]; h0 [B,H,K,V] or None.
+    Returns (o, h_final)."""
+    q, k, v, g, beta, h0 = (_f64(x) for x in (q, k, v, g, beta, h0))
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    assert k.shape == (B, H, T, K) and v.shape == (B, H, T, V)
+    assert g.shape == (B, H, T) and beta.shape == (B, H, T)
+    o = np.empty((B, H, T, V))
+    hf = np.empty((B, H, K, V)) if want_final else None
+    rc = _load().gdn_oracle_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                _ptr(o), _ptr(hf), B, H, T, K, V, float(scale), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"gdn_oracle_f64 failed with status {rc}")
+    return o, hf
+
+
+def gdn_chunked_reference(q, k, v, g, beta, h0=None, scale=1.0, chunk=64):
+    """The gated delta rule in chunk form, fp64, as a second evaluation.
+
+    Unrolling the recurrence inside a chunk from its start state S (gamma_i =
+    exp of the chunk-local inclusive cumsum of g):
+      the written rows u_i = beta_i (v_i - exp(g_i) k_i S_{i-1}) satisfy
+      (I + A) U = diag(beta) V - diag(beta gamma) K S,
+      A_ij = beta_i (gamma_i / gamma_j) (k_i . k_j) for j < i;
+      o_i = scale [gamma_i q_i S + sum_{j<=i} (gamma_i / gamma_j) (q_i . k_j) u_j];
+      S_next = gamma_last S + sum_j (gamma_last / gamma_j) k_j^T u_j.
+    The triangular system is solved with numpy.linalg.solve."""
+    q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    o = np.zeros((B, H, T, V))
+    hf = np.zeros((B, H, K, V))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((K, V)) if h0 is None else np.array(h0[b, h], dtype=np.float64)
+            for lo in range(0, T, chunk):
+                hi = min(T, lo + chunk)
+                n = hi - lo
+                Q, Kc, Vc = q[b, h, lo:hi], k[b, h, lo:hi], v[b, h, lo:hi]
+                bt = beta[b, h, lo:hi]
+                G = np.cumsum(g[b, h, lo:hi])
+                ratio = np.exp(G[:, None] - G[None, :])          # gamma_i / gamma_j
+                strict = np.tril(np.ones((n, n)), -1)
+                A = bt[:, None] * ratio * (Kc @ Kc.T) * strict
+                rhs = bt[:, None] * Vc - (bt * np.exp(G))[:, None] * (Kc @ S)
+                U = np.linalg.solve(np.eye(n) + A, rhs)
+                P = (Q @ Kc.T) * ratio * np.tril(np.ones((n, n)))
+                o[b, h, lo:hi] = scale * (np.exp(G)[:, None] * (Q @ S) + P @ U)
+                S = np.exp(G[-1]) * S + (Kc * np.exp(G[-1] - G)[:, None]).T @ U
+            hf[b, h] = S
     return o, hf

@@ -475,3 +475,111 @@ def test_backward_gate_gradient_identity(with_h0):
             q[:, :, sl], k[:, :, sl], v[:, :, sl], g[:, :, sl], states[:, :, n], do[:, :, sl],
             dhf, 0.5)
         assert _rel(dg[:, :, t0], np.sum(U * states[:, :, n], axis=-1)) < 1e-11
+
+
+# --- gated delta rule ------------------------------------------------------------
+
+def _gdn_rand(rng, B, H, T, K, V, h0=True, gate_scale=0.3):
+    q = rng.standard_normal((B, H, T, K))
+    k = rng.standard_normal((B, H, T, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, T, V))
+    g = -np.abs(rng.standard_normal((B, H, T))) * gate_scale
+    beta = rng.uniform(0.05, 1.0, (B, H, T))
+    h = rng.standard_normal((B, H, K, V)) if h0 else None
+    return q, k, v, g, beta, h
+
+
+def _gdn_golden():
+    with open(os.path.join(GOLDEN, "gdn", "two_tokens.json")) as f:
+        c = json.load(f)
+    T, K, V = c["T"], c["K"], c["V"]
+    arr = lambda key, shape: np.array(c[key], dtype=np.float64).reshape(shape)  # noqa: E731
+    return dict(q=arr("q", (1, 1, T, K)), k=arr("k", (1, 1, T, K)), v=arr("v", (1, 1, T, V)),
+                g=np.log(arr("decay", (1, 1, T))), beta=arr("beta", (1, 1, T)),
+                h0=arr("h0", (1, 1, K, V)), scale=c["scale"], o=arr("o", (1, 1, T, V)),
+                hf=arr("h_final", (1, 1, K, V)))
+
+
+@pytest.mark.parametrize("fn", ["gdn_recurrence", "gdn_chunked_reference"])
+def test_gdn_matches_golden(fn):
+    c = _gdn_golden()
+    o, hf = getattr(oracle, fn)(c["q"], c["k"], c["v"], c["g"], c["beta"], c["h0"], c["scale"])
+    np.testing.assert_allclose(o, c["o"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(hf, c["hf"], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 3, 2), (2, 2, 37, 8, 5), (1, 2, 130, 16, 16)])
+@pytest.mark.parametrize("chunk", [1, 5, 16, 64])
+def test_gdn_chunked_matches_recurrence(shape, chunk):
+    rng = np.random.default_rng(hash(("gdn", shape, chunk)) % 2**32)
+    q, k, v, g, beta, h0 = _gdn_rand(rng, *shape)
+    o, hf = oracle.gdn_recurrence(q, k, v, g, beta, h0, scale=0.4)
+    oc, hfc = oracle.gdn_chunked_reference(q, k, v, g, beta, h0, scale=0.4, chunk=chunk)
+    assert _rel(o, oc) < 1e-11 and _rel(hf, hfc) < 1e-11
+
+
+def test_gdn_zero_beta_is_pure_decay():
+    """beta = 0: nothing is written, o_t = scale exp(G_t) q_t h0."""
+    rng = np.random.default_rng(51)
+    q, k, v, g, _, h0 = _gdn_rand(rng, 2, 2, 40, 6, 5)
+    beta = np.zeros(g.shape)
+    o, hf = oracle.gdn_recurrence(q, k, v, g, beta, h0, scale=0.7)
+    G = np.cumsum(g, axis=2)
+    ref = 0.7 * np.exp(G)[..., None] * np.einsum("bhtk,bhkv->bhtv", q, h0)
+    assert _rel(o, ref) < 1e-13
+    assert _rel(hf, np.exp(G[..., -1])[..., None, None] * h0) < 1e-13
+
+
+def test_gdn_orthonormal_keys_overwrite_rows():
+    """g = 0, beta = 1 and basis-vector keys: each write replaces one row of S
+    (an associative table), checked by replacing rows of a plain array."""
+    rng = np.random.default_rng(52)
+    T, K, V = 50, 6, 4
+    idx = rng.integers(0, K, T)
+    k = np.eye(K)[idx][None, None]
+    q = rng.standard_normal((1, 1, T, K))
+    v = rng.standard_normal((1, 1, T, V))
+    h0 = rng.standard_normal((1, 1, K, V))
+    o, hf = oracle.gdn_recurrence(q, k, v, np.zeros((1, 1, T)), np.ones((1, 1, T)), h0, scale=1.0)
+    table = h0[0, 0].copy()
+    for t in range(T):
+        table[idx[t]] = v[0, 0, t]
+        np.testing.assert_allclose(o[0, 0, t], q[0, 0, t] @ table, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hf[0, 0], table, rtol=0, atol=1e-13)
+
+
+def test_gdn_split_invariance():
+    rng = np.random.default_rng(53)
+    q, k, v, g, beta, h0 = _gdn_rand(rng, 1, 2, 90, 8, 8)
+    o, hf = oracle.gdn_recurrence(q, k, v, g, beta, h0, 0.5)
+    a = slice(0, 33)
+    b = slice(33, 90)
+    oa, ha = oracle.gdn_recurrence(q[:, :, a], k[:, :, a], v[:, :, a], g[:, :, a], beta[:, :, a], h0, 0.5)
+    ob, hb = oracle.gdn_recurrence(q[:, :, b], k[:, :, b], v[:, :, b], g[:, :, b], beta[:, :, b], ha, 0.5)
+    assert _rel(np.concatenate([oa, ob], axis=2), o) < 1e-13 and _rel(hb, hf) < 1e-13
+
+
+@pytest.mark.parametrize("mistake", ["read_before_decay", "no_beta_on_read", "output_before_write"])
+def test_gdn_pins_catch_planted_mistakes(mistake):
+    """Plausible slips in a Python copy of the update fail the golden fixture."""
+    c = _gdn_golden()
+    S = c["h0"][0, 0].copy()
+    outs = []
+    for t in range(c["q"].shape[2]):
+        a, b = np.exp(c["g"][0, 0, t]), c["beta"][0, 0, t]
+        kt, vt, qt = c["k"][0, 0, t], c["v"][0, 0, t], c["q"][0, 0, t]
+        if mistake == "read_before_decay":
+            r = b * (vt - kt @ S)
+            S = a * S + np.outer(kt, r)
+        else:
+            S = a * S
+            if mistake == "output_before_write":
+                outs.append(qt @ S)
+            r = (vt - kt @ S) if mistake == "no_beta_on_read" else b * (vt - kt @ S)
+            if mistake == "no_beta_on_read":
+                r = b * vt - kt @ S
+            S = S + np.outer(kt, r)
+        if mistake != "output_before_write":
+            outs.append(qt @ S)
+    assert not np.allclose(np.array(outs), c["o"][0, 0], atol=1e-12)
