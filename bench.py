@@ -75,8 +75,8 @@ DECODE_METRIC = "decode tokens/s, GLA decode step H=16 D=128 bf16 q/k/v/o, fp32 
 # D=128, B=1, T=16K: 2.17 ms) as tokens/s: another machine, context only.
 PAGES_TOKENS_PER_S = {"prefill_16k": 1 * 16384 / 2.17e-3, "prefill_4k": 1 * 4096 / 0.47e-3}
 KERNEL_SOURCES = [os.path.join(ROOT, "chunked_state_recurrence_amd", "csrc", f)
-                  for f in ("gla_kernels.hip", "gla_bwd.hip", "gla_api.hip", "gla_internal.h",
-                            "gla_device.h")]
+                  for f in ("gla_kernels.hip", "gla_bwd.hip", "gla_gdn.hip", "gla_api.hip",
+                            "gla_internal.h", "gla_device.h")]
 COPY_BYTES = 1 << 30
 
 

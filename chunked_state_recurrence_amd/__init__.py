@@ -1,9 +1,9 @@
 """MI355X-native chunked gated linear attention (GLA): prefill forward, backward
-and decode.
+and decode, and the gated delta rule forward.
 
 The computation lives in libgla.so (hand-written HIP kernels for gfx950 behind
-the C ABI in include/gla.h, include/gla_scalar.h, include/gla_bwd.h
-and include/gla_decode.h); this package is its thin Python binding.  Build
+the C ABI in include/gla.h, include/gla_scalar.h, include/gla_bwd.h,
+include/gla_gdn.h and include/gla_decode.h); this package is its thin Python binding.  Build
 the library with ``python -m chunked_state_recurrence_amd.build``.
 """
 
@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     GLAError,
     GLALibraryMissing,
     LIB_PATH,
+    gla_gdn_fwd,
     gla_bwd,
     gla_bwd_f32,
     gla_decode,

@@ -1,5 +1,5 @@
 """ctypes binding of libgla.so (include/gla.h, include/gla_scalar.h,
-include/gla_bwd.h, include/gla_decode.h, include/gla_stages.h).
+include/gla_bwd.h, include/gla_gdn.h, include/gla_decode.h, include/gla_stages.h).
 
 Argument marshalling only: shape/dtype/device checks, output allocation with
 torch, and the call.  Every step of the computation runs in the HIP kernels
@@ -27,9 +27,9 @@ ERRORS = {
 EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_version",
             "gla_release", "gla_profile_start", "gla_profile_stop", "gla_stage_cumsum",
             "gla_stage_intra", "gla_stage_states", "gla_decode", "gla_decode_f32",
-            "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32")
+            "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd")
 KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode", 5: "bwd_segment",
-                6: "bwd"}
+                6: "bwd", 7: "gdn"}
 
 
 class _KernelTime(ctypes.Structure):
@@ -65,6 +65,7 @@ def load_library(path: str = LIB_PATH):
     lib.gla_fwd_scalar.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_bwd.argtypes = [P] * 12 + [I, I, I, I, I, I, F, P]
     lib.gla_bwd_f32.argtypes = [P] * 12 + [I, I, I, I, I, I, F, P]
+    lib.gla_gdn_fwd.argtypes = [P] * 8 + [I, I, I, I, I, I, F, P]
     lib.gla_fwd_scalar_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_stage_states.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_stage_cumsum.argtypes = [P, P, P, I, I, I, I, I, P]
@@ -83,7 +84,7 @@ def load_library(path: str = LIB_PATH):
     lib.gla_profile_stop.restype = ctypes.c_int
     for name in ("gla_fwd", "gla_fwd_f32", "gla_stage_states", "gla_stage_cumsum",
                  "gla_stage_intra", "gla_set_tuning", "gla_version", "gla_decode", "gla_decode_f32",
-                 "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32"):
+                 "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -217,6 +218,32 @@ def gla_bwd_f32(q, k, v, g, h0, do, dh_final=None, *, chunk=0, scale=None, want_
     """fp32 backward: the same with fp32 q, k, v, do, dq, dk, dv."""
     return _bwd(load_library().gla_bwd_f32, torch.float32, q, k, v, g, h0, do, dh_final, chunk,
                 scale, want_dh0, out, stream)
+
+
+def gla_gdn_fwd(q, k, v, g, beta, h0=None, *, chunk=0, scale=None, want_final=False, o=None,
+            h_final=None, stream=None):
+    """Gated delta rule forward: q, k, v bf16 [B,H,T,D]; g, beta fp32 [B,H,T];
+    h0 fp32 [B,H,D,D] or None.  Returns (o bf16, h_final fp32 or None)."""
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    for t, n, dt, shp in ((q, "q", torch.bfloat16, (B, H, T, K)), (k, "k", torch.bfloat16, (B, H, T, K)),
+                          (v, "v", torch.bfloat16, (B, H, T, V)), (g, "g", torch.float32, (B, H, T)),
+                          (beta, "beta", torch.float32, (B, H, T)),
+                          (h0, "h0", torch.float32, (B, H, K, V))):
+        _need(t, n, dt, shp, dev)
+    if scale is None:
+        scale = K ** -0.5
+    if o is None:
+        o = torch.empty((B, H, T, V), dtype=torch.bfloat16, device=dev)
+    _need(o, "o", torch.bfloat16, (B, H, T, V), dev)
+    if want_final and h_final is None:
+        h_final = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+    _need(h_final, "h_final", torch.float32, (B, H, K, V), dev)
+    _check(load_library().gla_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o),
+                                  _ptr(h_final), B, H, T, K, V, int(chunk), float(scale),
+                                  _stream(stream)))
+    return o, h_final
 
 
 def _decode(fn, io_dtype, q, k, v, g, state, scale, o, stream):

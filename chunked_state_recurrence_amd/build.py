@@ -2,7 +2,8 @@
 
     python -m chunked_state_recurrence_amd.build
 
-Compiles ``csrc/gla_kernels.hip``, ``csrc/gla_bwd.hip`` and ``csrc/gla_api.hip`` with hipcc into
+Compiles ``csrc/gla_kernels.hip``, ``csrc/gla_bwd.hip``, ``csrc/gla_gdn.hip`` and
+``csrc/gla_api.hip`` with hipcc into
 ``chunked_state_recurrence_amd/libgla.so``.  Packed fp32 VALU instructions
 are disabled for the device code.
 """
@@ -19,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgla.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("gla_kernels.hip", "gla_bwd.hip", "gla_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("gla_kernels.hip", "gla_bwd.hip", "gla_gdn.hip", "gla_api.hip")]
 ARCH = "gfx950"
 
 

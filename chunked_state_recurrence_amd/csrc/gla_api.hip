@@ -1,7 +1,7 @@
 // gla_api.hip — C ABI of libgla.so: argument validation, segment scheduling,
 // workspace, launches.  Declarations and contracts: include/gla.h,
-// include/gla_scalar.h, include/gla_bwd.h, include/gla_decode.h and
-// include/gla_stages.h.
+// include/gla_scalar.h, include/gla_bwd.h, include/gla_gdn.h,
+// include/gla_decode.h and include/gla_stages.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -13,6 +13,7 @@
 #include "gla.h"
 #include "gla_bwd.h"
 #include "gla_decode.h"
+#include "gla_gdn.h"
 #include "gla_scalar.h"
 #include "gla_stages.h"
 #include "gla_internal.h"
@@ -410,6 +411,42 @@ int gla_fwd_scalar_f32(const float *q, const float *k, const float *v, const flo
     Call c{gla::DTYPE_F32, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
            static_cast<hipStream_t>(stream), true};
     return run_forward(c);
+}
+
+// Gated delta rule forward (include/gla_gdn.h).
+int gla_gdn_fwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g, const float *beta,
+            const float *h0, gla_bf16 *o, float *h_final, int B, int H, int T, int K, int V, int chunk,
+            float scale, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (B <= 0 || H <= 0 || T < 0 || K <= 0 || V <= 0) return GLA_ERR_SHAPE;
+    if (long(B) * H > (1L << 30) || long(T) * K >= (1L << 29)) return GLA_ERR_SHAPE;
+    if (K != V || (K != 64 && K != 128) || (chunk != 0 && chunk != 64)) return GLA_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GLA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, h0, o, h_final};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return GLA_ERR_ALIGN;
+    const size_t bh = size_t(B) * H, bht = bh * T;
+    const size_t nx = bht * K * 2, ns = bht * 4, nst = bh * K * V * 4;
+    struct R { const void *p; size_t n; } ins[] = {{q, nx}, {k, nx}, {v, nx}, {g, ns}, {beta, ns}, {h0, nst}};
+    for (const R &r : ins) {
+        if (overlaps(o, nx, r.p, r.n)) return GLA_ERR_ALIAS;
+        if (overlaps(h_final, nst, r.p, r.n)) return GLA_ERR_ALIAS;
+    }
+    if (overlaps(h_final, nst, o, nx)) return GLA_ERR_ALIAS;
+    DeviceState *dev = nullptr;
+    int rc = current_device(&dev);
+    if (rc != GLA_OK) return rc;
+    if (T == 0) {
+        if (h_final && traced(GLA_KERNEL_OTHER, s, [&] {
+                return gla::launch_copy_state(h_final, h0, long(bh) * K * V, s);
+            }) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+        return GLA_OK;
+    }
+    gla::GdnParams p{q, k, v, g, beta, h0, o, h_final, T, scale};
+    if (traced(GLA_KERNEL_GDN, s, [&] { return gla::launch_gdn(K, p, long(bh), s); }) != hipSuccess)
+        return GLA_ERR_LAUNCH;
+    return GLA_OK;
 }
 
 // One decode step (include/gla_decode.h).

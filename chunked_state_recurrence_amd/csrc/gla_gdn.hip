@@ -1,0 +1,417 @@
+// gla_gdn.hip — gfx950 kernel for the gated delta rule (Gated DeltaNet
+// forward), chunk form.
+//
+// Recurrence (per batch row and head; scalar gate and write strength per
+// token): S_t = exp(g_t) (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t,
+// o_t = scale q_t S_t.  The evaluation page "面向长序列大模型的线性注意力算子
+// 性能评测方法与优化实践" (sections 一 and 三.3) describes the GDN class as
+// gating plus an incremental state update without a formula; this is the
+// published gated delta rule.
+//
+// Chunk form (rows i, j of a chunk; gamma_i = exp of the chunk-local
+// inclusive cumsum of g; S the chunk-start state).  The rows written into the
+// state, u_i = beta_i (v_i - exp(g_i) k_i S_{i-1}), satisfy
+//     (I + A) U = diag(beta) V - diag(beta gamma) K S,
+//     A_ij = beta_i (gamma_i / gamma_j) (k_i . k_j)        (j < i),
+// so with T = (I + A)^{-1}:  U = T diag(beta) V - W S,  W = T diag(beta) (gamma K),
+//     o_i    = scale [ gamma_i q_i S + sum_{j<=i} (gamma_i / gamma_j) (q_i . k_j) u_j ]
+//     S_next = gamma_C S + sum_j (gamma_C / gamma_j) k_j^T u_j.
+// Every factor is at most 1 (gamma_i / gamma_j with j <= i), so extreme gates
+// need no special path.  T is formed by blocks: the 16 x 16 diagonal blocks
+// by forward substitution (one lane per column), the others level by level,
+// T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ, with fp32 MFMA.
+//
+// One work-group per (batch, head) walks the chunks in order; S stays in MFMA
+// accumulators (wave w owns value columns [w D/NW, (w+1) D/NW)), and is fed to
+// the S products straight from them (the row operand's columns are permuted
+// in LDS, as in the forward output pass).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gla_device.h"
+#include "gla_internal.h"
+
+namespace gla {
+
+template <int D, int C> struct GdnLayout {
+    static constexpr int QP = D + 8;                 // permuted-row tiles, bf16 elements per row
+    static constexpr int PD = 2 * D + 32;            // bank-spread bf16 tiles, bytes per row
+    static constexpr int PC = 2 * C + 32;            // bank-spread bf16 C x C tiles
+    static constexpr int PF = C + 4;                 // fp32 C x C tiles, floats per row
+    static constexpr int TD = BF16::tile_bytes(C, PD);
+    static constexpr int TQ = C * QP * 2;
+    static constexpr int R = TD > TQ ? TD : TQ;      // a region holding either layout
+    // kr: raw k rows, later -W (permuted);  qr: raw q rows, later U (bank-spread);
+    // kg: gamma k, later (gamma_C / gamma) k
+    static constexpr int kr = 0, qr = kr + R, kg = qr + R, qh = kg + TD, vv = qh + TQ;
+    static constexpr int pp = vv + TD;                          // P (bf16, rows i, columns j <= i)
+    static constexpr int tb = pp + BF16::tile_bytes(C, PC);     // T diag(beta) (bf16)
+    static constexpr int aa = tb + BF16::tile_bytes(C, PC);     // A (fp32)
+    static constexpr int tt = aa + C * PF * 4;                  // T (fp32)
+    static constexpr int bytes = tt + C * PF * 4;
+};
+
+// 16 x 16 x 16 fp32 product from LDS blocks (row-major, `pa` / `pb` floats per
+// row): acc[e] += sum_m A[4 q4 + e][m] B[m][n16]... with the operands supplied
+// as v_mfma_f32_16x16x4f32 takes them (lane (n16, q4) gives A[n16][4i + q4]
+// and B[4i + q4][n16] in step i).
+__device__ __forceinline__ f32x4_t mma16_f32(const float *A, int pa, const float *B, int pb,
+                                             int n16, int q4, f32x4_t acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[n16 * pa + 4 * i + q4], B[(4 * i + q4) * pb + n16],
+                                                   acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ void wave_lds_fence() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int D, int C>
+__global__ void __launch_bounds__((Shape<D, C>::NW * 64))
+gdn_kernel(const GdnParams p) {
+    using E = BF16;
+    using L = GdnLayout<D, C>;
+    using frag_t = E::frag_t;
+    constexpr int NW = Shape<D, C>::NW;
+    constexpr int RPW = Shape<D, C>::RPW;
+    constexpr int NB = C / 16;
+    constexpr int CPL = D / 64;
+    constexpr int VS = D / NW;
+    constexpr int NTW = VS / 16;
+    constexpr int MT = D / 16;
+    constexpr int KS = D / 32;
+    constexpr int TS = C / 32;
+    constexpr int NTILE = NB * (NB + 1) / 2;
+    static_assert(C == 64 && NB == 4, "the blocked inverse is written for 64-row chunks");
+    static_assert(L::bytes + 2 * C * 4 <= 163840, "LDS");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
+    __shared__ float sGc[C];     // chunk-local inclusive cumsum of g, log2 units
+    __shared__ float sBeta[C];
+    unsigned char *tKr = smem + L::kr;   // raw k, row-major (then -W, permuted)
+    unsigned char *tQr = smem + L::qr;   // raw q, row-major (then U, bank-spread)
+    unsigned char *tKg = smem + L::kg;   // gamma k, then (gamma_C / gamma) k
+    __bf16 *tQh = reinterpret_cast<__bf16 *>(smem + L::qh);   // scale gamma q, permuted columns
+    unsigned char *tV = smem + L::vv;
+    unsigned char *tP = smem + L::pp;
+    unsigned char *tTb = smem + L::tb;
+    float *tA = reinterpret_cast<float *>(smem + L::aa);
+    float *tT = reinterpret_cast<float *>(smem + L::tt);
+    __bf16 *tW = reinterpret_cast<__bf16 *>(tKr);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int n16 = lane & 15;
+    const int q4 = lane >> 4;
+    const long bh = blockIdx.x;
+    const int T = p.T;
+    const int N = (T + C - 1) / C;
+    const int vb = w * VS;
+    const int r0 = RPW * w;
+
+    const rsrc_t bq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + bh * long(T) * D, long(T) * D * 2);
+    const rsrc_t bk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + bh * long(T) * D, long(T) * D * 2);
+    const rsrc_t bv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + bh * long(T) * D, long(T) * D * 2);
+    const rsrc_t bo = make_rsrc(reinterpret_cast<uint16_t *>(p.o) + bh * long(T) * D, long(T) * D * 2);
+    const rsrc_t bg = make_rsrc(p.g + bh * long(T), long(T) * 4);
+    const rsrc_t bb = make_rsrc(p.beta + bh * long(T), long(T) * 4);
+
+    auto rowp = [&](unsigned char *tile, int r, int pitch) {
+        return reinterpret_cast<__bf16 *>(tile + E::rowoff(r, pitch));
+    };
+
+    // ---- state ---------------------------------------------------------------
+    f32x4_t S[MT][NTW];
+    {
+        const float *src = p.h0 ? p.h0 + bh * long(D) * D : nullptr;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S[mt][nt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] : 0.f;
+    }
+    // entries above the diagonal of P and T diag(beta) are never written
+    for (int i = tid; i < 2 * E::tile_bytes(C, L::PC) / 4; i += NW * 64) reinterpret_cast<uint32_t *>(tP)[i] = 0u;
+
+    for (int c = 0; c < N; ++c) {
+        const int t0 = c * C;
+        // ---- rows of the chunk: q, k into registers, v into LDS, gates ----------
+        Raw<E, CPL> rq[RPW], rk[RPW];
+        {
+            const int eoff = (t0 + r0) * D + lane * CPL;
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                rq[i].load(bq, eoff * 2, i * D * 2);
+                rk[i].load(bk, eoff * 2, i * D * 2);
+            }
+            const int row0 = __builtin_amdgcn_readfirstlane(t0 + r0);
+            const int lr0 = __builtin_amdgcn_readfirstlane(r0);
+            mem_fence_compiler();
+#pragma unroll
+            for (int i = 0; i < RPW; ++i)   // 4 bytes per lane: a 64-wide row takes lanes 0..31
+                if (CPL == 2 || lane < 32) dma<4>(bv, tV + E::rowoff(lr0 + i, L::PD), lane * 4, (row0 + i) * D * 2);
+            mem_fence_compiler();
+            if (w == 0) {   // gates (log2) scanned over the chunk, one row per lane
+                float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bg, (t0 + lane) * 4, 0, 0)) * kLog2e;
+                const float bt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bb, (t0 + lane) * 4, 0, 0));
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float y = __shfl_up(x, off, 64);
+                    if (lane >= off) x += y;
+                }
+                sGc[lane] = x;
+                sBeta[lane] = bt;
+            }
+            wait_vmem<0>();
+        }
+        block_sync();  // B1: gates, v rows
+
+        // ---- operand rows ----------------------------------------------------------
+        const float gcl = sGc[C - 1];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int r = r0 + i;
+            const float gr = sGc[r];
+            const float gam = fexp2(gr);
+#pragma unroll
+            for (int u = 0; u < CPL; ++u) {
+                const int col = lane * CPL + u;
+                const float qv = rq[i].get(u), kv = rk[i].get(u);
+                reinterpret_cast<__bf16 *>(tKr)[r * L::QP + col] = (__bf16)kv;
+                reinterpret_cast<__bf16 *>(tQr)[r * L::QP + col] = (__bf16)qv;
+                rowp(tKg, r, L::PD)[col] = (__bf16)(kv * gam);
+                tQh[r * L::QP + perm_col(col)] = (__bf16)(qv * gam * p.scale);
+            }
+        }
+        block_sync();  // B2: operand tiles
+
+        // ---- A = beta_i (gamma_i / gamma_j) (k_i . k_j) (j < i, fp32) and
+        //      P = (gamma_i / gamma_j) (q_i . k_j) (j <= i, bf16), causal tiles ----------
+        const __bf16 *kraw = reinterpret_cast<const __bf16 *>(tKr);
+        const __bf16 *qraw = reinterpret_cast<const __bf16 *>(tQr);
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+            if (t % NW != w) continue;
+            int I = 0, J = t;
+#pragma unroll
+            for (int r = 0; r < NB; ++r)
+                if (J > r) { J -= r + 1; I = r + 1; }
+            f32x4_t kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int pos = ks * 32 + 8 * q4;
+                const frag_t kj = E::ld_frag(kraw + (16 * J + n16) * L::QP + pos);
+                kk = E::mma(kj, E::ld_frag(kraw + (16 * I + n16) * L::QP + pos), kk);
+                qk = E::mma(kj, E::ld_frag(qraw + (16 * I + n16) * L::QP + pos), qk);
+            }
+            // acc[e] = (. . k_j)[i = 16I + n16][j = 16J + 4q4 + e]
+            const int i = 16 * I + n16;
+            const float gi = sGc[i], bi = sBeta[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * J + 4 * q4 + e;
+                const float ratio = j <= i ? fexp2(gi - sGc[j]) : 0.f;
+                tA[i * L::PF + j] = j < i ? bi * ratio * kk[e] : 0.f;
+                rowp(tP, i, L::PC)[j] = (__bf16)(p.scale * ratio * qk[e]);
+            }
+        }
+        block_sync();  // B3: A, P
+
+        // ---- T = (I + A)^{-1}: diagonal blocks by substitution (wave 0, one lane
+        //      per column of each of the four blocks) ---------------------------------
+        if (w == 0) {
+            const int blk = lane >> 4, col = lane & 15;
+            float tcol[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x = i == col ? 1.f : 0.f;
+#pragma unroll
+                for (int j = 0; j < i; ++j) x -= tA[(16 * blk + i) * L::PF + 16 * blk + j] * tcol[j];
+                tcol[i] = x;
+            }
+            const float bc = sBeta[16 * blk + col];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                tT[(16 * blk + i) * L::PF + 16 * blk + col] = tcol[i];
+                rowp(tTb, 16 * blk + i, L::PC)[16 * blk + col] = (__bf16)(tcol[i] * bc);
+            }
+        }
+        block_sync();  // B4: diagonal blocks of T
+        // off-diagonal blocks, by distance from the diagonal: wave J makes T_{J+d, J}
+#pragma unroll
+        for (int d = 1; d < NB; ++d) {
+            if (w < NB - d) {
+                const int J = w, I = J + d;
+                f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+                for (int Kb = J; Kb < I; ++Kb)
+                    x = mma16_f32(tA + (16 * I) * L::PF + 16 * Kb, L::PF, tT + (16 * Kb) * L::PF + 16 * J, L::PF,
+                                  n16, q4, x);
+                // x[e] = X[4q4 + e][n16]; park X in T's (I, J) block, then T_IJ = -T_II X
+                float *blkIJ = tT + (16 * I) * L::PF + 16 * J;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) blkIJ[(4 * q4 + e) * L::PF + n16] = x[e];
+                wave_lds_fence();
+                f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+                float av[4], bv4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    av[i] = tT[(16 * I + n16) * L::PF + 16 * I + 4 * i + q4];
+                    bv4[i] = blkIJ[(4 * i + q4) * L::PF + n16];
+                }
+                wave_lds_fence();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv4[i], y, 0, 0, 0);
+                const float bc = sBeta[16 * J + n16];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    blkIJ[(4 * q4 + e) * L::PF + n16] = -y[e];
+                    rowp(tTb, 16 * I + 4 * q4 + e, L::PC)[16 * J + n16] = (__bf16)(-y[e] * bc);
+                }
+            }
+            block_sync();  // B5..B7: one level of T
+        }
+
+        // ---- W = T diag(beta) (gamma K) and U~ = T diag(beta) V for this wave's
+        //      columns; acc[e] = X[row 16m + n16][col + 4q4 + e] -------------------------
+        f32x4_t Wa[NTW][NB], Ua[NTW][NB];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                Wa[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                Ua[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const frag_t kf = E::ld_col8(tKg, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16);
+                const frag_t vf = E::ld_col8(tV, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16);
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    if (ts * 32 > 16 * m + 15) continue;   // T is lower triangular
+                    const frag_t tf = E::ld_frag(rowp(tTb, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
+                    Wa[nt][m] = E::mma(kf, tf, Wa[nt][m]);
+                    Ua[nt][m] = E::mma(vf, tf, Ua[nt][m]);
+                }
+            }
+        block_sync();  // B8: gamma k no longer read
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    tW[(16 * m + n16) * L::QP + perm_col(vb + 16 * nt + 4 * q4 + e)] = (__bf16)(-Wa[nt][m][e]);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {   // (gamma_C / gamma) k over gamma k
+            const int r = r0 + i;
+            const float gk = fexp2(gcl - sGc[r]);
+#pragma unroll
+            for (int u = 0; u < CPL; ++u) rowp(tKg, r, L::PD)[lane * CPL + u] = (__bf16)(rk[i].get(u) * gk);
+        }
+        block_sync();  // B9: -W and the state-update rows visible
+
+        // ---- U = U~ - W S and O = (scale gamma q) S, S straight from its accumulators ----
+        f32x4_t O[NTW][NB];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int m = 0; m < NB; ++m) O[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            frag_t sf[NTW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { x[e] = S[2 * ks][nt][e]; x[4 + e] = S[2 * ks + 1][nt][e]; }
+                sf[nt] = E::pack(x);
+            }
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                const frag_t wf = E::ld_frag(tW + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
+                const frag_t qf = E::ld_frag(tQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    Ua[nt][m] = E::mma(sf[nt], wf, Ua[nt][m]);
+                    O[nt][m] = E::mma(sf[nt], qf, O[nt][m]);
+                }
+            }
+        }
+        // U rows into the (former raw q) region, bank-spread layout
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                __bf16 *dst = rowp(tQr, 16 * m + n16, L::PD) + vb + 16 * nt + 4 * q4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[e] = (__bf16)Ua[nt][m][e];
+            }
+        block_sync();  // B10: U visible
+
+        // ---- O += P U; o rows to HBM ---------------------------------------------------
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int ts = 0; ts < TS; ++ts) {
+                if (ts * 32 > 16 * m + 15) continue;
+                const frag_t pf = E::ld_frag(rowp(tP, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    O[nt][m] = E::mma(E::ld_col8(tQr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), pf, O[nt][m]);
+            }
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                E::st4(bo, ((t0 + 16 * m + n16) * D + vb + 16 * nt + 4 * q4) * 2, O[nt][m]);
+            }
+
+        // ---- S <- gamma_C S + ((gamma_C / gamma) k)^T U ------------------------------------
+        const float gC = fexp2(gcl);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[mt][nt][e] *= gC;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ts = 0; ts < TS; ++ts) {
+                const frag_t a = E::ld_col8(tKg, L::PD, ts * 32 + 8 * q4, 16 * mt, n16);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    S[mt][nt] = E::mma(a, E::ld_col8(tQr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), S[mt][nt]);
+            }
+        block_sync();  // B11: tiles free for the next chunk
+    }
+
+    if (p.h_final) {
+        float *dst = p.h_final + bh * long(D) * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
+    }
+}
+
+hipError_t launch_gdn(int D, const GdnParams &p, long nbh, hipStream_t s) {
+    if (nbh <= 0) return hipSuccess;
+    if (D == 128)
+        hipLaunchKernelGGL((gdn_kernel<128, 64>), dim3(unsigned(nbh)), dim3(Shape<128, 64>::NW * 64), 0, s, p);
+    else if (D == 64)
+        hipLaunchKernelGGL((gdn_kernel<64, 64>), dim3(unsigned(nbh)), dim3(Shape<64, 64>::NW * 64), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace gla

@@ -49,6 +49,18 @@ struct BwdParams {
     float scale;
 };
 
+// gated delta rule (gla_gdn.hip): one work-group per (batch, head)
+struct GdnParams {
+    const void *q, *k, *v;     // bf16 [heads][T][D]
+    const float *g, *beta;     // [heads][T]
+    const float *h0;           // [heads][D][D] or null
+    void *o;                   // bf16 [heads][T][D]
+    float *h_final;            // [heads][D][D] or null
+    int T;
+    float scale;
+};
+hipError_t launch_gdn(int D, const GdnParams &p, long nbh, hipStream_t s);
+
 bool chunk_supported(int dtype, int D, int C);
 // work-groups of the state pass that fit on one CU (LDS bound), 1 or 2
 int state_units_per_cu(int dtype, int D, int C);

@@ -30,6 +30,12 @@ Backward inputs (make_grad_inputs): the loss gradients do ~ N(0, 1) (in the
 workload's dtype) and dh_final ~ N(0, 0.1) (fp32), from a generator of their
 own seeded with the workload seed + 1000.
 
+Gated delta rule workloads (GDN_WORKLOADS, make_gdn_inputs): q and k
+L2-normalised per token (the delta rule's convention), v ~ N(0, 1), all
+three rounded to bf16; g = logsigmoid(N(0, 1)) / 16 and beta = sigmoid(N(0,
+1)), fp32, one per token and head; h0 ~ N(0, std) when asked.  Draw order
+q, k, v, g normal, beta normal, h0, from one generator per call.
+
 Decode workloads (DECODE_WORKLOADS) draw the same way with T = 1: one new
 token per (batch, head) and a carried fp32 state drawn as h0.  The pages do
 not measure decode; the batch is sized so that the state of one step
@@ -88,6 +94,13 @@ SCALAR_WORKLOADS = {
                                    None, True, None, 6, scalar_gate=True),
 }
 
+# Gated delta rule: 16 sequences x 16 heads of 4K tokens (one work-group per
+# sequence-head fills the GPU), and a long single sequence.
+GDN_WORKLOADS = {
+    "gdn_b16_4k": Workload("gdn_b16_4k", 16, 16, 4096, 128, "bf16", "l2", "ls16", None, True, 64, 7),
+    "gdn_16k": Workload("gdn_16k", 1, 16, 16384, 128, "bf16", "l2", "ls16", None, True, 64, 8),
+}
+
 # Decode: B sequences x H heads each take one step against a carried state.
 DECODE_WORKLOADS = {
     "decode_b256": Workload("decode_b256", 256, 16, 1, 128, "bf16", "l2", "ls16", 0.05, True, None, 5),
@@ -143,6 +156,36 @@ def make_inputs(wl: Workload, *, B=None, H=None, T=None, gate=None, seed=None,
         q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
     return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(),
             "g": g.float().contiguous(), "h0": None if h0 is None else h0.contiguous()}
+
+
+def make_gdn_inputs(wl: Workload, *, B=None, H=None, T=None, gate=None, seed=None,
+                    h0_std="default", beta=None):
+    """Draw (q, k, v, g, beta, h0) for the gated delta rule on workload ``wl``.
+    ``gate`` overrides g as for make_inputs; ``beta`` may fix beta to a constant."""
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    T = wl.T if T is None else T
+    D = wl.D
+    gate = wl.gate if gate is None else gate
+    seed = wl.seed if seed is None else seed
+    std = wl.h0_std if h0_std == "default" else h0_std
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    shape = (B, H, T, D)
+    q = F.normalize(torch.randn(shape, generator=gen), dim=-1, eps=1e-6)
+    k = F.normalize(torch.randn(shape, generator=gen), dim=-1, eps=1e-6)
+    v = torch.randn(shape, generator=gen)
+    g = _gate(gate, (B, H, T), gen)
+    b = torch.sigmoid(torch.randn((B, H, T), generator=gen))
+    if beta is not None:
+        b = torch.full((B, H, T), float(beta))
+    h0 = None
+    if std is not None:
+        h0 = torch.randn((B, H, D, D), generator=gen) * std
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(),
+            "g": g.float().contiguous(), "beta": b.float().contiguous(),
+            "h0": None if h0 is None else h0.contiguous()}
 
 
 def make_grad_inputs(wl: Workload, *, B=None, H=None, T=None, seed=None, dh_final=True):

@@ -141,6 +141,26 @@ def test_backward_argument_errors(fn, kw, code):
     assert _bwd(lib, fn, **kw) == code
 
 
+def _gdn(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + STEP, v=FAKE + 2 * STEP, g=FAKE + 3 * STEP, beta=FAKE + 4 * STEP,
+             h0=None, o=FAKE + 5 * STEP, hf=None, B=1, H=2, T=100, K=128, V=128, chunk=0, scale=0.1)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.gla_gdn_fwd(*(vp(a[n]) for n in ("q", "k", "v", "g", "beta", "h0", "o", "hf")),
+                       a["B"], a["H"], a["T"], a["K"], a["V"], a["chunk"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(T=-1), -2), (dict(K=128, V=64), -3), (dict(K=96, V=96), -3),
+    (dict(chunk=32), -3), (dict(beta=None), -1), (dict(g=None), -1), (dict(o=None), -1),
+    (dict(q=FAKE + 8), -4), (dict(o=FAKE + 64), -7), (dict(o=FAKE + 4 * STEP + 256), -7),
+    (dict(hf=FAKE + 5 * STEP + 512), -7),
+])
+def test_gdn_argument_errors(kw, code):
+    lib = gla.load_library()
+    assert _gdn(lib, **kw) == code
+
+
 def test_fp32_chunk_support_table():
     lib = gla.load_library()
     vp = ctypes.c_void_p
