@@ -33,6 +33,13 @@ chunk pass against HBM bandwidth with its algorithmic bytes (bf16 q, k, v,
 do read and dq, dk, dv written, fp32 g read and dg written, and the fp32
 chunk-start state read once per chunk).
 
+Gated delta rule (a separate line, not the headline):
+    python bench.py --workload gdn_b16_4k
+A step is one gla_gdn_fwd call over the workload; ``value`` is B*T / step
+time; ``roofline`` prices the kernel against HBM bandwidth with its
+algorithmic bytes (bf16 q, k, v, o and fp32 g, beta per token-head, plus the
+fp32 final state) and also reports its bf16 MFMA rate.
+
 Decode (a separate line, not the headline):
     python bench.py --workload decode_b256 [--steps K] [--warmup W]
 A step is one gla_decode call: one token for each of B sequences x H heads
@@ -70,6 +77,7 @@ METRIC = "prefill tokens/s, chunk GLA fwd H=16 D=128 bf16; % MFMA peak / HBM BW"
 SCALAR_METRIC = "prefill tokens/s, chunk scalar-gate linear attention fwd H=16 D=128 bf16; % HBM BW"
 BWD_METRIC = ("backward tokens/s, chunk GLA bwd H=16 D=128 bf16 (forward states recomputed); "
               "% HBM BW")
+GDN_METRIC = "prefill tokens/s, chunk gated delta rule fwd H=16 D=128 bf16; % HBM BW"
 DECODE_METRIC = "decode tokens/s, GLA decode step H=16 D=128 bf16 q/k/v/o, fp32 state; % HBM BW"
 # The pages' number for this workload (FLA chunk_gla, RTX 4090, bf16, H=16,
 # D=128, B=1, T=16K: 2.17 ms) as tokens/s: another machine, context only.
@@ -100,6 +108,19 @@ def backward_bytes(wl, chunk: int) -> int:
     es = 2 if wl.dtype == "bf16" else 4
     n_chunks = wl.B * wl.H * ((wl.T + chunk - 1) // chunk)
     return th * wl.D * (7 * es + 8) + n_chunks * wl.D * wl.D * 4
+
+
+def gdn_bytes(wl) -> int:
+    """Per token-head: bf16 q, k, v, o (2 B each) and fp32 g, beta; plus the
+    fp32 final state per head."""
+    return wl.B * wl.H * (wl.T * (wl.D * 8 + 8) + wl.D * wl.D * 4)
+
+
+def gdn_flops(wl, chunk: int = 64) -> int:
+    """Matrix products per token-head of the chunk form: k k^T, q k^T, W and
+    U~ (chunk-deep), W S, q S and the state update (D-deep), P U."""
+    th = wl.B * wl.H * wl.T
+    return th * (2 * chunk * wl.D * 5 + 2 * wl.D * wl.D * 3)
 
 
 def decode_bytes(wl) -> int:
@@ -305,6 +326,111 @@ def cpu_baseline_backward(wl, x, gr, min_s: float = 10.0):
             "seconds": round(sum(times), 3)}
 
 
+def cpu_baseline_gdn(wl, x, min_s: float = 10.0):
+    """The fp64 gated-delta-rule oracle on the host over whole heads (as many
+    as there are threads), repeated until min_s has passed; scaled to all heads."""
+    import numpy as np
+    import oracle
+    from chunked_state_recurrence_amd.workloads import to_f64_numpy
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)][:threads]
+    f = {n: (None if x[n] is None else np.stack([to_f64_numpy(x[n][b, h]) for (b, h) in pairs])[None])
+         for n in ("q", "k", "v", "g", "beta", "h0")}
+    times = []
+    while sum(times) < min_s:
+        t0 = time.perf_counter()
+        oracle.gdn_recurrence(f["q"], f["k"], f["v"], f["g"], f["beta"], f["h0"], wl.scale,
+                              threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.mean(times) * wl.B * wl.H / len(pairs)
+    return {"value": wl.B * wl.T / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pairs)} of {wl.B * wl.H} (batch, head) sequences, full T={wl.T}, fp64 "
+                      f"token recurrence, {len(times)} passes of {statistics.mean(times):.2f} s; "
+                      "scaled to all heads",
+            "seconds": round(sum(times), 3)}
+
+
+def bench_gdn(args, wl):
+    import torch
+
+    import chunked_state_recurrence_amd as gla
+    from chunked_state_recurrence_amd.workloads import make_gdn_inputs
+
+    dev = torch.device("cuda:0")
+    host = make_gdn_inputs(wl)
+    sets = []
+    for s in range(2):   # two independent input sets alternate
+        d = {n: (None if host[n] is None else host[n].to(dev))
+             for n in ("q", "k", "v", "g", "beta", "h0")}
+        if s == 1:
+            d = {n: (None if t is None else t.clone()) for n, t in d.items()}
+        d["o"] = torch.empty(wl.B, wl.H, wl.T, wl.D, dtype=torch.bfloat16, device=dev)
+        d["hf"] = torch.empty(wl.B, wl.H, wl.D, wl.D, dtype=torch.float32, device=dev)
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        d = sets[i & 1]
+        gla.gla_gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], scale=wl.scale,
+                        o=d["o"], h_final=d["hf"], want_final=True, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    gla.profile_start(args.steps + 8)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kms = [t for kind, t in gla.profile_stop() if kind == "gdn"]
+    if args.copy_calibration:
+        copy_calibration(dev)
+    k_ms = statistics.mean(kms)
+    per_launch = gdn_bytes(wl)
+    achieved = per_launch / (k_ms * 1e-3) / 1e9
+    flops = gdn_flops(wl)
+    traffic = None
+    c = read_counters(wl.name)
+    if c and "fetch_factor" in c:
+        m = c["median_per_dispatch_KiB"]
+        f, w = m.get("gdn:FETCH_SIZE"), m.get("gdn:WRITE_SIZE")
+        if f is not None and w is not None:
+            traffic = int(f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"])
+    res = {
+        "metric": GDN_METRIC,
+        "value": wl.B * wl.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.D, "V": wl.D,
+                   "chunk": 64, "h_final": True, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gdn_kernel<128,64>", "kernel_ms": k_ms,
+                     "algorithmic_bytes_per_launch": per_launch,
+                     "mfma_tflops": flops / (k_ms * 1e-3) / 1e12,
+                     "mfma_frac": flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_gdn(wl, host)
+    print(json.dumps(res), flush=True)
+
+
 def bench_backward(args, wl):
     import torch
 
@@ -419,7 +545,7 @@ def summarize_counters(outdir: str, wl_name: str):
         last_chunk = max((int(r["Dispatch_Id"]) for r in rows
                           if any(s in r["Kernel_Name"]
                                  for s in ("chunk_kernel", "state_kernel", "decode_kernel",
-                                           "bwd_kernel"))),
+                                           "bwd_kernel", "gdn_kernel"))),
                          default=-1)
         for r in rows:
             name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
@@ -431,6 +557,8 @@ def summarize_counters(outdir: str, wl_name: str):
                 kind = "scan"
             elif "decode_kernel" in name:
                 kind = "decode"
+            elif "gdn_kernel" in name:
+                kind = "gdn"
             elif "bwd_kernel" in name:
                 kind = "bwd" if name.split(",")[3].strip(" >)(")[:1] == "1" else "bwd_segment"
             elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_chunk:
@@ -482,11 +610,14 @@ def main():
     import torch
 
     import chunked_state_recurrence_amd as gla
-    from chunked_state_recurrence_amd.workloads import (DECODE_WORKLOADS, SCALAR_WORKLOADS,
-                                                        WORKLOADS, make_inputs)
+    from chunked_state_recurrence_amd.workloads import (DECODE_WORKLOADS, GDN_WORKLOADS,
+                                                        SCALAR_WORKLOADS, WORKLOADS, make_inputs)
 
     if args.workload in DECODE_WORKLOADS:
         bench_decode(args, DECODE_WORKLOADS[args.workload])
+        return
+    if args.workload in GDN_WORKLOADS:
+        bench_gdn(args, GDN_WORKLOADS[args.workload])
         return
     wl = {**WORKLOADS, **SCALAR_WORKLOADS}[args.workload]
     if args.backward:
