@@ -443,7 +443,15 @@ int gla_gdn_fwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const f
             return GLA_ERR_LAUNCH;
         return GLA_OK;
     }
-    gla::GdnParams p{q, k, v, g, beta, h0, o, h_final, T, scale};
+    // split value columns over work-groups while batch x heads leaves CUs idle
+    int nvb = 1;
+    {
+        int target;
+        std::lock_guard<std::mutex> lk(g_mu);
+        target = g_target_wgs;
+        while (nvb < K / 16 && long(bh) * nvb * 2 <= target) nvb *= 2;
+    }
+    gla::GdnParams p{q, k, v, g, beta, h0, o, h_final, T, scale, nvb};
     if (traced(GLA_KERNEL_GDN, s, [&] { return gla::launch_gdn(K, p, long(bh), s); }) != hipSuccess)
         return GLA_ERR_LAUNCH;
     return GLA_OK;

@@ -21,10 +21,14 @@
 // by forward substitution (one lane per column), the others level by level,
 // T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ, with fp32 MFMA.
 //
-// One work-group per (batch, head) walks the chunks in order; S stays in MFMA
-// accumulators (wave w owns value columns [w D/NW, (w+1) D/NW)), and is fed to
-// the S products straight from them (the row operand's columns are permuted
-// in LDS, as in the forward output pass).
+// One work-group per (batch, head, block of value columns) walks the chunks
+// in order.  Value columns of S evolve independently (the state is mixed only
+// along its key rows), so when batch x heads would leave CUs idle the value
+// columns are split over several work-groups; each one forms the chunk-local
+// A, P, T and W for all key dims and U, o, S for its own columns.  S stays in
+// MFMA accumulators (the block's value columns are spread 16 per wave over
+// its first waves) and is fed to the S products straight from them (the row
+// operand's columns are permuted in LDS, as in the forward output pass).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -108,7 +112,10 @@ gdn_kernel(const GdnParams p) {
     const long bh = blockIdx.x;
     const int T = p.T;
     const int N = (T + C - 1) / C;
-    const int vb = w * VS;
+    const int kcb = w * VS;                         // this wave's key columns of W
+    const int VB = D / p.nvb;                       // value columns of this work-group
+    const bool vw = kcb < VB;                       // does this wave own value columns?
+    const int vb = int(blockIdx.y) * VB + kcb;      // its first value column
     const int r0 = RPW * w;
 
     const rsrc_t bq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + bh * long(T) * D, long(T) * D * 2);
@@ -132,7 +139,7 @@ gdn_kernel(const GdnParams p) {
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    S[mt][nt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] : 0.f;
+                    S[mt][nt][e] = src && vw ? src[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] : 0.f;
     }
     // entries above the diagonal of P and T diag(beta) are never written
     for (int i = tid; i < 2 * E::tile_bytes(C, L::PC) / 4; i += NW * 64) reinterpret_cast<uint32_t *>(tP)[i] = 0u;
@@ -289,14 +296,21 @@ gdn_kernel(const GdnParams p) {
         for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
-                const frag_t kf = E::ld_col8(tKg, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16);
-                const frag_t vf = E::ld_col8(tV, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16);
+                const frag_t kf = E::ld_col8(tKg, L::PD, ts * 32 + 8 * q4, kcb + 16 * nt, n16);
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {
                     if (ts * 32 > 16 * m + 15) continue;   // T is lower triangular
                     const frag_t tf = E::ld_frag(rowp(tTb, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
                     Wa[nt][m] = E::mma(kf, tf, Wa[nt][m]);
-                    Ua[nt][m] = E::mma(vf, tf, Ua[nt][m]);
+                }
+                if (vw) {
+                    const frag_t vf = E::ld_col8(tV, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16);
+#pragma unroll
+                    for (int m = 0; m < NB; ++m) {
+                        if (ts * 32 > 16 * m + 15) continue;
+                        const frag_t tf = E::ld_frag(rowp(tTb, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
+                        Ua[nt][m] = E::mma(vf, tf, Ua[nt][m]);
+                    }
                 }
             }
         block_sync();  // B8: gamma k no longer read
@@ -306,7 +320,7 @@ gdn_kernel(const GdnParams p) {
             for (int m = 0; m < NB; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    tW[(16 * m + n16) * L::QP + perm_col(vb + 16 * nt + 4 * q4 + e)] = (__bf16)(-Wa[nt][m][e]);
+                    tW[(16 * m + n16) * L::QP + perm_col(kcb + 16 * nt + 4 * q4 + e)] = (__bf16)(-Wa[nt][m][e]);
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {   // (gamma_C / gamma) k over gamma k
             const int r = r0 + i;
@@ -317,11 +331,13 @@ gdn_kernel(const GdnParams p) {
         block_sync();  // B9: -W and the state-update rows visible
 
         // ---- U = U~ - W S and O = (scale gamma q) S, S straight from its accumulators ----
+        // (waves that own value columns only; the others wait at the barriers)
         f32x4_t O[NTW][NB];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
             for (int m = 0; m < NB; ++m) O[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (vw) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             frag_t sf[NTW];
@@ -352,9 +368,12 @@ gdn_kernel(const GdnParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dst[e] = (__bf16)Ua[nt][m][e];
             }
+        }
         block_sync();  // B10: U visible
 
-        // ---- O += P U; o rows to HBM ---------------------------------------------------
+        // ---- O += P U; o rows to HBM; S <- gamma_C S + ((gamma_C / gamma) k)^T U --------
+        const float gC = fexp2(gcl);
+        if (vw) {
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
@@ -372,8 +391,6 @@ gdn_kernel(const GdnParams p) {
                 E::st4(bo, ((t0 + 16 * m + n16) * D + vb + 16 * nt + 4 * q4) * 2, O[nt][m]);
             }
 
-        // ---- S <- gamma_C S + ((gamma_C / gamma) k)^T U ------------------------------------
-        const float gC = fexp2(gcl);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -389,10 +406,11 @@ gdn_kernel(const GdnParams p) {
                 for (int nt = 0; nt < NTW; ++nt)
                     S[mt][nt] = E::mma(a, E::ld_col8(tQr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), S[mt][nt]);
             }
+        }
         block_sync();  // B11: tiles free for the next chunk
     }
 
-    if (p.h_final) {
+    if (p.h_final && vw) {
         float *dst = p.h_final + bh * long(D) * D;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -405,10 +423,13 @@ gdn_kernel(const GdnParams p) {
 
 hipError_t launch_gdn(int D, const GdnParams &p, long nbh, hipStream_t s) {
     if (nbh <= 0) return hipSuccess;
+    // value blocks of at least 16 columns, a power of two, at most one wave's worth each
+    if (p.nvb < 1 || p.nvb > D / 16 || (p.nvb & (p.nvb - 1)) != 0) return hipErrorInvalidValue;
+    const dim3 grid(unsigned(nbh), unsigned(p.nvb));
     if (D == 128)
-        hipLaunchKernelGGL((gdn_kernel<128, 64>), dim3(unsigned(nbh)), dim3(Shape<128, 64>::NW * 64), 0, s, p);
+        hipLaunchKernelGGL((gdn_kernel<128, 64>), grid, dim3(Shape<128, 64>::NW * 64), 0, s, p);
     else if (D == 64)
-        hipLaunchKernelGGL((gdn_kernel<64, 64>), dim3(unsigned(nbh)), dim3(Shape<64, 64>::NW * 64), 0, s, p);
+        hipLaunchKernelGGL((gdn_kernel<64, 64>), grid, dim3(Shape<64, 64>::NW * 64), 0, s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -58,6 +58,7 @@ struct GdnParams {
     float *h_final;            // [heads][D][D] or null
     int T;
     float scale;
+    int nvb;                   // value-column blocks per (batch, head): 1, 2, 4 or 8 (D / 16 at most)
 };
 hipError_t launch_gdn(int D, const GdnParams &p, long nbh, hipStream_t s);
 

@@ -90,6 +90,20 @@ def test_extreme_gates_and_writes(gate, beta):
     check(x, o, hf)
 
 
+@pytest.mark.parametrize("target", [1, 32, 0])
+def test_value_block_split(target):
+    """Value columns split over 1, 2 (B*H = 16, target 32) or 8 (default)
+    work-groups per head give the same result."""
+    say(f"[gdn value blocks] target_wgs={target}")
+    x = make_gdn_inputs(BASE, B=2, H=8, T=333, seed=63, h0_std=0.2)
+    gla.set_tuning(target, 0)
+    try:
+        o, hf = gpu_run(x)
+    finally:
+        gla.set_tuning(0, 0)
+    check(x, o, hf)
+
+
 def test_zero_length_sequence():
     say("[gdn T=0]")
     q = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device=DEV)
