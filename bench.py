@@ -116,6 +116,23 @@ def gdn_bytes(wl) -> int:
     return wl.B * wl.H * (wl.T * (wl.D * 8 + 8) + wl.D * wl.D * 4)
 
 
+GDN_RECORD_BYTES = {128: 119808, 64: 62464}   # per chunk and head, gdn_record_bytes() in the library
+
+
+def gdn_prep_bytes(wl, chunk: int = 64) -> int:
+    """Two-launch form, prep launch: bf16 q, k, v and fp32 g, beta read per
+    token-head; one record plus gamma_C written per chunk and head."""
+    n = -(-wl.T // chunk)
+    return wl.B * wl.H * (wl.T * (wl.D * 6 + 8) + n * (GDN_RECORD_BYTES[wl.D] + 4))
+
+
+def gdn_walk_bytes(wl, chunk: int = 64) -> int:
+    """Two-launch form, walk launch: every record (and gamma_C) read once per
+    chunk and head, bf16 o written per token-head, the fp32 final state."""
+    n = -(-wl.T // chunk)
+    return wl.B * wl.H * (n * (GDN_RECORD_BYTES[wl.D] + 4) + wl.T * wl.D * 2 + wl.D * wl.D * 4)
+
+
 def gdn_flops(wl, chunk: int = 64) -> int:
     """Matrix products per token-head of the chunk form: k k^T, q k^T, W and
     U~ (chunk-deep), W S, q S and the state update (D-deep), P U."""
@@ -386,22 +403,31 @@ def bench_gdn(args, wl):
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    gla.profile_start(args.steps + 8)
+    gla.profile_start(4 * args.steps + 8)
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    kms = [t for kind, t in gla.profile_stop() if kind == "gdn"]
+    by = {}
+    for kind, t in gla.profile_stop():
+        by.setdefault(kind, []).append(t)
     if args.copy_calibration:
         copy_calibration(dev)
-    k_ms = statistics.mean(kms)
-    per_launch = gdn_bytes(wl)
+    # the one-launch form, or the larger of the two launches of the other form
+    names = {"gdn": ("gdn_kernel<128,64,false>", gdn_bytes(wl)),
+             "gdn_prep": ("gdn_kernel<128,64,true> (prep)", gdn_prep_bytes(wl)),
+             "gdn_walk": ("gdn_walk_kernel<128,64>", gdn_walk_bytes(wl))}
+    kinds = [k for k in names if k in by]
+    dom = max(kinds, key=lambda k: sum(by[k]))
+    k_ms = statistics.mean(by[dom])
+    kname, per_launch = names[dom]
     achieved = per_launch / (k_ms * 1e-3) / 1e9
     flops = gdn_flops(wl)
+    path_ms = sum(sum(by[k]) for k in kinds) / args.steps
     traffic = None
     c = read_counters(wl.name)
     if c and "fetch_factor" in c:
         m = c["median_per_dispatch_KiB"]
-        f, w = m.get("gdn:FETCH_SIZE"), m.get("gdn:WRITE_SIZE")
+        f, w = m.get(f"{dom}:FETCH_SIZE"), m.get(f"{dom}:WRITE_SIZE")
         if f is not None and w is not None:
             traffic = int(f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"])
     res = {
@@ -421,10 +447,14 @@ def bench_gdn(args, wl):
                    "chunk": 64, "h_final": True, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdn_kernel<128,64>", "kernel_ms": k_ms,
-                     "algorithmic_bytes_per_launch": per_launch,
-                     "mfma_tflops": flops / (k_ms * 1e-3) / 1e12,
-                     "mfma_frac": flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+                     "kernel": kname, "kernel_ms": k_ms,
+                     "algorithmic_bytes_per_launch": per_launch},
+        "whole_path": {"launches": {k: statistics.mean(by[k]) for k in kinds},
+                       "kernels_ms_per_step": path_ms,
+                       "algorithmic_bytes": gdn_bytes(wl),
+                       "hbm_frac": gdn_bytes(wl) / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "mfma_tflops": flops / (path_ms * 1e-3) / 1e12,
+                       "mfma_frac": flops / (path_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline_gdn(wl, host)
@@ -545,7 +575,7 @@ def summarize_counters(outdir: str, wl_name: str):
         last_chunk = max((int(r["Dispatch_Id"]) for r in rows
                           if any(s in r["Kernel_Name"]
                                  for s in ("chunk_kernel", "state_kernel", "decode_kernel",
-                                           "bwd_kernel", "gdn_kernel"))),
+                                           "bwd_kernel", "gdn_kernel", "gdn_walk_kernel"))),
                          default=-1)
         for r in rows:
             name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
@@ -557,8 +587,10 @@ def summarize_counters(outdir: str, wl_name: str):
                 kind = "scan"
             elif "decode_kernel" in name:
                 kind = "decode"
+            elif "gdn_walk_kernel" in name:
+                kind = "gdn_walk"
             elif "gdn_kernel" in name:
-                kind = "gdn"
+                kind = "gdn_prep" if "true" in name else "gdn"
             elif "bwd_kernel" in name:
                 kind = "bwd" if name.split(",")[3].strip(" >)(")[:1] == "1" else "bwd_segment"
             elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_chunk:

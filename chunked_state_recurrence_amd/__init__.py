@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     profile_stop,
     release,
     set_tuning,
+    gdn_set_path,
     strerror,
     version,
 )

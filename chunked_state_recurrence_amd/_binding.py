@@ -27,9 +27,11 @@ ERRORS = {
 EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_version",
             "gla_release", "gla_profile_start", "gla_profile_stop", "gla_stage_cumsum",
             "gla_stage_intra", "gla_stage_states", "gla_decode", "gla_decode_f32",
-            "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd")
+            "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd",
+            "gla_gdn_set_path")
 KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode", 5: "bwd_segment",
-                6: "bwd", 7: "gdn"}
+                6: "bwd", 7: "gdn", 8: "gdn_prep", 9: "gdn_walk"}
+GDN_PATHS = {"auto": 0, "one": 1, "two": 2}
 
 
 class _KernelTime(ctypes.Structure):
@@ -73,6 +75,7 @@ def load_library(path: str = LIB_PATH):
     lib.gla_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
     lib.gla_decode_f32.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
     lib.gla_set_tuning.argtypes = [I, I]
+    lib.gla_gdn_set_path.argtypes = [I, I]
     lib.gla_strerror.argtypes = [I]
     lib.gla_strerror.restype = ctypes.c_char_p
     lib.gla_version.argtypes = []
@@ -84,7 +87,8 @@ def load_library(path: str = LIB_PATH):
     lib.gla_profile_stop.restype = ctypes.c_int
     for name in ("gla_fwd", "gla_fwd_f32", "gla_stage_states", "gla_stage_cumsum",
                  "gla_stage_intra", "gla_set_tuning", "gla_version", "gla_decode", "gla_decode_f32",
-                 "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd"):
+                 "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd",
+                 "gla_gdn_set_path"):
         getattr(lib, name).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -315,6 +319,12 @@ def gla_stage_intra(q, k, g, *, chunk=64, scale=None, stream=None):
 
 def set_tuning(target_wgs: int = 0, head_group: int = 0):
     _check(load_library().gla_set_tuning(int(target_wgs), int(head_group)))
+
+
+def gdn_set_path(path: str = "auto", window_chunks: int = 0):
+    """Form of gla_gdn_fwd: "auto", "one" (one launch) or "two" (prep + walk);
+    window_chunks > 0 caps the two-launch windows (chunks of 64 tokens)."""
+    _check(load_library().gla_gdn_set_path(GDN_PATHS[path], int(window_chunks)))
 
 
 def profile_start(capacity: int):

@@ -35,6 +35,11 @@ std::mutex g_mu;
 std::vector<DeviceState> g_dev;
 int g_target_wgs = kDefaultTargetWgs;
 int g_head_group = 0;
+int g_gdn_path = GLA_GDN_AUTO;
+int g_gdn_window = 0;   // chunks per window of the two-launch form (0 = by the record cap)
+// records of the gated delta rule's two-launch form are made for windows of
+// chunks whose records take at most this many bytes
+constexpr size_t kGdnRecordCap = size_t(1) << 30;
 
 // launch tracing (gla_profile_start / gla_profile_stop)
 struct Trace {
@@ -443,17 +448,63 @@ int gla_gdn_fwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const f
             return GLA_ERR_LAUNCH;
         return GLA_OK;
     }
-    // split value columns over work-groups while batch x heads leaves CUs idle
-    int nvb = 1;
+    int target, path, wcap;
     {
-        int target;
         std::lock_guard<std::mutex> lk(g_mu);
         target = g_target_wgs;
-        while (nvb < K / 16 && long(bh) * nvb * 2 <= target) nvb *= 2;
+        path = g_gdn_path;
+        wcap = g_gdn_window;
     }
-    gla::GdnParams p{q, k, v, g, beta, h0, o, h_final, T, scale, nvb};
-    if (traced(GLA_KERNEL_GDN, s, [&] { return gla::launch_gdn(K, p, long(bh), s); }) != hipSuccess)
-        return GLA_ERR_LAUNCH;
+    const int N = (T + 63) / 64;
+    const bool two = path == GLA_GDN_TWO_LAUNCH || (path == GLA_GDN_AUTO && long(bh) * 4 <= target);
+    if (!two) {
+        // split value columns over work-groups while batch x heads leaves CUs idle
+        int nvb = 1;
+        while (nvb < K / 16 && long(bh) * nvb * 2 <= target) nvb *= 2;
+        gla::GdnParams p{q, k, v, g, beta, h0, o, h_final, T, scale, nvb};
+        p.nbh = int(bh);
+        if (traced(GLA_KERNEL_GDN, s, [&] { return gla::launch_gdn(K, p, long(bh), s); }) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+        return GLA_OK;
+    }
+    // two launches per window of chunks: the chunk-local prep (all chunks at
+    // once), then the sequential walk carrying the state
+    const size_t rec = gla::gdn_record_bytes(K);
+    int window = int(std::max<size_t>(1, std::min<size_t>(size_t(N), kGdnRecordCap / (bh * rec))));
+    if (wcap > 0) window = std::min(window, wcap);
+    const bool multi = window < N;
+    const size_t nrec = bh * size_t(window);
+    const size_t need = nrec * rec + nrec * 4 + (multi ? nst : 0);
+    float *ws = nullptr;
+    if ((rc = ensure_workspace(dev, need, &ws)) != GLA_OK) return rc;
+    unsigned char *wsb = reinterpret_cast<unsigned char *>(ws);
+    float *ws_gc = reinterpret_cast<float *>(wsb + nrec * rec);
+    float *carry = multi ? reinterpret_cast<float *>(wsb + nrec * rec + nrec * 4) : nullptr;
+    const int slices_max = int(std::min<long>(65535, std::max<long>(1, (target + long(bh) - 1) / long(bh))));
+    for (int c0 = 0; c0 < N; c0 += window) {
+        const int nc = std::min(window, N - c0);
+        const bool last = c0 + nc >= N;
+        gla::GdnParams p{q, k, v, g, beta, c0 == 0 ? h0 : carry, o, last ? h_final : carry, T, scale, 1};
+        p.ws = wsb;
+        p.ws_gc = ws_gc;
+        p.c0 = c0;
+        p.nc = nc;
+        p.nbh = int(bh);
+        const int slices = std::min(nc, slices_max);
+        if (traced(GLA_KERNEL_GDN_PREP, s, [&] { return gla::launch_gdn_prep(K, p, slices, s); }) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+        if (traced(GLA_KERNEL_GDN_WALK, s, [&] { return gla::launch_gdn_walk(K, p, s); }) != hipSuccess)
+            return GLA_ERR_LAUNCH;
+    }
+    return GLA_OK;
+}
+
+int gla_gdn_set_path(int path, int window_chunks) {
+    if (path != GLA_GDN_AUTO && path != GLA_GDN_ONE_LAUNCH && path != GLA_GDN_TWO_LAUNCH) return GLA_ERR_SHAPE;
+    if (window_chunks < 0) return GLA_ERR_SHAPE;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_gdn_path = path;
+    g_gdn_window = window_chunks;
     return GLA_OK;
 }
 

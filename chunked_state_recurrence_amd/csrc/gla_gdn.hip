@@ -56,6 +56,28 @@ template <int D, int C> struct GdnLayout {
     static constexpr int bytes = tt + C * PF * 4;
 };
 
+// Per-chunk record that the prep pass leaves for the walk (device memory,
+// [heads][chunks of the window] records).  The three operand tiles are byte
+// images of the LDS tiles the walk reads them from (pads included), so the
+// walk stages them with plain 16-byte direct loads:
+//   wi: -W rows, permuted columns          qi: Q' = scale gamma q - P W rows, permuted
+//   ki: (gamma_C / gamma) k rows, bank-spread
+//   ut, ot: U~ = T diag(beta) V and O0 = P U~ (fp32) in the MFMA accumulator
+//   layout, [value block of 16][row tile of 16][lane][4]: one value block's
+//   tiles are 4 KB of contiguous bytes.
+template <int D, int C> struct GdnRec {
+    using L = GdnLayout<D, C>;
+    static constexpr int IW = C * L::QP * 2;
+    static constexpr int IK = L::TD;
+    static constexpr int wi = 0, qi = IW, ki = 2 * IW, ut = ki + IK, ot = ut + C * D * 4;
+    static constexpr int bytes = ot + C * D * 4;
+    static constexpr int images = ut;                 // bytes of the three tile images
+    static constexpr int blk = (C / 16) * 1024;       // one value block of ut or ot
+    static_assert(IW % 1024 == 0 && IK % 1024 == 0 && bytes % 1024 == 0, "1 KB direct-load granules");
+};
+
+size_t gdn_record_bytes(int D) { return D == 128 ? GdnRec<128, 64>::bytes : GdnRec<64, 64>::bytes; }
+
 // 16 x 16 x 16 fp32 product from LDS blocks (row-major, `pa` / `pb` floats per
 // row): acc[e] += sum_m A[4 q4 + e][m] B[m][n16]... with the operands supplied
 // as v_mfma_f32_16x16x4f32 takes them (lane (n16, q4) gives A[n16][4i + q4]
@@ -71,7 +93,11 @@ __device__ __forceinline__ f32x4_t mma16_f32(const float *A, int pa, const float
 
 __device__ __forceinline__ void wave_lds_fence() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int D, int C>
+// PREP = false: the whole recurrence, one work-group per (batch, head, value
+// block) walking every chunk.  PREP = true: the chunk-local half only (no
+// state), work-group (head, slice) taking chunks slice, slice + slices, ... of
+// the window [c0, c0 + nc) and writing each chunk's record for the walk.
+template <int D, int C, bool PREP>
 __global__ void __launch_bounds__((Shape<D, C>::NW * 64))
 gdn_kernel(const GdnParams p) {
     using E = BF16;
@@ -111,11 +137,13 @@ gdn_kernel(const GdnParams p) {
     const int q4 = lane >> 4;
     const long bh = blockIdx.x;
     const int T = p.T;
-    const int N = (T + C - 1) / C;
+    const int N = PREP ? p.nc : (T + C - 1) / C;   // chunks walked, counted from chunk cb
+    const int cb = PREP ? p.c0 : 0;
+    const int cfirst = PREP ? int(blockIdx.y) : 0, cstep = PREP ? int(gridDim.y) : 1;
     const int kcb = w * VS;                         // this wave's key columns of W
-    const int VB = D / p.nvb;                       // value columns of this work-group
+    const int VB = PREP ? D : D / p.nvb;            // value columns of this work-group
     const bool vw = kcb < VB;                       // does this wave own value columns?
-    const int vb = int(blockIdx.y) * VB + kcb;      // its first value column
+    const int vb = (PREP ? 0 : int(blockIdx.y)) * VB + kcb;   // its first value column
     const int r0 = RPW * w;
 
     const rsrc_t bq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + bh * long(T) * D, long(T) * D * 2);
@@ -131,7 +159,7 @@ gdn_kernel(const GdnParams p) {
 
     // ---- state ---------------------------------------------------------------
     f32x4_t S[MT][NTW];
-    {
+    if constexpr (!PREP) {
         const float *src = p.h0 ? p.h0 + bh * long(D) * D : nullptr;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -144,41 +172,69 @@ gdn_kernel(const GdnParams p) {
     // entries above the diagonal of P and T diag(beta) are never written
     for (int i = tid; i < 2 * E::tile_bytes(C, L::PC) / 4; i += NW * 64) reinterpret_cast<uint32_t *>(tP)[i] = 0u;
 
-    for (int c = 0; c < N; ++c) {
-        const int t0 = c * C;
-        // ---- rows of the chunk: q, k into registers, v into LDS, gates ----------
-        Raw<E, CPL> rq[RPW], rk[RPW];
-        {
-            const int eoff = (t0 + r0) * D + lane * CPL;
+    // Loads of chunk cn: q and k rows into the staging area over the fp32 A / T
+    // tiles (each wave its own rows, 16-byte lanes), v rows into the bank-spread
+    // tile, gates of the chunk into wave 0's registers.  Chunk c + 1 is requested
+    // while chunk c still works, once those areas are free.
+    unsigned char *stq = smem + L::aa;
+    unsigned char *stk = stq + C * D * 2;
+    constexpr int NSL = RPW * D * 2 / 1024;   // 16-byte-lane loads per wave and operand
+    static_assert(NSL * 1024 == RPW * D * 2 && 2 * C * D * 2 <= 2 * C * L::PF * 4, "staging");
+    float gx = 0.f, gb = 0.f;
+    auto issue_qk = [&](int cn) {
+        const int row0 = __builtin_amdgcn_readfirstlane((cb + cn) * C + r0);
+        const int lr0 = __builtin_amdgcn_readfirstlane(r0);
+        mem_fence_compiler();
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                rq[i].load(bq, eoff * 2, i * D * 2);
-                rk[i].load(bk, eoff * 2, i * D * 2);
-            }
-            const int row0 = __builtin_amdgcn_readfirstlane(t0 + r0);
-            const int lr0 = __builtin_amdgcn_readfirstlane(r0);
-            mem_fence_compiler();
-#pragma unroll
-            for (int i = 0; i < RPW; ++i)   // 4 bytes per lane: a 64-wide row takes lanes 0..31
-                if (CPL == 2 || lane < 32) dma<4>(bv, tV + E::rowoff(lr0 + i, L::PD), lane * 4, (row0 + i) * D * 2);
-            mem_fence_compiler();
-            if (w == 0) {   // gates (log2) scanned over the chunk, one row per lane
-                float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bg, (t0 + lane) * 4, 0, 0)) * kLog2e;
-                const float bt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bb, (t0 + lane) * 4, 0, 0));
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_up(x, off, 64);
-                    if (lane >= off) x += y;
-                }
-                sGc[lane] = x;
-                sBeta[lane] = bt;
-            }
-            wait_vmem<0>();
+        for (int i = 0; i < NSL; ++i) {
+            dma<16>(bq, stq + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
+            dma<16>(bk, stk + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
         }
+        mem_fence_compiler();
+    };
+    auto issue_vg = [&](int cn) {
+        const int row0 = __builtin_amdgcn_readfirstlane((cb + cn) * C + r0);
+        const int lr0 = __builtin_amdgcn_readfirstlane(r0);
+        mem_fence_compiler();
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)   // 4 bytes per lane: a 64-wide row takes lanes 0..31
+            if (CPL == 2 || lane < 32) dma<4>(bv, tV + E::rowoff(lr0 + i, L::PD), lane * 4, (row0 + i) * D * 2);
+        mem_fence_compiler();
+        if (w == 0) {
+            gx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bg, ((cb + cn) * C + lane) * 4, 0, 0));
+            gb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bb, ((cb + cn) * C + lane) * 4, 0, 0));
+        }
+    };
+    if (cfirst < N) {
+        issue_qk(cfirst);
+        issue_vg(cfirst);
+    }
+
+    for (int c = cfirst; c < N; c += cstep) {
+        const int t0 = (cb + c) * C;
+        const int cn = c + cstep;
+        // ---- gates of the chunk scanned (log2 units), one row per lane -------------
+        if (w == 0) {
+            float x = gx * kLog2e;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            sGc[lane] = x;
+            sBeta[lane] = gb;
+        }
+        wait_vmem<0>();   // this chunk's rows (requested one chunk ahead)
         block_sync();  // B1: gates, v rows
 
         // ---- operand rows ----------------------------------------------------------
         const float gcl = sGc[C - 1];
+        Raw<E, CPL> rq[RPW], rk[RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            rq[i].x = reinterpret_cast<const decltype(rq[i].x) *>(stq + (r0 + i) * D * 2)[lane];
+            rk[i].x = reinterpret_cast<const decltype(rk[i].x) *>(stk + (r0 + i) * D * 2)[lane];
+        }
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int r = r0 + i;
@@ -281,6 +337,7 @@ gdn_kernel(const GdnParams p) {
             }
             block_sync();  // B5..B7: one level of T
         }
+        if (cn < N) issue_qk(cn);   // the A / T tiles are no longer read
 
         // ---- W = T diag(beta) (gamma K) and U~ = T diag(beta) V for this wave's
         //      columns; acc[e] = X[row 16m + n16][col + 4q4 + e] -------------------------
@@ -313,7 +370,8 @@ gdn_kernel(const GdnParams p) {
                     }
                 }
             }
-        block_sync();  // B8: gamma k no longer read
+        block_sync();  // B8: gamma k and v no longer read
+        if (!PREP && cn < N) issue_vg(cn);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
@@ -328,7 +386,79 @@ gdn_kernel(const GdnParams p) {
 #pragma unroll
             for (int u = 0; u < CPL; ++u) rowp(tKg, r, L::PD)[lane * CPL + u] = (__bf16)(rk[i].get(u) * gk);
         }
+        using R = GdnRec<D, C>;
+        unsigned char *rec = nullptr;
+        if constexpr (PREP) {
+            // W (bf16, bank-spread, over raw q) and U~ (bf16, over v) as operands of
+            // P W and P U~; U~ in fp32 into the record
+            rec = static_cast<unsigned char *>(p.ws) + (size_t(bh) * p.nc + c) * R::bytes;
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    __bf16 *dw = rowp(tQr, 16 * m + n16, L::PD) + kcb + 16 * nt + 4 * q4;
+                    __bf16 *du = rowp(tV, 16 * m + n16, L::PD) + vb + 16 * nt + 4 * q4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dw[e] = (__bf16)Wa[nt][m][e];
+                        du[e] = (__bf16)Ua[nt][m][e];
+                    }
+                    *reinterpret_cast<f32x4_t *>(rec + R::ut + ((vb + 16 * nt) / 16) * R::blk + m * 1024 + lane * 16) =
+                        Ua[nt][m];
+                }
+        }
         block_sync();  // B9: -W and the state-update rows visible
+
+        if constexpr (PREP) {
+            // ---- Q' = scale gamma q - P W (in place over the permuted q tile) and
+            //      O0 = P U~ (fp32, into the record); acc[e] = X[row 16m + n16][col + 4q4 + e]
+            f32x4_t Qa[NTW][NB], Oa[NTW][NB];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    Qa[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    Oa[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+                    if (ts * 32 > 16 * m + 15) continue;   // P is lower triangular
+                    const frag_t pf = E::ld_frag(rowp(tP, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) {
+                        Qa[nt][m] = E::mma(E::ld_col8(tQr, L::PD, ts * 32 + 8 * q4, kcb + 16 * nt, n16), pf, Qa[nt][m]);
+                        Oa[nt][m] = E::mma(E::ld_col8(tV, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), pf, Oa[nt][m]);
+                    }
+                }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        __bf16 &x = tQh[(16 * m + n16) * L::QP + perm_col(kcb + 16 * nt + 4 * q4 + e)];
+                        x = (__bf16)(float(x) - Qa[nt][m][e]);
+                    }
+                    *reinterpret_cast<f32x4_t *>(rec + R::ot + ((vb + 16 * nt) / 16) * R::blk + m * 1024 + lane * 16) =
+                        Oa[nt][m];
+                }
+            block_sync();  // B10: the three tile images complete, v and raw q free
+            if (cn < N) issue_vg(cn);
+            // tile images to the record, 16 bytes per lane
+            {
+                const unsigned char *src[3] = {tKr, reinterpret_cast<const unsigned char *>(tQh), tKg};
+                const int off[3] = {R::wi, R::qi, R::ki};
+                const int len[3] = {R::IW, R::IW, R::IK};
+#pragma unroll
+                for (int a = 0; a < 3; ++a)
+                    for (int o = tid * 16; o < len[a]; o += NW * 64 * 16)
+                        *reinterpret_cast<u32x4_t *>(rec + off[a] + o) =
+                            *reinterpret_cast<const u32x4_t *>(src[a] + o);
+            }
+            if (tid == 0) p.ws_gc[size_t(bh) * p.nc + c] = fexp2(gcl);
+        } else {
 
         // ---- U = U~ - W S and O = (scale gamma q) S, S straight from its accumulators ----
         // (waves that own value columns only; the others wait at the barriers)
@@ -407,17 +537,152 @@ gdn_kernel(const GdnParams p) {
                     S[mt][nt] = E::mma(a, E::ld_col8(tQr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), S[mt][nt]);
             }
         }
+        }
         block_sync();  // B11: tiles free for the next chunk
     }
 
-    if (p.h_final && vw) {
+    if constexpr (!PREP) {
+        if (p.h_final && vw) {
+            float *dst = p.h_final + bh * long(D) * D;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
+        }
+    }
+}
+
+// The sequential half: one wave per (batch, head, 16 value columns) walks the
+// chunks of the window with its columns of S in MFMA accumulators,
+//     U = U~ - W S,   o = O0 + Q' S,   S <- gamma_C S + ((gamma_C / gamma) k)^T U,
+// reading each chunk's record (staged by direct loads into LDS one chunk ahead).
+// The D / 16 waves of one head are placed on one XCD (work-groups are dealt to
+// the XCDs round-robin), so they share the records through that XCD's L2.
+// p.h0 is the state at the window start (null = zero), p.h_final receives the
+// state at its end (null = not written); they may be the same buffer.
+template <int D, int C>
+__global__ void __launch_bounds__(64)
+gdn_walk_kernel(const GdnParams p) {
+    using E = BF16;
+    using L = GdnLayout<D, C>;
+    using R = GdnRec<D, C>;
+    using frag_t = E::frag_t;
+    constexpr int NB = C / 16;
+    constexpr int MT = D / 16;
+    constexpr int KS = D / 32;
+    constexpr int TS = C / 32;
+    constexpr int NVB = D / 16;
+    constexpr int PU = 32;                                     // U tile: 16 bf16 columns a row
+    constexpr int OU = R::images, OO = OU + R::blk, OG = OO + R::blk;
+    constexpr int BUF = OG + 256;                              // one chunk's staged record
+    constexpr int NIMG = R::images / 1024, NBLK = R::blk / 1024;
+    constexpr int NISSUE = NIMG + 2 * NBLK + 1;                // direct loads per chunk
+    static_assert(NISSUE <= 63, "vmcnt range");
+    static_assert(2 * BUF + E::tile_bytes(C, PU) <= 163840, "LDS");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF + E::tile_bytes(C, PU)];
+    unsigned char *tU = smem + 2 * BUF;
+
+    const int lane = threadIdx.x;
+    const int n16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const long bh = long(j / NVB) * 8 + xcd;
+    if (bh >= p.nbh) return;
+    const int vb = (j % NVB) * 16;
+    const int nc = p.nc;
+    const int T = p.T;
+
+    const rsrc_t brec = make_rsrc(static_cast<const unsigned char *>(p.ws) + size_t(bh) * nc * R::bytes,
+                                  long(nc) * R::bytes);
+    const rsrc_t bgc = make_rsrc(p.ws_gc + size_t(bh) * nc, long(nc) * 4);
+    const rsrc_t bo = make_rsrc(reinterpret_cast<uint16_t *>(p.o) + bh * long(T) * D, long(T) * D * 2);
+
+    f32x4_t S[MT];
+    {
+        const float *src = p.h0 ? p.h0 + bh * long(D) * D : nullptr;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[mt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + vb + n16] : 0.f;
+    }
+
+    auto issue = [&](int c) {
+        unsigned char *buf = smem + (c & 1) * BUF;
+        const int base = __builtin_amdgcn_readfirstlane(c * R::bytes);
+        const int vblk = __builtin_amdgcn_readfirstlane(vb / 16);
+        mem_fence_compiler();
+#pragma unroll
+        for (int i = 0; i < NIMG; ++i) dma<16>(brec, buf + i * 1024, lane * 16, base + i * 1024);
+#pragma unroll
+        for (int i = 0; i < NBLK; ++i) {
+            dma<16>(brec, buf + OU + i * 1024, lane * 16, base + R::ut + vblk * R::blk + i * 1024);
+            dma<16>(brec, buf + OO + i * 1024, lane * 16, base + R::ot + vblk * R::blk + i * 1024);
+        }
+        dma<4>(bgc, buf + OG, lane * 4, c * 4);   // gamma_C of chunks c.. (lane 0's is used)
+        mem_fence_compiler();
+    };
+
+    if (nc > 0) issue(0);
+    for (int c = 0; c < nc; ++c) {
+        __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the buffer reloaded next
+        if (c + 1 < nc) {
+            issue(c + 1);
+            wait_vmem<NISSUE>();
+        } else {
+            wait_vmem<0>();
+        }
+        mem_fence_compiler();
+        const unsigned char *buf = smem + (c & 1) * BUF;
+        const __bf16 *wi = reinterpret_cast<const __bf16 *>(buf + R::wi);
+        const __bf16 *qi = reinterpret_cast<const __bf16 *>(buf + R::qi);
+        f32x4_t U[NB], O[NB];
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            U[m] = *reinterpret_cast<const f32x4_t *>(buf + OU + m * 1024 + lane * 16);
+            O[m] = *reinterpret_cast<const f32x4_t *>(buf + OO + m * 1024 + lane * 16);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[e] = S[2 * ks][e]; x[4 + e] = S[2 * ks + 1][e]; }
+            const frag_t sf = E::pack(x);
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                U[m] = E::mma(sf, E::ld_frag(wi + (16 * m + n16) * L::QP + ks * 32 + 8 * q4), U[m]);
+                O[m] = E::mma(sf, E::ld_frag(qi + (16 * m + n16) * L::QP + ks * 32 + 8 * q4), O[m]);
+            }
+        }
+        const int t0 = (p.c0 + c) * C;
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+            E::st4(bo, ((t0 + 16 * m + n16) * D + vb + 4 * q4) * 2, O[m]);
+            __bf16 *dst = reinterpret_cast<__bf16 *>(tU + E::rowoff(16 * m + n16, PU)) + 4 * q4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = (__bf16)U[m][e];
+        }
+        wave_lds_fence();
+        const float gC = *reinterpret_cast<const float *>(buf + OG);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[mt][e] *= gC;
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts) {
+            const frag_t uf = E::ld_col8(tU, PU, ts * 32 + 8 * q4, 0, n16);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                S[mt] = E::mma(E::ld_col8(buf + R::ki, L::PD, ts * 32 + 8 * q4, 16 * mt, n16), uf, S[mt]);
+        }
+    }
+    if (p.h_final) {
         float *dst = p.h_final + bh * long(D) * D;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
+            for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * q4 + e) * D + vb + n16] = S[mt][e];
     }
 }
 
@@ -427,9 +692,37 @@ hipError_t launch_gdn(int D, const GdnParams &p, long nbh, hipStream_t s) {
     if (p.nvb < 1 || p.nvb > D / 16 || (p.nvb & (p.nvb - 1)) != 0) return hipErrorInvalidValue;
     const dim3 grid(unsigned(nbh), unsigned(p.nvb));
     if (D == 128)
-        hipLaunchKernelGGL((gdn_kernel<128, 64>), grid, dim3(Shape<128, 64>::NW * 64), 0, s, p);
+        hipLaunchKernelGGL((gdn_kernel<128, 64, false>), grid, dim3(Shape<128, 64>::NW * 64), 0, s, p);
     else if (D == 64)
-        hipLaunchKernelGGL((gdn_kernel<64, 64>), grid, dim3(Shape<64, 64>::NW * 64), 0, s, p);
+        hipLaunchKernelGGL((gdn_kernel<64, 64, false>), grid, dim3(Shape<64, 64>::NW * 64), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_prep(int D, const GdnParams &p, int slices, hipStream_t s) {
+    if (p.nbh <= 0 || p.nc <= 0) return hipSuccess;
+    if (slices < 1 || slices > p.nc || slices > 65535 || !p.ws || !p.ws_gc) return hipErrorInvalidValue;
+    const dim3 grid(unsigned(p.nbh), unsigned(slices));
+    if (D == 128)
+        hipLaunchKernelGGL((gdn_kernel<128, 64, true>), grid, dim3(Shape<128, 64>::NW * 64), 0, s, p);
+    else if (D == 64)
+        hipLaunchKernelGGL((gdn_kernel<64, 64, true>), grid, dim3(Shape<64, 64>::NW * 64), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_walk(int D, const GdnParams &p, hipStream_t s) {
+    if (p.nbh <= 0 || p.nc <= 0) return hipSuccess;
+    if (!p.ws || !p.ws_gc) return hipErrorInvalidValue;
+    // the D / 16 waves of a head on one XCD: 8 x ceil(heads / 8) x (D / 16) work-groups
+    const long wgs = 8L * ((p.nbh + 7) / 8) * (D / 16);
+    if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
+    if (D == 128)
+        hipLaunchKernelGGL((gdn_walk_kernel<128, 64>), dim3(unsigned(wgs)), dim3(64), 0, s, p);
+    else if (D == 64)
+        hipLaunchKernelGGL((gdn_walk_kernel<64, 64>), dim3(unsigned(wgs)), dim3(64), 0, s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -59,8 +59,17 @@ struct GdnParams {
     int T;
     float scale;
     int nvb;                   // value-column blocks per (batch, head): 1, 2, 4 or 8 (D / 16 at most)
+    // two-launch form (chunk-parallel prep, then the sequential walk) over the
+    // window of chunks [c0, c0 + nc): per-chunk records and gamma_C per chunk
+    void *ws;                  // [heads][nc] records of gdn_record_bytes(D)
+    float *ws_gc;              // [heads][nc]
+    int c0, nc;
+    int nbh;                   // batch x heads
 };
 hipError_t launch_gdn(int D, const GdnParams &p, long nbh, hipStream_t s);
+size_t gdn_record_bytes(int D);
+hipError_t launch_gdn_prep(int D, const GdnParams &p, int slices, hipStream_t s);
+hipError_t launch_gdn_walk(int D, const GdnParams &p, hipStream_t s);
 
 bool chunk_supported(int dtype, int D, int C);
 // work-groups of the state pass that fit on one CU (LDS bound), 1 or 2

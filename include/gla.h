@@ -105,7 +105,9 @@ int gla_set_tuning(int target_wgs, int head_group);
  * (segment end states), GLA_KERNEL_SCAN (segment-state scan),
  * GLA_KERNEL_DECODE (a gla_decode step, gla_decode.h), GLA_KERNEL_BWD_SEGMENT
  * and GLA_KERNEL_BWD (the backward's segment pass and chunk pass,
- * gla_bwd.h), GLA_KERNEL_GDN (gla_gdn_fwd, gla_gdn.h), GLA_KERNEL_OTHER.
+ * gla_bwd.h), GLA_KERNEL_GDN, GLA_KERNEL_GDN_PREP and GLA_KERNEL_GDN_WALK
+ * (gla_gdn_fwd's one-launch form and the two launches of its other form,
+ * gla_gdn.h), GLA_KERNEL_OTHER.
  * gla_profile_start(capacity) creates the events
  * (capacity launches; more are not traced) and returns GLA_OK or
  * GLA_ERR_ALLOC.  gla_profile_stop waits for the traced work, writes up to
@@ -122,6 +124,8 @@ int gla_set_tuning(int target_wgs, int head_group);
 #define GLA_KERNEL_BWD_SEGMENT 5
 #define GLA_KERNEL_BWD     6
 #define GLA_KERNEL_GDN     7
+#define GLA_KERNEL_GDN_PREP 8
+#define GLA_KERNEL_GDN_WALK 9
 typedef struct {
     int kind;     /* GLA_KERNEL_* */
     float ms;     /* device time between the bracketing events */

@@ -23,13 +23,26 @@
  * L2-normalised, as the delta rule assumes (the bf16 error bound of the
  * matrix products relies on it).
  *
- * One work-group per (batch, head) walks the sequence: this build has no
- * sequence parallelism for the gated delta rule, so B*H should fill the GPU
- * (256 work-groups, one per CU) for full speed.
+ * Two evaluation forms, same results up to rounding:
+ *   one launch  — one work-group per (batch, head, block of value columns)
+ *                 forms each chunk's system and walks the state through the
+ *                 chunks; used when B*H fills the GPU;
+ *   two launches — a chunk-parallel prep forms, for every chunk at once, the
+ *                 chunk-local products (T, W, U~ and the output terms that do
+ *                 not involve the state) into a per-chunk record, then a walk
+ *                 with one wave per (batch, head, 16 value columns) carries the
+ *                 state through the records; used when B*H is small.  The
+ *                 records (gdn_record bytes = 117 KiB per chunk and head at
+ *                 K = 128, 61 KiB at 64) live in the library's cached per-device
+ *                 workspace (grown with hipMalloc, freed by gla_release());
+ *                 long sequences are processed in windows of at most 1 GiB of
+ *                 records, the state carried between windows in the workspace.
  *
  * Ownership, nullability (h0 NULL = zero state, h_final NULL = not written),
  * aliasing (o, h_final must not overlap the inputs or each other), streams,
- * determinism and error codes: as gla_fwd in gla.h.  No workspace is used.
+ * determinism and error codes: as gla_fwd in gla.h (GLA_ERR_ALLOC when the
+ * workspace of the two-launch form cannot be grown).  Calls on one device
+ * must not overlap in time.
  */
 #ifndef GLA_GDN_H
 #define GLA_GDN_H
@@ -44,6 +57,20 @@ int gla_gdn_fwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v,
             const float *g, const float *beta, const float *h0, gla_bf16 *o,
             float *h_final, int B, int H, int T, int K, int V, int chunk,
             float scale, void *stream);
+
+/*
+ * gla_gdn_set_path — which form gla_gdn_fwd uses (process-wide; a schedule
+ * knob with no effect on results beyond rounding): GLA_GDN_AUTO (default:
+ * two launches when 4*B*H <= the work-group target of gla_set_tuning, 256 by
+ * default), GLA_GDN_ONE_LAUNCH, GLA_GDN_TWO_LAUNCH.  window_chunks > 0 caps
+ * the two-launch form's windows at that many 64-token chunks (0 = only the
+ * 1 GiB record cap).  Returns GLA_OK, or GLA_ERR_SHAPE for another path or a
+ * negative window.
+ */
+#define GLA_GDN_AUTO       0
+#define GLA_GDN_ONE_LAUNCH 1
+#define GLA_GDN_TWO_LAUNCH 2
+int gla_gdn_set_path(int path, int window_chunks);
 
 #ifdef __cplusplus
 }

@@ -161,6 +161,16 @@ def test_gdn_argument_errors(kw, code):
     assert _gdn(lib, **kw) == code
 
 
+def test_gdn_set_path_arguments():
+    lib = gla.load_library()
+    assert lib.gla_gdn_set_path(3, 0) == -2
+    assert lib.gla_gdn_set_path(-1, 0) == -2
+    assert lib.gla_gdn_set_path(2, -1) == -2
+    for path in (1, 2, 0):
+        assert lib.gla_gdn_set_path(path, 5) == 0
+    assert lib.gla_gdn_set_path(0, 0) == 0
+
+
 def test_fp32_chunk_support_table():
     lib = gla.load_library()
     vp = ctypes.c_void_p
