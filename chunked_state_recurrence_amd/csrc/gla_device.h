@@ -146,6 +146,47 @@ __device__ __forceinline__ void dma(rsrc_t r, void *lds, int voff, int soff) {
     if constexpr (SIZE == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 4, voff, soff, 0, 0);
     if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 16, voff, soff, 0, 0);
 }
+// The same direct-to-LDS load issued from inline assembly.  The compiler's
+// wait insertion then does not know about it: it adds no wait before later
+// LDS reads or writes for it (it cannot tell which of them alias the load's
+// target, so for the builtin form it waits for every such load in flight,
+// which stalls a prefetch at the next LDS access).  Every consumer must wait
+// for it explicitly (wait_vmem, then a barrier where other waves read it).
+// The descriptor is passed as its four words (see rsrc_words), the LDS
+// destination as a byte address (lds_addr): lane l's SIZE bytes land at
+// lds + l * SIZE.  The leading s_nop covers the wait states a VMEM read of an
+// SGPR just written by a VALU instruction needs, the second one those of a
+// direct load after an M0 write.
+__device__ __forceinline__ u32x4_t rsrc_words(const void *base, long bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return u32x4_t{uint32_t(a), uint32_t(a >> 32) & 0xffffu, uint32_t(bytes), 0x00020000u};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
+}
+// SALU_OPERANDS = true is for call sites whose SGPR operands are all written
+// by scalar instructions (checked in the generated code): the leading s_nop is
+// then left out.
+template <int SIZE, bool SALU_OPERANDS = false>
+__device__ __forceinline__ void dma_untracked(u32x4_t rs, uint32_t lds, int voff, int soff) {
+    static_assert(SIZE == 4 || SIZE == 16, "direct load size");
+    if constexpr (SALU_OPERANDS) {
+        if constexpr (SIZE == 16)
+            __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                                 :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+        else
+            __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                                 :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+    } else {
+        if constexpr (SIZE == 16)
+            __asm__ __volatile__("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                                 :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+        else
+            __asm__ __volatile__("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                                 :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+    }
+}
+
 // Wait until at most n vector-memory operations of this wave are in flight
 // (operations retire in issue order).  The direct-to-LDS loads have no
 // register results, so the compiler inserts no wait for them by itself.

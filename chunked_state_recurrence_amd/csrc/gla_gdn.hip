@@ -46,14 +46,18 @@ template <int D, int C> struct GdnLayout {
     static constexpr int TD = BF16::tile_bytes(C, PD);
     static constexpr int TQ = C * QP * 2;
     static constexpr int R = TD > TQ ? TD : TQ;      // a region holding either layout
-    // kr: raw k rows, later -W (permuted);  qr: raw q rows, later U (bank-spread);
-    // kg: gamma k, later (gamma_C / gamma) k
-    static constexpr int kr = 0, qr = kr + R, kg = qr + R, qh = kg + TD, vv = qh + TQ;
-    static constexpr int pp = vv + TD;                          // P (bf16, rows i, columns j <= i)
-    static constexpr int tb = pp + BF16::tile_bytes(C, PC);     // T diag(beta) (bf16)
-    static constexpr int aa = tb + BF16::tile_bytes(C, PC);     // A (fp32)
-    static constexpr int tt = aa + C * PF * 4;                  // T (fp32)
-    static constexpr int bytes = tt + C * PF * 4;
+    // Three LDS arrays: the targets of the direct loads that run ahead of their
+    // chunk (the fp32 A / T area, which stages the next chunk's q and k rows,
+    // and the v tile) are kept apart from the tiles in use meanwhile.
+    // main: kr raw k rows, later -W (permuted);  qr raw q rows, later U or W
+    // (bank-spread);  kg gamma k, later (gamma_C / gamma) k;  qh scale gamma q
+    // (permuted);  pp P (bf16, rows i, columns j <= i);  tb T diag(beta) (bf16)
+    static constexpr int kr = 0, qr = kr + R, kg = qr + R, qh = kg + TD, pp = qh + TQ;
+    static constexpr int tb = pp + BF16::tile_bytes(C, PC);
+    static constexpr int main_bytes = tb + BF16::tile_bytes(C, PC);
+    static constexpr int at_bytes = 2 * C * PF * 4;            // A then T (fp32)
+    static constexpr int v_bytes = TD;                          // v rows (bank-spread)
+    static constexpr int bytes = main_bytes + at_bytes + v_bytes;
 };
 
 // Per-chunk record that the prep pass leaves for the walk (device memory,
@@ -116,18 +120,20 @@ gdn_kernel(const GdnParams p) {
     static_assert(C == 64 && NB == 4, "the blocked inverse is written for 64-row chunks");
     static_assert(L::bytes + 2 * C * 4 <= 163840, "LDS");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::main_bytes];
+    __shared__ __attribute__((aligned(16))) unsigned char sAT[L::at_bytes];
+    __shared__ __attribute__((aligned(16))) unsigned char sVV[L::v_bytes];
     __shared__ float sGc[C];     // chunk-local inclusive cumsum of g, log2 units
     __shared__ float sBeta[C];
     unsigned char *tKr = smem + L::kr;   // raw k, row-major (then -W, permuted)
     unsigned char *tQr = smem + L::qr;   // raw q, row-major (then U, bank-spread)
     unsigned char *tKg = smem + L::kg;   // gamma k, then (gamma_C / gamma) k
     __bf16 *tQh = reinterpret_cast<__bf16 *>(smem + L::qh);   // scale gamma q, permuted columns
-    unsigned char *tV = smem + L::vv;
+    unsigned char *tV = sVV;
     unsigned char *tP = smem + L::pp;
     unsigned char *tTb = smem + L::tb;
-    float *tA = reinterpret_cast<float *>(smem + L::aa);
-    float *tT = reinterpret_cast<float *>(smem + L::tt);
+    float *tA = reinterpret_cast<float *>(sAT);
+    float *tT = tA + C * L::PF;
     __bf16 *tW = reinterpret_cast<__bf16 *>(tKr);
 
     const int tid = threadIdx.x;
@@ -146,12 +152,12 @@ gdn_kernel(const GdnParams p) {
     const int vb = (PREP ? 0 : int(blockIdx.y)) * VB + kcb;   // its first value column
     const int r0 = RPW * w;
 
-    const rsrc_t bq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + bh * long(T) * D, long(T) * D * 2);
-    const rsrc_t bk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + bh * long(T) * D, long(T) * D * 2);
-    const rsrc_t bv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + bh * long(T) * D, long(T) * D * 2);
     const rsrc_t bo = make_rsrc(reinterpret_cast<uint16_t *>(p.o) + bh * long(T) * D, long(T) * D * 2);
     const rsrc_t bg = make_rsrc(p.g + bh * long(T), long(T) * 4);
     const rsrc_t bb = make_rsrc(p.beta + bh * long(T), long(T) * 4);
+    const u32x4_t wq = rsrc_words(reinterpret_cast<const uint16_t *>(p.q) + bh * long(T) * D, long(T) * D * 2);
+    const u32x4_t wk = rsrc_words(reinterpret_cast<const uint16_t *>(p.k) + bh * long(T) * D, long(T) * D * 2);
+    const u32x4_t wv = rsrc_words(reinterpret_cast<const uint16_t *>(p.v) + bh * long(T) * D, long(T) * D * 2);
 
     auto rowp = [&](unsigned char *tile, int r, int pitch) {
         return reinterpret_cast<__bf16 *>(tile + E::rowoff(r, pitch));
@@ -160,14 +166,20 @@ gdn_kernel(const GdnParams p) {
     // ---- state ---------------------------------------------------------------
     f32x4_t S[MT][NTW];
     if constexpr (!PREP) {
-        const float *src = p.h0 ? p.h0 + bh * long(D) * D : nullptr;
+        if (p.h0 && vw) {   // one branch around all loads, so they are in flight together
+            const float *src = p.h0 + bh * long(D) * D;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
+                for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    S[mt][nt][e] = src && vw ? src[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] : 0.f;
+                    for (int e = 0; e < 4; ++e) S[mt][nt][e] = src[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16];
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) S[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
     }
     // entries above the diagonal of P and T diag(beta) are never written
     for (int i = tid; i < 2 * E::tile_bytes(C, L::PC) / 4; i += NW * 64) reinterpret_cast<uint32_t *>(tP)[i] = 0u;
@@ -176,7 +188,7 @@ gdn_kernel(const GdnParams p) {
     // tiles (each wave its own rows, 16-byte lanes), v rows into the bank-spread
     // tile, gates of the chunk into wave 0's registers.  Chunk c + 1 is requested
     // while chunk c still works, once those areas are free.
-    unsigned char *stq = smem + L::aa;
+    unsigned char *stq = sAT;
     unsigned char *stk = stq + C * D * 2;
     constexpr int NSL = RPW * D * 2 / 1024;   // 16-byte-lane loads per wave and operand
     static_assert(NSL * 1024 == RPW * D * 2 && 2 * C * D * 2 <= 2 * C * L::PF * 4, "staging");
@@ -187,8 +199,8 @@ gdn_kernel(const GdnParams p) {
         mem_fence_compiler();
 #pragma unroll
         for (int i = 0; i < NSL; ++i) {
-            dma<16>(bq, stq + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
-            dma<16>(bk, stk + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
+            dma_untracked<16>(wq, lds_addr(stq) + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
+            dma_untracked<16>(wk, lds_addr(stk) + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
         }
         mem_fence_compiler();
     };
@@ -198,7 +210,8 @@ gdn_kernel(const GdnParams p) {
         mem_fence_compiler();
 #pragma unroll
         for (int i = 0; i < RPW; ++i)   // 4 bytes per lane: a 64-wide row takes lanes 0..31
-            if (CPL == 2 || lane < 32) dma<4>(bv, tV + E::rowoff(lr0 + i, L::PD), lane * 4, (row0 + i) * D * 2);
+            if (CPL == 2 || lane < 32)
+                dma_untracked<4>(wv, lds_addr(sVV) + E::rowoff(lr0 + i, L::PD), lane * 4, (row0 + i) * D * 2);
         mem_fence_compiler();
         if (w == 0) {
             gx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bg, ((cb + cn) * C + lane) * 4, 0, 0));
@@ -594,33 +607,36 @@ gdn_walk_kernel(const GdnParams p) {
     const int nc = p.nc;
     const int T = p.T;
 
-    const rsrc_t brec = make_rsrc(static_cast<const unsigned char *>(p.ws) + size_t(bh) * nc * R::bytes,
-                                  long(nc) * R::bytes);
-    const rsrc_t bgc = make_rsrc(p.ws_gc + size_t(bh) * nc, long(nc) * 4);
+    const u32x4_t wrec = rsrc_words(static_cast<const unsigned char *>(p.ws) + size_t(bh) * nc * R::bytes,
+                                    long(nc) * R::bytes);
+    const u32x4_t wgc = rsrc_words(p.ws_gc + size_t(bh) * nc, long(nc) * 4);
     const rsrc_t bo = make_rsrc(reinterpret_cast<uint16_t *>(p.o) + bh * long(T) * D, long(T) * D * 2);
 
     f32x4_t S[MT];
-    {
-        const float *src = p.h0 ? p.h0 + bh * long(D) * D : nullptr;
+    if (p.h0) {
+        const float *src = p.h0 + bh * long(D) * D;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[mt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + vb + n16] : 0.f;
+            for (int e = 0; e < 4; ++e) S[mt][e] = src[(16 * mt + 4 * q4 + e) * D + vb + n16];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) S[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
     auto issue = [&](int c) {
-        unsigned char *buf = smem + (c & 1) * BUF;
+        const uint32_t lb = lds_addr(smem) + (c & 1) * BUF;
         const int base = __builtin_amdgcn_readfirstlane(c * R::bytes);
         const int vblk = __builtin_amdgcn_readfirstlane(vb / 16);
         mem_fence_compiler();
 #pragma unroll
-        for (int i = 0; i < NIMG; ++i) dma<16>(brec, buf + i * 1024, lane * 16, base + i * 1024);
+        for (int i = 0; i < NIMG; ++i) dma_untracked<16, true>(wrec, lb + i * 1024, lane * 16, base + i * 1024);
 #pragma unroll
         for (int i = 0; i < NBLK; ++i) {
-            dma<16>(brec, buf + OU + i * 1024, lane * 16, base + R::ut + vblk * R::blk + i * 1024);
-            dma<16>(brec, buf + OO + i * 1024, lane * 16, base + R::ot + vblk * R::blk + i * 1024);
+            dma_untracked<16, true>(wrec, lb + OU + i * 1024, lane * 16, base + R::ut + vblk * R::blk + i * 1024);
+            dma_untracked<16, true>(wrec, lb + OO + i * 1024, lane * 16, base + R::ot + vblk * R::blk + i * 1024);
         }
-        dma<4>(bgc, buf + OG, lane * 4, c * 4);   // gamma_C of chunks c.. (lane 0's is used)
+        dma_untracked<4, true>(wgc, lb + OG, lane * 4, c * 4);   // gamma_C of chunks c.. (lane 0's is used)
         mem_fence_compiler();
     };
 
