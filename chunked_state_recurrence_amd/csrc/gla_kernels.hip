@@ -640,7 +640,7 @@ template <int D, int C> struct StateLayout {
     static constexpr int VP = D * 2 + 32;    // padded bf16 row pitch (bytes) of the v / k~ tiles
     static constexpr int KB = C * D * 2;     // raw key tile, dense rows
     static constexpr int VB = BF16::tile_bytes(C, VP);   // value tile / scaled key tile
-    static constexpr int bytes = 3 * (KB + VB) + VB + NW * D * 4 + D * 4;
+    static constexpr int bytes = 3 * (KB + VB) + VB + NW * D * 4;
     static_assert(bytes <= 163840, "state pass LDS");
 };
 
@@ -668,7 +668,6 @@ state_kernel(const KernelParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char sV0[L::VB], sV1[L::VB], sV2[L::VB];
     __shared__ __attribute__((aligned(16))) unsigned char sKK[L::VB];   // k exp2(Gamma - Gc), rows
     __shared__ __attribute__((aligned(16))) float sBt[NW * D];          // wave totals
-    __shared__ __attribute__((aligned(16))) float sEG[D];               // exp2(Gamma)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -720,6 +719,12 @@ state_kernel(const KernelParams p) {
 #pragma unroll
     for (int u = 0; u < CPL; ++u) seg_gamma[u] = 0.f;
 
+    // Steps c_begin .. c_end - 1 take the unit's chunks last to first:
+    //     E = sum_c diag(exp(gates after chunk c)) (k_c exp(Gamma_c - Gc))^T V_c,
+    // with the decays after the chunk (seg_gamma, log2 units) folded into the
+    // key rows, so the accumulators are never rescaled.  The unit's first
+    // chunks are then the ones read last, which the output pass reads first.
+    auto chunk_of = [&](int c) { return c_end - 1 - (c - c_begin); };
     // one chunk from stage B while the next two chunks load into the others
     auto step = [&](int c, auto bsel) {
         constexpr int B = decltype(bsel)::value;
@@ -750,11 +755,11 @@ state_kernel(const KernelParams p) {
         // last chunk is requested again, so the waits count the same loads)
         {
             constexpr int N2 = (B + 2) % 3;
-            issue(min(c + 2, c_end - 1), N2 == 0 ? rg0 : N2 == 1 ? rg1 : rg2,
+            issue(chunk_of(min(c + 2, c_end - 1)), N2 == 0 ? rg0 : N2 == 1 ? rg1 : rg2,
                   N2 == 0 ? sK0 : N2 == 1 ? sK1 : sK2, N2 == 0 ? sV0 : N2 == 1 ? sV1 : sV2);
         }
 
-        float aw[CPL];   // rows after the wave's
+        float aw[CPL];   // gates after the wave's rows: the rest of the chunk and every later chunk
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
             float after = 0.f, tot = 0.f;
@@ -764,11 +769,10 @@ state_kernel(const KernelParams p) {
                 if (j > w) after += t;
                 tot += t;
             }
-            aw[u] = after;
+            aw[u] = after + seg_gamma[u];
             seg_gamma[u] += tot;
-            if (w == 0) sEG[lane * CPL + u] = fexp2(tot);
         }
-        // k exp2(Gamma - Gc_i): two sums of gates <= 0, rows into the k~ tile
+        // k exp2(gates after row i): sums of gates <= 0, rows into the k~ tile
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             float kk[CPL];
@@ -785,14 +789,6 @@ state_kernel(const KernelParams p) {
         wait_vmem<2 * NCH>();   // this chunk's value rows arrived (after them: chunks c + 1, c + 2)
         block_sync();  // B2: k~ tile, value rows and decays visible
 
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4_t egv = *reinterpret_cast<const f32x4_t *>(sEG + 16 * mt + 4 * q4);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) S[mt][nt][e] *= egv[e];
-        }
         frag_t vf[NTW][TS];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
@@ -809,8 +805,8 @@ state_kernel(const KernelParams p) {
     };
 
     if (c_begin < c_end) {   // prologue: the first two chunks
-        issue(c_begin, rg0, sK0, sV0);
-        issue(min(c_begin + 1, c_end - 1), rg1, sK1, sV1);
+        issue(chunk_of(c_begin), rg0, sK0, sV0);
+        issue(chunk_of(min(c_begin + 1, c_end - 1)), rg1, sK1, sV1);
     }
     // whole rounds of three, then the remainder, so that every path into a
     // step has issued the same loads (the waits stay tight)
