@@ -48,7 +48,7 @@ tokens/s = B / step time; ``roofline`` prices the decode kernel against HBM
 bandwidth with its algorithmic bytes (fp32 state read + written, bf16 q, k,
 v, o and fp32 g per (batch, head) row).
 
-Helpers for the counter runs (used under rocprofv3):
+Helpers for the counter runs (used under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE):
     --copy-calibration  also runs a plain device copy of known size, so
                         FETCH_SIZE / WRITE_SIZE can be scaled to bytes
     --summarize-counters DIR  parses rocprofv3 counter CSVs under DIR and
@@ -63,6 +63,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -153,11 +154,20 @@ def algorithmic_flops(wl, chunk: int) -> int:
     return th * (4 * wl.D * wl.D + (chunk + 1) * 2 * wl.D)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space, so that a change to a
+    comment keeps the counters taken before it."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
+    """Digest of the kernel sources' code (comments and spacing ignored)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -635,7 +645,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU mode; see DESIGN.md for how it would shard)",
+              "(the path has no multi-GPU mode: heads would shard across GPUs with no "
+              "communication, a sequence split would exchange one segment state per GPU)",
               file=sys.stderr)
         sys.exit(2)
 

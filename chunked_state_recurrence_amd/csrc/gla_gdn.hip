@@ -29,6 +29,15 @@
 // MFMA accumulators (the block's value columns are spread 16 per wave over
 // its first waves) and is fed to the S products straight from them (the row
 // operand's columns are permuted in LDS, as in the forward output pass).
+//
+// Two-launch form, for few (batch, head) pairs: the chain of phases above is
+// long and only the state products depend on S, so a prep launch (the same
+// kernel, PREP = true) forms every chunk's state-independent half at once and
+// stores it as a record: -W, Q' = scale gamma q - P W, K^ = (gamma_C / gamma) k,
+// U~ and O0 = P U~ (with bf16 W and U~ as the MFMA operands), and gamma_C.  A
+// walk (gdn_walk_kernel) then carries S through the records:
+//     U = U~ - W S,   o = O0 + Q' S,   S <- gamma_C S + K^T U,
+// the same o as above since q^ S + P (U~ - W S) = (q^ - P W) S + P U~.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

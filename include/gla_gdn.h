@@ -32,7 +32,7 @@
  *                 not involve the state) into a per-chunk record, then a walk
  *                 with one wave per (batch, head, 16 value columns) carries the
  *                 state through the records; used when B*H is small.  The
- *                 records (gdn_record bytes = 117 KiB per chunk and head at
+ *                 records (117 KiB per chunk and head at
  *                 K = 128, 61 KiB at 64) live in the library's cached per-device
  *                 workspace (grown with hipMalloc, freed by gla_release());
  *                 long sequences are processed in windows of at most 1 GiB of
