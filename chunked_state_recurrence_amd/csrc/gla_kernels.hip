@@ -687,11 +687,16 @@ state_kernel(const KernelParams p) {
     const rsrc_t bv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + bh * long(T) * D, long(T) * D * 2);
     constexpr int GD = SG ? 1 : D;   // gates per token (SG: one scalar gate per token)
     const rsrc_t bg = make_rsrc(p.g + bh * long(T) * GD, long(T) * GD * 4);
+    const u32x4_t wk = rsrc_words(reinterpret_cast<const uint16_t *>(p.k) + bh * long(T) * D, long(T) * D * 2);
+    const u32x4_t wv = rsrc_words(reinterpret_cast<const uint16_t *>(p.v) + bh * long(T) * D, long(T) * D * 2);
 
     RawG<CPL> rg0[RPW], rg1[RPW], rg2[RPW];   // gate rows of the three stages
 
     // this wave's gate rows (registers), key and value rows (LDS) of chunk c
     // (rows past T read as zero).  Issue order g, k, v is what the waits count on.
+    // The key and value rows are untracked direct loads (dma_untracked): with
+    // the builtin form the compiler waited for all loads in flight, the next
+    // two chunks' included, before the first transposing read of each step.
     auto issue = [&](int c, RawG<CPL> *tg, unsigned char *tk, unsigned char *tv) {
         const int row0 = __builtin_amdgcn_readfirstlane(c * C + r0);
         const int lr0 = __builtin_amdgcn_readfirstlane(r0);
@@ -703,10 +708,10 @@ state_kernel(const KernelParams p) {
         }
 #pragma unroll
         for (int i = 0; i < NKL; ++i)
-            dma<16>(bk, tk + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
+            dma_untracked<16>(wk, lds_addr(tk) + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
 #pragma unroll
         for (int i = 0; i < NVL; ++i)   // 4 bytes per lane: a 64-wide row takes lanes 0..31
-            if (CPL == 2 || lane < 32) dma<4>(bv, tv + E::rowoff(lr0 + i, L::VP), lane * 4, (row0 + i) * D * 2);
+            if (CPL == 2 || lane < 32) dma_untracked<4>(wv, lds_addr(tv) + E::rowoff(lr0 + i, L::VP), lane * 4, (row0 + i) * D * 2);
         mem_fence_compiler();
     };
 
