@@ -346,8 +346,18 @@ int run_backward(BwdCall &b) {
         p.T = b.T; p.N = N; p.cps = pl.cps; p.P = pl.P; p.ws_slots = pl.P - 1;
         p.bh0 = g0; p.scale = b.scale;
         if (pl.P > 1) {
+            // bf16: the state-pass kernel, pipelined, walking each segment first
+            // chunk first (its last rows are the chunk pass's first); fp32: the
+            // chunk kernel's segment mode
+            gla::KernelParams kp{};
+            kp.k = b.q; kp.v = b.dout; kp.g = b.g;
+            kp.ws_E = p.ws_E; kp.ws_G = p.ws_G;
+            kp.T = b.T; kp.N = N; kp.cps = pl.cps; kp.P = pl.P - 1; kp.ws_slots = pl.P - 1;
+            kp.bh0 = g0; kp.scale = b.scale;
             if (traced(GLA_KERNEL_BWD_SEGMENT, b.stream, [&] {
-                    return gla::launch_bwd(b.dtype, D, b.chunk, false, p, pl.P - 1, nbh, b.stream);
+                    return b.dtype == gla::DTYPE_BF16
+                               ? gla::launch_bwd_segments(D, b.chunk, kp, pl.P - 1, nbh, b.stream)
+                               : gla::launch_bwd(b.dtype, D, b.chunk, false, p, pl.P - 1, nbh, b.stream);
                 }) != hipSuccess)
                 return GLA_ERR_LAUNCH;
             if (traced(GLA_KERNEL_SCAN, b.stream, [&] {

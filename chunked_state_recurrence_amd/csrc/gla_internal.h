@@ -67,6 +67,9 @@ struct GdnParams {
     int nbh;                   // batch x heads
 };
 hipError_t launch_gdn(int D, const GdnParams &p, long nbh, hipStream_t s);
+// the backward's segment pass on the state-pass kernel (bf16; p.k = q, p.v = do,
+// p.ws_slots = segments - 1, grid_x = p.ws_slots)
+hipError_t launch_bwd_segments(int D, int C, const KernelParams &p, int grid_x, int grid_y, hipStream_t s);
 size_t gdn_record_bytes(int D);
 hipError_t launch_gdn_prep(int D, const GdnParams &p, int slices, hipStream_t s);
 hipError_t launch_gdn_walk(int D, const GdnParams &p, hipStream_t s);

@@ -644,7 +644,14 @@ template <int D, int C> struct StateLayout {
     static_assert(bytes <= 163840, "state pass LDS");
 };
 
-template <int D, int C, bool SG>
+// BWD = true: the backward's segment pass with the same machinery.  Fed with
+// k := q, v := do, it forms each segment's contribution to the gradient of
+// the state before the segment, sum_t scale (q_t e^{gates from the segment
+// start through t})^T do_t (rows of the first chunk in the segment first, the
+// prefix decay folded into the q rows), for segments P-1 .. 1 into slots
+// 0 .. P-2 (slot = block x, segment = ws_slots - slot), plus the segment's
+// total log2-decay: what the backward scan takes.
+template <int D, int C, bool SG, bool BWD>
 __global__ void __launch_bounds__((Shape<D, C>::NW * 64))
 state_kernel(const KernelParams p) {
     using E = BF16;
@@ -674,7 +681,9 @@ state_kernel(const KernelParams p) {
     const int w = tid >> 6;
     const int n16 = lane & 15;
     const int q4 = lane >> 4;
-    const int seg = blockIdx.x;
+    static_assert(!(BWD && SG), "the backward takes per-key-dim gates");
+    const int slot = blockIdx.x;
+    const int seg = BWD ? p.ws_slots - slot : slot;
     const long bhl = blockIdx.y;
     const long bh = p.bh0 + bhl;
     const int T = p.T;
@@ -729,7 +738,8 @@ state_kernel(const KernelParams p) {
     // with the decays after the chunk (seg_gamma, log2 units) folded into the
     // key rows, so the accumulators are never rescaled.  The unit's first
     // chunks are then the ones read last, which the output pass reads first.
-    auto chunk_of = [&](int c) { return c_end - 1 - (c - c_begin); };
+    // (BWD: first chunk first, the decay of every earlier chunk folded in)
+    auto chunk_of = [&](int c) { return BWD ? c : c_end - 1 - (c - c_begin); };
     // one chunk from stage B while the next two chunks load into the others
     auto step = [&](int c, auto bsel) {
         constexpr int B = decltype(bsel)::value;
@@ -743,17 +753,26 @@ state_kernel(const KernelParams p) {
 #pragma unroll
         for (int i = 0; i < RPW; ++i)
             rk[i].x = *reinterpret_cast<const decltype(rk[i].x) *>(kt + ((r0 + i) * D + lane * CPL) * 2);
-        // gate sums in log2 units: suffix after each row and total, per wave
+        // gate sums in log2 units, per wave: the suffix after each row (BWD: the
+        // prefix through each row) and the total
         float Sw[RPW][CPL];
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
-            float suf = 0.f;
+            float run = 0.f;
+            if constexpr (BWD) {
 #pragma unroll
-            for (int i = RPW - 1; i >= 0; --i) {
-                Sw[i][u] = suf;
-                suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
+                for (int i = 0; i < RPW; ++i) {
+                    run = __builtin_fmaf(rg[i].get(u), kLog2e, run);
+                    Sw[i][u] = run;
+                }
+            } else {
+#pragma unroll
+                for (int i = RPW - 1; i >= 0; --i) {
+                    Sw[i][u] = run;
+                    run = __builtin_fmaf(rg[i].get(u), kLog2e, run);
+                }
             }
-            sBt[w * D + lane * CPL + u] = suf;
+            sBt[w * D + lane * CPL + u] = run;
         }
         block_sync();  // B1: wave totals visible; every wave is done with chunk c - 1
         // chunk c - 1's stage is free: request chunk c + 2 (near the end the
@@ -764,25 +783,29 @@ state_kernel(const KernelParams p) {
                   N2 == 0 ? sK0 : N2 == 1 ? sK1 : sK2, N2 == 0 ? sV0 : N2 == 1 ? sV1 : sV2);
         }
 
-        float aw[CPL];   // gates after the wave's rows: the rest of the chunk and every later chunk
+        // gates after the wave's rows: the rest of the chunk and every later chunk
+        // (BWD: before them, the earlier waves' rows and every earlier chunk)
+        float aw[CPL];
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
-            float after = 0.f, tot = 0.f;
+            float other = 0.f, tot = 0.f;
 #pragma unroll
             for (int j = 0; j < NW; ++j) {
                 const float t = sBt[j * D + lane * CPL + u];
-                if (j > w) after += t;
+                if (BWD ? j < w : j > w) other += t;
                 tot += t;
             }
-            aw[u] = after + seg_gamma[u];
+            aw[u] = other + seg_gamma[u];
             seg_gamma[u] += tot;
         }
-        // k exp2(gates after row i): sums of gates <= 0, rows into the k~ tile
+        // k exp2(gates after row i) (BWD: scale q exp2(gates through row i)):
+        // sums of gates <= 0, rows into the k~ tile
+        const float rs = BWD ? p.scale : 1.f;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             float kk[CPL];
 #pragma unroll
-            for (int u = 0; u < CPL; ++u) kk[u] = rk[i].get(u) * fexp2(aw[u] + Sw[i][u]);
+            for (int u = 0; u < CPL; ++u) kk[u] = rk[i].get(u) * (rs * fexp2(aw[u] + Sw[i][u]));
             __bf16 *dst = reinterpret_cast<__bf16 *>(sKK + E::rowoff(r0 + i, L::VP)) + lane * CPL;
             if constexpr (CPL == 2) {
                 typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
@@ -825,10 +848,10 @@ state_kernel(const KernelParams p) {
     if (c + 1 < c_end) step(c + 1, std::integral_constant<int, 1>{});
     wait_vmem<0>();   // no direct load may land after the work-group ends
 
-    float *dst = p.ws_E + (bhl * p.ws_slots + seg) * long(D) * D;
+    float *dst = p.ws_E + (bhl * p.ws_slots + slot) * long(D) * D;
     if (w == 0)
 #pragma unroll
-        for (int u = 0; u < CPL; ++u) p.ws_G[(bhl * p.ws_slots + seg) * D + lane * CPL + u] = seg_gamma[u];
+        for (int u = 0; u < CPL; ++u) p.ws_G[(bhl * p.ws_slots + slot) * D + lane * CPL + u] = seg_gamma[u];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -950,11 +973,19 @@ static hipError_t launch_one(const KernelParams &p, int grid_x, int grid_y, hipS
     return hipGetLastError();
 }
 
-template <int D, int C, bool SG>
+template <int D, int C, bool SG, bool BWD = false>
 static hipError_t launch_state(const KernelParams &p, int grid_x, int grid_y, hipStream_t s) {
     if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
-    hipLaunchKernelGGL((state_kernel<D, C, SG>), dim3(grid_x, grid_y), dim3(Shape<D, C>::NW * 64), 0, s, p);
+    hipLaunchKernelGGL((state_kernel<D, C, SG, BWD>), dim3(grid_x, grid_y), dim3(Shape<D, C>::NW * 64), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_bwd_segments(int D, int C, const KernelParams &p, int grid_x, int grid_y, hipStream_t s) {
+    if (D == 128 && C == 64) return launch_state<128, 64, false, true>(p, grid_x, grid_y, s);
+    if (D == 128 && C == 32) return launch_state<128, 32, false, true>(p, grid_x, grid_y, s);
+    if (D == 64 && C == 64) return launch_state<64, 64, false, true>(p, grid_x, grid_y, s);
+    if (D == 64 && C == 32) return launch_state<64, 32, false, true>(p, grid_x, grid_y, s);
+    return hipErrorInvalidValue;
 }
 
 template <typename E, int D, int C>
