@@ -591,8 +591,8 @@ def summarize_counters(outdir: str, wl_name: str):
             name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
             if "chunk_kernel" in name:
                 kind = {"0": "output", "1": "segment"}.get(name.split(",")[3].strip(" >")[:1])
-            elif "state_kernel" in name:
-                kind = "segment"
+            elif "state_kernel" in name:   # 4th template argument: the backward's segment pass
+                kind = "bwd_segment" if name.split(",")[3].strip(" >)(").startswith("true") else "segment"
             elif "scan_kernel" in name:
                 kind = "scan"
             elif "decode_kernel" in name:
