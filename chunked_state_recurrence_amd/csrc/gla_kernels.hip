@@ -626,23 +626,53 @@ chunk_kernel(const KernelParams p) {
 // ---------------------------------------------------------------------------
 // State pass, bf16: the end state of each state unit (a run of chunks) from a
 // zero start, S <- diag(exp2 Gamma) S + (k exp2(Gamma - Gc))^T V per chunk,
-// and the unit's total log2-decay.  Three-stage pipeline, so that two
-// chunks' rows are always on their way from HBM while one is worked on: key
-// and value rows go straight into LDS (three buffers each), gate rows into
-// registers (three sets); chunk c + 2 is requested at the first barrier of
-// chunk c, once every wave is done with chunk c - 1's buffers.
+// and the unit's total log2-decay.  NST-stage pipeline (four stages at
+// D = 128, C = 64, else three), so that NST - 1 chunks' rows are on their way
+// from HBM while one is worked on: key and value rows go straight into LDS
+// (NST buffers each), gate rows into registers (NST sets); chunk c + NST - 1
+// is requested at the first barrier of chunk c, once every wave is done with
+// chunk c - 1's buffers.  The compiler's own wait for the gate registers
+// counts only the register loads, so at the start of a step it also holds
+// for the key and value rows of chunk c + 1: with four stages chunks c + 2
+// and c + 3 stay in flight there.
 // Wave w owns the gate / key rows [r0, r0 + RPW) for the exponent sums and
 // value columns [w*D/NW, (w+1)*D/NW) of S.  The k~^T and V operands of the
 // update are read as MFMA fragments with transposing LDS reads.
 // ---------------------------------------------------------------------------
 template <int D, int C> struct StateLayout {
     static constexpr int NW = Shape<D, C>::NW;
-    static constexpr int VP = D * 2 + 32;    // padded bf16 row pitch (bytes) of the v / k~ tiles
+    static constexpr int VP = D * 2 + 32;    // padded bf16 row pitch (bytes) of the v tiles
     static constexpr int KB = C * D * 2;     // raw key tile, dense rows
-    static constexpr int VB = BF16::tile_bytes(C, VP);   // value tile / scaled key tile
-    static constexpr int bytes = 3 * (KB + VB) + VB + NW * D * 4;
+    static constexpr int VB = BF16::tile_bytes(C, VP);   // value tile
+    // D = 128, C = 64: four stages (three chunks in flight), which fit only
+    // with the scaled key tile in dense swizzled rows (KKB = KB); other shapes
+    // keep three stages and the padded layout for that tile
+    static constexpr bool kFour = D == 128 && C == 64;
+    static constexpr int NST = kFour ? 4 : 3;
+    static constexpr int KKB = kFour ? KB : VB;
+    static constexpr int bytes = NST * (KB + VB) + KKB + NW * D * 4;
     static_assert(bytes <= 163840, "state pass LDS");
 };
+
+// Scaled key tile of the four-stage state pass: dense 256-byte rows (D = 128
+// bf16) whose 8-byte units are permuted by row, unit u of row r stored at
+// u ^ (4 (r % 4) + 16 ((r / 8) % 2)).  A transposing read touches rows
+// k0..k0+3 (k0 a multiple of 4) and four aligned units of each: the XOR
+// with 4 (r % 4) spreads them over 16 distinct units, and rows eight apart
+// (the next 16-lane group) go to the other half of the row's units.
+__device__ __forceinline__ int kk_swz(int r) { return ((r & 3) << 2) | (((r >> 3) & 1) << 4); }
+__device__ __forceinline__ int kk_off(int r, int u) { return r * 256 + ((u ^ kk_swz(r)) << 3); }
+// 8 consecutive tokens (k0 a multiple of 8) of column c0 + (lane % 16) of that tile
+__device__ __forceinline__ bf16x8_t kk_col8(const unsigned char *tile, int k0, int c0, int n16) {
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4_t *lds_s4_p;
+    const int r = k0 + (n16 >> 2), u = (c0 >> 2) + (n16 & 3);
+    const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_p)(tile + kk_off(r, u)));
+    const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_p)(tile + kk_off(r + 4, u)));
+    typedef short s8_t __attribute__((ext_vector_type(8)));
+    const s8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
 
 // BWD = true: the backward's segment pass with the same machinery.  Fed with
 // k := q, v := do, it forms each segment's contribution to the gradient of
@@ -666,14 +696,19 @@ state_kernel(const KernelParams p) {
     constexpr int NKL = RPW * D * 2 / 1024;   // direct loads per wave and chunk: keys
     constexpr int NVL = RPW;                  // values (one per row)
     constexpr int NCH = RPW + NKL + NVL;      // vector-memory operations per wave and chunk
+    constexpr int NST = L::NST;               // pipeline stages (chunks in flight: NST - 1)
     static_assert(RPW * D * 2 % 1024 == 0, "key rows per wave must fill whole loads");
+    // (waits past 63 are clamped, which only waits longer; the four-stage
+    // shape keeps every count exact)
+    static_assert(NST == 3 || NVL + (NST - 1) * NCH <= 63, "four stages: loads in flight must fit the vmcnt counter");
     typedef typename E::frag_t frag_t;
 
     // Separate arrays per buffer: the compiler can then tell that fragment
     // reads of one buffer do not touch the loads landing in another.
-    __shared__ __attribute__((aligned(16))) unsigned char sK0[L::KB], sK1[L::KB], sK2[L::KB];
-    __shared__ __attribute__((aligned(16))) unsigned char sV0[L::VB], sV1[L::VB], sV2[L::VB];
-    __shared__ __attribute__((aligned(16))) unsigned char sKK[L::VB];   // k exp2(Gamma - Gc), rows
+    constexpr int KB3 = NST == 4 ? L::KB : 16, VB3 = NST == 4 ? L::VB : 16;   // fourth stage
+    __shared__ __attribute__((aligned(16))) unsigned char sK0[L::KB], sK1[L::KB], sK2[L::KB], sK3[KB3];
+    __shared__ __attribute__((aligned(16))) unsigned char sV0[L::VB], sV1[L::VB], sV2[L::VB], sV3[VB3];
+    __shared__ __attribute__((aligned(16))) unsigned char sKK[L::KKB];  // k exp2(Gamma - Gc), rows
     __shared__ __attribute__((aligned(16))) float sBt[NW * D];          // wave totals
 
     const int tid = threadIdx.x;
@@ -699,7 +734,7 @@ state_kernel(const KernelParams p) {
     const u32x4_t wk = rsrc_words(reinterpret_cast<const uint16_t *>(p.k) + bh * long(T) * D, long(T) * D * 2);
     const u32x4_t wv = rsrc_words(reinterpret_cast<const uint16_t *>(p.v) + bh * long(T) * D, long(T) * D * 2);
 
-    RawG<CPL> rg0[RPW], rg1[RPW], rg2[RPW];   // gate rows of the three stages
+    RawG<CPL> rg0[RPW], rg1[RPW], rg2[RPW], rg3[NST == 4 ? RPW : 1];   // gate rows per stage
 
     // this wave's gate rows (registers), key and value rows (LDS) of chunk c
     // (rows past T read as zero).  Issue order g, k, v is what the waits count on.
@@ -740,15 +775,30 @@ state_kernel(const KernelParams p) {
     // chunks are then the ones read last, which the output pass reads first.
     // (BWD: first chunk first, the decay of every earlier chunk folded in)
     auto chunk_of = [&](int c) { return BWD ? c : c_end - 1 - (c - c_begin); };
-    // one chunk from stage B while the next two chunks load into the others
-    auto step = [&](int c, auto bsel) {
+    auto stage_g = [&](auto bsel) -> RawG<CPL> * {
         constexpr int B = decltype(bsel)::value;
-        RawG<CPL> *rg = B == 0 ? rg0 : B == 1 ? rg1 : rg2;
-        unsigned char *kt = B == 0 ? sK0 : B == 1 ? sK1 : sK2;
-        unsigned char *vt = B == 0 ? sV0 : B == 1 ? sV1 : sV2;
+        if constexpr (B == 0) return rg0; else if constexpr (B == 1) return rg1;
+        else if constexpr (B == 2) return rg2; else return rg3;
+    };
+    auto stage_k = [&](auto bsel) -> unsigned char * {
+        constexpr int B = decltype(bsel)::value;
+        if constexpr (B == 0) return sK0; else if constexpr (B == 1) return sK1;
+        else if constexpr (B == 2) return sK2; else return sK3;
+    };
+    auto stage_v = [&](auto bsel) -> unsigned char * {
+        constexpr int B = decltype(bsel)::value;
+        if constexpr (B == 0) return sV0; else if constexpr (B == 1) return sV1;
+        else if constexpr (B == 2) return sV2; else return sV3;
+    };
+    // one chunk from stage B while the next NST - 1 chunks load into the others
+    auto step = [&](int c, auto bsel) {
+        RawG<CPL> *rg = stage_g(bsel);
+        unsigned char *kt = stage_k(bsel);
+        unsigned char *vt = stage_v(bsel);
         // this wave's key rows of chunk c arrived (after them: its value rows
-        // and all of chunk c + 1); the gate registers are waited for by the compiler
-        wait_vmem<NVL + NCH>();
+        // and all of chunks c + 1 .. c + NST - 2); the gate registers are
+        // waited for by the compiler
+        wait_vmem<NVL + (NST - 2) * NCH>();
         Raw<E, CPL> rk[RPW];
 #pragma unroll
         for (int i = 0; i < RPW; ++i)
@@ -775,12 +825,12 @@ state_kernel(const KernelParams p) {
             sBt[w * D + lane * CPL + u] = run;
         }
         block_sync();  // B1: wave totals visible; every wave is done with chunk c - 1
-        // chunk c - 1's stage is free: request chunk c + 2 (near the end the
-        // last chunk is requested again, so the waits count the same loads)
+        // chunk c - 1's stage is free: request chunk c + NST - 1 (near the end
+        // the last chunk is requested again, so the waits count the same loads)
         {
-            constexpr int N2 = (B + 2) % 3;
-            issue(chunk_of(min(c + 2, c_end - 1)), N2 == 0 ? rg0 : N2 == 1 ? rg1 : rg2,
-                  N2 == 0 ? sK0 : N2 == 1 ? sK1 : sK2, N2 == 0 ? sV0 : N2 == 1 ? sV1 : sV2);
+            constexpr int N2 = (decltype(bsel)::value + NST - 1) % NST;
+            const auto nsel = std::integral_constant<int, N2>{};
+            issue(chunk_of(min(c + NST - 1, c_end - 1)), stage_g(nsel), stage_k(nsel), stage_v(nsel));
         }
 
         // gates after the wave's rows: the rest of the chunk and every later chunk
@@ -806,7 +856,9 @@ state_kernel(const KernelParams p) {
             float kk[CPL];
 #pragma unroll
             for (int u = 0; u < CPL; ++u) kk[u] = rk[i].get(u) * (rs * fexp2(aw[u] + Sw[i][u]));
-            __bf16 *dst = reinterpret_cast<__bf16 *>(sKK + E::rowoff(r0 + i, L::VP)) + lane * CPL;
+            __bf16 *dst = L::kFour
+                              ? reinterpret_cast<__bf16 *>(sKK + kk_off(r0 + i, lane >> 1) + (lane & 1) * 4)
+                              : reinterpret_cast<__bf16 *>(sKK + E::rowoff(r0 + i, L::VP)) + lane * CPL;
             if constexpr (CPL == 2) {
                 typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
                 *reinterpret_cast<b2_t *>(dst) = b2_t{(__bf16)kk[0], (__bf16)kk[1]};
@@ -814,7 +866,7 @@ state_kernel(const KernelParams p) {
                 dst[0] = (__bf16)kk[0];
             }
         }
-        wait_vmem<2 * NCH>();   // this chunk's value rows arrived (after them: chunks c + 1, c + 2)
+        wait_vmem<(NST - 1) * NCH>();   // this chunk's value rows arrived (after them: chunks c + 1 .. c + NST - 1)
         block_sync();  // B2: k~ tile, value rows and decays visible
 
         frag_t vf[NTW][TS];
@@ -826,26 +878,34 @@ state_kernel(const KernelParams p) {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int ts = 0; ts < TS; ++ts) {
-                const frag_t a = E::ld_col8(sKK, L::VP, ts * 32 + 8 * q4, 16 * mt, n16);
+                const frag_t a = L::kFour ? kk_col8(sKK, ts * 32 + 8 * q4, 16 * mt, n16)
+                                          : E::ld_col8(sKK, L::VP, ts * 32 + 8 * q4, 16 * mt, n16);
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) S[mt][nt] = E::mma(a, vf[nt][ts], S[mt][nt]);
             }
     };
 
-    if (c_begin < c_end) {   // prologue: the first two chunks
+    if (c_begin < c_end) {   // prologue: the first NST - 1 chunks
         issue(chunk_of(c_begin), rg0, sK0, sV0);
         issue(chunk_of(min(c_begin + 1, c_end - 1)), rg1, sK1, sV1);
+        if constexpr (NST == 4) issue(chunk_of(min(c_begin + 2, c_end - 1)), rg2, sK2, sV2);
     }
-    // whole rounds of three, then the remainder, so that every path into a
+    // whole rounds of NST, then the remainder, so that every path into a
     // step has issued the same loads (the waits stay tight)
+    const auto s0 = std::integral_constant<int, 0>{};
+    const auto s1 = std::integral_constant<int, 1>{};
+    const auto s2 = std::integral_constant<int, 2>{};
+    const auto s3 = std::integral_constant<int, NST == 4 ? 3 : 0>{};
     int c = c_begin;
-    for (; c + 3 <= c_end; c += 3) {
-        step(c, std::integral_constant<int, 0>{});
-        step(c + 1, std::integral_constant<int, 1>{});
-        step(c + 2, std::integral_constant<int, 2>{});
+    for (; c + NST <= c_end; c += NST) {
+        step(c, s0);
+        step(c + 1, s1);
+        step(c + 2, s2);
+        if constexpr (NST == 4) step(c + 3, s3);
     }
-    if (c < c_end) step(c, std::integral_constant<int, 0>{});
-    if (c + 1 < c_end) step(c + 1, std::integral_constant<int, 1>{});
+    if (c < c_end) step(c, s0);
+    if (c + 1 < c_end) step(c + 1, s1);
+    if constexpr (NST == 4) if (c + 2 < c_end) step(c + 2, s2);
     wait_vmem<0>();   // no direct load may land after the work-group ends
 
     float *dst = p.ws_E + (bhl * p.ws_slots + slot) * long(D) * D;
