@@ -312,20 +312,29 @@ chunk_kernel(const KernelParams p) {
         if constexpr (!kCumsum) load_g(cn);
         block_sync();  // B1: wave totals visible
 
-        float rw[CPL], aw[CPL], gam[CPL];   // rows before the wave's, after, all
+        // rows before the wave's, after them, all: before and all from one
+        // running sum over the wave totals (the same additions in the same
+        // order as separate sums); after, a sum of its own, is formed only
+        // where it is used (the state-only pass here, the exact path below)
+        float rw[CPL], aw[CPL], gam[CPL];
+        auto rows_after = [&](int u) {
+            float after = 0.f;
+#pragma unroll
+            for (int j = 0; j < NW; ++j)
+                if (j > w) after += sBtot[(buf * NW + j) * D + lane * CPL + u];
+            return after;
+        };
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
-            float before = 0.f, after = 0.f, tot = 0.f;
+            float pre = 0.f, before = 0.f;
 #pragma unroll
             for (int j = 0; j < NW; ++j) {
-                const float b = sBtot[(buf * NW + j) * D + lane * CPL + u];
-                if (j < w) before += b;
-                if (j > w) after += b;
-                tot += b;
+                if (j == w) before = pre;
+                pre += sBtot[(buf * NW + j) * D + lane * CPL + u];
             }
             rw[u] = before;
-            aw[u] = after;
-            gam[u] = tot;
+            gam[u] = pre;
+            if constexpr (!kScores) aw[u] = rows_after(u);
         }
 
         if constexpr (kCumsum) {
@@ -376,6 +385,8 @@ chunk_kernel(const KernelParams p) {
                     store_row(sKt, r0 + i, kt);
                 }
             } else {
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) aw[u] = rows_after(u);
 #pragma unroll
                 for (int u = 0; u < CPL; ++u) {
                     float suf = aw[u];   // rows after i within the chunk: exponent <= 0
