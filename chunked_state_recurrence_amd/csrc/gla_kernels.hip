@@ -642,10 +642,14 @@ chunk_kernel(const KernelParams p) {
 // from HBM while one is worked on: key and value rows go straight into LDS
 // (NST buffers each), gate rows into registers (NST sets); chunk c + NST - 1
 // is requested at the first barrier of chunk c, once every wave is done with
-// chunk c - 1's buffers.  The compiler's own wait for the gate registers
-// counts only the register loads, so at the start of a step it also holds
-// for the key and value rows of chunk c + 1: with four stages chunks c + 2
-// and c + 3 stay in flight there.
+// chunk c - 1's buffers.  The compiler adds its own wait for the gate
+// registers at the start of a step, counting the loads it knows were issued
+// after them.  Four stages issue the key and value rows with the builtin
+// direct loads, which it counts, so that wait holds only for chunk c (chunks
+// c + 1 and c + 2 stay in flight); no wait is added before the transposing
+// reads, since every stage buffer is an array of its own named at compile
+// time.  Three stages issue them untracked (below), and the compiler's wait,
+// blind to them, then also holds for chunk c + 1's rows.
 // Wave w owns the gate / key rows [r0, r0 + RPW) for the exponent sums and
 // value columns [w*D/NW, (w+1)*D/NW) of S.  The k~^T and V operands of the
 // update are read as MFMA fragments with transposing LDS reads.
@@ -749,9 +753,10 @@ state_kernel(const KernelParams p) {
 
     // this wave's gate rows (registers), key and value rows (LDS) of chunk c
     // (rows past T read as zero).  Issue order g, k, v is what the waits count on.
-    // The key and value rows are untracked direct loads (dma_untracked): with
-    // the builtin form the compiler waited for all loads in flight, the next
-    // two chunks' included, before the first transposing read of each step.
+    // Three stages: the key and value rows are untracked direct loads
+    // (dma_untracked): with the builtin form and the stage buffers picked at
+    // run time the compiler waited for all loads in flight, the next two
+    // chunks' included, before the first transposing read of each step.
     auto issue = [&](int c, RawG<CPL> *tg, unsigned char *tk, unsigned char *tv) {
         const int row0 = __builtin_amdgcn_readfirstlane(c * C + r0);
         const int lr0 = __builtin_amdgcn_readfirstlane(r0);
@@ -761,12 +766,19 @@ state_kernel(const KernelParams p) {
             if constexpr (SG) tg[i].load_one(bg, row0 * 4, i * 4);   // same address in every lane
             else tg[i].load(bg, (row0 * D + lane * CPL) * 4, i * D * 4);
         }
+        if constexpr (L::kFour) {   // tracked: the compiler's own waits then count them
 #pragma unroll
-        for (int i = 0; i < NKL; ++i)
-            dma_untracked<16>(wk, lds_addr(tk) + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
+            for (int i = 0; i < NKL; ++i) dma<16>(bk, tk + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
 #pragma unroll
-        for (int i = 0; i < NVL; ++i)   // 4 bytes per lane: a 64-wide row takes lanes 0..31
-            if (CPL == 2 || lane < 32) dma_untracked<4>(wv, lds_addr(tv) + E::rowoff(lr0 + i, L::VP), lane * 4, (row0 + i) * D * 2);
+            for (int i = 0; i < NVL; ++i) dma<4>(bv, tv + E::rowoff(lr0 + i, L::VP), lane * 4, (row0 + i) * D * 2);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NKL; ++i)
+                dma_untracked<16>(wk, lds_addr(tk) + lr0 * D * 2 + i * 1024, lane * 16, row0 * D * 2 + i * 1024);
+#pragma unroll
+            for (int i = 0; i < NVL; ++i)   // 4 bytes per lane: a 64-wide row takes lanes 0..31
+                if (CPL == 2 || lane < 32) dma_untracked<4>(wv, lds_addr(tv) + E::rowoff(lr0 + i, L::VP), lane * 4, (row0 + i) * D * 2);
+        }
         mem_fence_compiler();
     };
 
@@ -914,9 +926,15 @@ state_kernel(const KernelParams p) {
         step(c + 2, s2);
         if constexpr (NST == 4) step(c + 3, s3);
     }
-    if (c < c_end) step(c, s0);
-    if (c + 1 < c_end) step(c + 1, s1);
-    if constexpr (NST == 4) if (c + 2 < c_end) step(c + 2, s2);
+    // nested, so that each remainder step is reached only through the one
+    // before it (the compiler's wait counts then see every load issued)
+    if (c < c_end) {
+        step(c, s0);
+        if (c + 1 < c_end) {
+            step(c + 1, s1);
+            if constexpr (NST == 4) if (c + 2 < c_end) step(c + 2, s2);
+        }
+    }
     wait_vmem<0>();   // no direct load may land after the work-group ends
 
     float *dst = p.ws_E + (bhl * p.ws_slots + slot) * long(D) * D;
