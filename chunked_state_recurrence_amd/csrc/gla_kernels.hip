@@ -39,16 +39,20 @@
 
 namespace gla {
 
-// LDS carve-up (bytes) per mode; pitches pad rows by 16 bytes against bank
-// conflicts.  Only the tiles a mode uses are allocated, so the state-only
-// pass fits several work-groups per CU.
+// LDS carve-up (bytes) per mode; pitches pad rows against bank conflicts.
+// bf16 rows are padded by 32 bytes: the MFMA fragment reads (16 rows of a
+// tile, four 16-byte groups per row, one group per quarter-wave) then run
+// without conflicts on gfx950 (measured with an LDS probe: a 16-byte pad
+// costs every 16-byte read a second pass).  Only the tiles a mode uses are
+// allocated, so the state-only pass fits several work-groups per CU.
 template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int es = sizeof(typename E::lds_t);
     static constexpr int NW = Shape<D, C>::NW;
     static constexpr bool scores = MODE == MODE_OUT || MODE == MODE_INTRA;
     static constexpr bool state = MODE == MODE_OUT || MODE == MODE_SEG;
-    static constexpr int QP = D + 16 / es;   // Qh / Kt row pitch (elements)
-    static constexpr int TP = C + 16 / es;   // Kht / Vt / A row pitch (elements)
+    static constexpr int PAD = es == 2 ? 32 : 16;   // row pad (bytes)
+    static constexpr int QP = D + PAD / es;  // Qh / Kt row pitch (elements)
+    static constexpr int TP = C + PAD / es;  // Kht / Vt / A row pitch (elements)
     static constexpr int DP = D + 4;         // decay tile row pitch (floats)
     // output pass: v rows staged row-major by direct loads; bf16 rows padded
     // by 32 bytes so the transposing fragment reads hit distinct banks
