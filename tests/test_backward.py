@@ -128,6 +128,18 @@ def test_bf16_segment_splits(target):
     check(x, gr, gpu_bwd(x, gr), TOL_BF16)
 
 
+@pytest.mark.parametrize("T", [576, 1100, 1343])
+def test_bf16_segment_unit_lengths(T):
+    """Segments of 3, 6 and 7 chunks (three per head): every remainder after
+    the segment pass's rounds of four chunks."""
+    say(f"[bwd segment lengths] T={T}")
+    wl = _wl("bf16", 128)
+    x = make_inputs(wl, B=1, H=2, T=T, seed=T + 7, h0_std=0.3)
+    gr = make_grad_inputs(wl, B=1, H=2, T=T, seed=T + 7)
+    gla.set_tuning(6, 0)
+    check(x, gr, gpu_bwd(x, gr), TOL_BF16)
+
+
 @pytest.mark.parametrize("gate", ["const:-30", "const:-10000", "ls41", "mixed"])
 def test_bf16_extreme_gates(gate):
     """Chunks past the span guard take the exact elementwise path."""

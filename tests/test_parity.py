@@ -140,6 +140,25 @@ def test_bf16_segment_splits(target):
     check(x, wl.scale, o, hf, TOL_BF16)
 
 
+# (T, chunks per state unit) at B=1, H=2 and a target of 6 work-groups (three
+# segments per head): the D = 128, C = 64 state pass runs its chunks in
+# rounds of four, then 1..3 remainder steps; these lengths give every
+# remainder, with and without a ragged last chunk
+UNIT_LENGTHS = [(384, 2), (576, 3), (960, 5), (1100, 6), (1343, 7), (1344, 7)]
+
+
+@pytest.mark.parametrize("T,cps", UNIT_LENGTHS, ids=[f"T{t}-cps{c}" for t, c in UNIT_LENGTHS])
+def test_bf16_state_unit_lengths(T, cps):
+    wl = WORKLOADS["prefill_4k"]
+    n = math.ceil(T / 64)
+    assert math.ceil(n / 3) == cps   # three segments of cps chunks (the last one shorter)
+    x = make_inputs(wl, B=1, H=2, T=T, seed=T, h0_std=0.3)
+    say(f"[state unit lengths] T={T} chunks per unit={cps}")
+    gla.set_tuning(6, 0)
+    o, hf = gpu_run(x)
+    check(x, wl.scale, o, hf, TOL_BF16)
+
+
 def test_bf16_head_groups():
     wl = WORKLOADS["prefill_4k"]
     x = make_inputs(wl, B=2, H=3, T=500, seed=6, h0_std=0.3)
