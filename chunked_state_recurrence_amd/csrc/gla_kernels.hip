@@ -650,10 +650,10 @@ chunk_kernel(const KernelParams p) {
 // registers at the start of a step, counting the loads it knows were issued
 // after them.  Four stages issue the key and value rows with the builtin
 // direct loads, which it counts, so that wait holds only for chunk c (chunks
-// c + 1 and c + 2 stay in flight); no wait is added before the transposing
-// reads, since every stage buffer is an array of its own named at compile
-// time.  Three stages issue them untracked (below), and the compiler's wait,
-// blind to them, then also holds for chunk c + 1's rows.
+// c + 1 and c + 2 stay in flight; in the generated code it is vmcnt(46), and
+// no other wait precedes the transposing reads).  Three stages issue them
+// untracked (below), and the compiler's wait, blind to them, then also holds
+// for chunk c + 1's rows.
 // Wave w owns the gate / key rows [r0, r0 + RPW) for the exponent sums and
 // value columns [w*D/NW, (w+1)*D/NW) of S.  The k~^T and V operands of the
 // update are read as MFMA fragments with transposing LDS reads.
@@ -758,9 +758,9 @@ state_kernel(const KernelParams p) {
     // this wave's gate rows (registers), key and value rows (LDS) of chunk c
     // (rows past T read as zero).  Issue order g, k, v is what the waits count on.
     // Three stages: the key and value rows are untracked direct loads
-    // (dma_untracked): with the builtin form and the stage buffers picked at
-    // run time the compiler waited for all loads in flight, the next two
-    // chunks' included, before the first transposing read of each step.
+    // (dma_untracked): an earlier three-stage build with the builtin form had
+    // the compiler wait for all loads in flight, the next two chunks'
+    // included, before the first transposing read of each step.
     auto issue = [&](int c, RawG<CPL> *tg, unsigned char *tk, unsigned char *tv) {
         const int row0 = __builtin_amdgcn_readfirstlane(c * C + r0);
         const int lr0 = __builtin_amdgcn_readfirstlane(r0);
