@@ -496,18 +496,51 @@ chunk_kernel(const KernelParams p) {
                         for (int x = 0; x < RPW; ++x)
                             if (x == il) qi[u] = qx[x][u];
                     }
-                    for (int j = i; j >= 0; --j) {
-                        float part = 0.f;
+                    // columns j = i, i-1, .. in groups of 8: the 8 cross-lane sums of
+                    // a group are independent and run interleaved (one at a time,
+                    // each waited for the previous one's shuffle chain)
+                    for (int jb = i; jb >= 0; jb -= 8) {
+                        float part[8];
 #pragma unroll
-                        for (int u = 0; u < CPL; ++u) {
-                            const int col = lane * CPL + u;
-                            part += qi[u] * E::l2f(sKt[j * L::QP + col]) * pr[u];
-                            pr[u] *= sDec[j * L::DP + col];   // exp(g_j + ... + g_i) for j-1
+                        for (int t = 0; t < 8; ++t) {
+                            const int j = jb - t;
+                            const bool ok = j >= 0;
+                            const int jj = ok ? j : 0;
+                            float pt = 0.f;
+#pragma unroll
+                            for (int u = 0; u < CPL; ++u) {
+                                const int col = lane * CPL + u;
+                                pt += qi[u] * E::l2f(sKt[jj * L::QP + col]) * pr[u];
+                                pr[u] *= ok ? sDec[jj * L::DP + col] : 1.f;   // exp(g_j + ... + g_i) for j-1
+                            }
+                            part[t] = ok ? pt : 0.f;
                         }
-                        const float s = wave_sum(part) * p.scale;
+#pragma unroll
+                        for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) part[t] += __shfl_xor(part[t], m, 64);
                         if (lane == 0) {
-                            if constexpr (kOut) sA[i * L::TP + j] = E::f2l(s);
-                            else p.dump[((bh * long(p.N) + c) * C + i) * C + j] = s;
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) {
+                                const int j = jb - t;
+                                if (j < 0) break;
+                                const float sc = part[t] * p.scale;
+                                if constexpr (kOut) sA[i * L::TP + j] = E::f2l(sc);
+                                else p.dump[((bh * long(p.N) + c) * C + i) * C + j] = sc;
+                            }
+                        }
+                        // once every running product has underflowed to 0, every
+                        // further term is exactly 0 (decay factors are finite and
+                        // <= 1): write the remaining columns and stop
+                        bool live = false;
+#pragma unroll
+                        for (int u = 0; u < CPL; ++u) live |= pr[u] != 0.f;
+                        if (__ballot(live) == 0) {
+                            for (int j = jb - 8 - lane; j >= 0; j -= 64) {
+                                if constexpr (kOut) sA[i * L::TP + j] = E::f2l(0.f);
+                                else p.dump[((bh * long(p.N) + c) * C + i) * C + j] = 0.f;
+                            }
+                            break;
                         }
                     }
                     if constexpr (kIntra) {
