@@ -183,6 +183,24 @@ def test_bf16_extreme_gates(gate):
     check(x, wl.scale, o, hf, TOL_BF16)
 
 
+@pytest.mark.parametrize("gate", ["const:-30", "const:-10000", "mixed"])
+def test_bf16_extreme_gates_full_size(gate):
+    """The prefill_16k shape (B=1, H=16, T=16K) with every chunk on the exact
+    path: sampled heads over their whole sequence against the oracle, every
+    output finite."""
+    wl = WORKLOADS["prefill_16k"]
+    say(f"[extreme gates, full size] {gate}")
+    if gate == "mixed":
+        x = make_inputs(wl, seed=18, h0_std=0.3)
+        gen = torch.Generator().manual_seed(19)
+        spikes = torch.rand(x["g"].shape, generator=gen) < 0.01
+        x["g"] = torch.where(spikes, torch.full_like(x["g"], -200.0), x["g"])
+    else:
+        x = make_inputs(wl, seed=18, gate=gate, h0_std=0.3)
+    o, hf = gpu_run(x)
+    check(x, wl.scale, o, hf, TOL_BF16, heads=[(0, 2), (0, 13)])
+
+
 def test_bf16_chunk_invariance():
     wl = WORKLOADS["prefill_4k"]
     x = make_inputs(wl, B=1, H=2, T=640, seed=10, h0_std=0.2)
