@@ -1,0 +1,62 @@
+"""Host logic of bench.py (CPU only): the counter summary's kernel
+classification and copy calibration, from a synthetic rocprofv3 counter CSV."""
+
+import csv
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+          "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+          "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+          "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, ctr, val) in enumerate(rows):
+            r = {k: 0 for k in FIELDS}
+            r.update(Dispatch_Id=i + 1, Kernel_Name=name, Counter_Name=ctr, Counter_Value=val)
+            w.writerow(r)
+
+
+def test_summarize_counters_classifies_kernels(tmp_path, monkeypatch):
+    names = {
+        "void gla::state_kernel<128, 64, false, false>(gla::KernelParams)": "segment",
+        "void gla::state_kernel<128, 64, false, true>(gla::KernelParams)": "bwd_segment",
+        "gla::scan_kernel(float*, float const*, float const*, long, int, int, int)": "scan",
+        "void gla::chunk_kernel<gla::BF16, 128, 64, 0, false>(gla::KernelParams)": "output",
+        "void gla::bwd_kernel<gla::BF16, 128, 64, 1>(gla::BwdParams)": "bwd",
+    }
+    rows = []
+    for k, (name, _) in enumerate(names.items()):
+        rows.append((name, "FETCH_SIZE", 1000.0 * (k + 1)))
+    # the calibration copy comes after the last chunk kernel: 1 GiB read counted as 512 MiB
+    rows.append(("__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288.0))
+    d = tmp_path / "fetch"
+    d.mkdir()
+    _write(d / "x_counter_collection.csv", rows)
+    w = tmp_path / "write"
+    w.mkdir()
+    _write(w / "x_counter_collection.csv",
+           [(n, "WRITE_SIZE", 10.0) for n in names] + [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0)])
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    bench.summarize_counters(str(tmp_path), "unit_test")
+    out = json.loads((prof / "counters_unit_test.json").read_text())
+    med = out["median_per_dispatch_KiB"]
+    for k, (_, kind) in enumerate(names.items()):
+        assert med[f"{kind}:FETCH_SIZE"] == 1000.0 * (k + 1)
+        assert med[f"{kind}:WRITE_SIZE"] == 10.0
+    assert abs(out["fetch_factor"] - 2.0) < 1e-12
+    assert abs(out["write_factor"] - 1.0) < 1e-12
+    assert out["source_digest"] == bench.source_digest()
