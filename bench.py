@@ -730,14 +730,17 @@ def main():
     by_kind = {}
     for kind, kms in kernels:
         by_kind.setdefault(kind, []).append(kms)
-    out_ms = statistics.mean(by_kind["output"])
+    # the output pass's device time per step: with head groups (--head-group)
+    # a step launches it once per group, each launch covering part of the heads
+    out_launches = len(by_kind["output"]) / args.steps
+    out_ms = sum(by_kind["output"]) / args.steps
     bytes_alg = algorithmic_bytes(wl)
     achieved = bytes_alg / (out_ms * 1e-3) / 1e9
     flops = algorithmic_flops(wl, chunk)
 
     traffic = None
     c = read_counters(args.workload)
-    if c and "fetch_factor" in c:
+    if c and "fetch_factor" in c and out_launches == 1:   # counters are taken per launch
         m = c["median_per_dispatch_KiB"]
         f, w = m.get("output:FETCH_SIZE"), m.get("output:WRITE_SIZE")
         if f is not None and w is not None:
