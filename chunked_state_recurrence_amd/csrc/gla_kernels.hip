@@ -515,16 +515,39 @@ chunk_kernel(const KernelParams p) {
                             }
                             part[t] = ok ? pt : 0.f;
                         }
+                        // the 8 sums over the 64 lanes as one transposing butterfly:
+                        // at the xor-32, -16 and -8 steps each lane keeps the half of
+                        // its values its lane bit selects and adds the partner's copy
+                        // of them (the same pairs a plain butterfly adds, so the same
+                        // result), then three ordinary steps; lane bits 3..5 then name
+                        // the column t a lane holds
+                        const int h5 = (lane >> 5) & 1, h4 = (lane >> 4) & 1, h3 = (lane >> 3) & 1;
+                        float r4[4], r2[2];
 #pragma unroll
-                        for (int m = 32; m >= 1; m >>= 1)
+                        for (int k2 = 0; k2 < 4; ++k2) {
+                            const float keep = h5 ? part[k2 + 4] : part[k2];
+                            const float send = h5 ? part[k2] : part[k2 + 4];
+                            r4[k2] = keep + __shfl_xor(send, 32, 64);
+                        }
 #pragma unroll
-                            for (int t = 0; t < 8; ++t) part[t] += __shfl_xor(part[t], m, 64);
-                        if (lane == 0) {
+                        for (int k2 = 0; k2 < 2; ++k2) {
+                            const float keep = h4 ? r4[k2 + 2] : r4[k2];
+                            const float send = h4 ? r4[k2] : r4[k2 + 2];
+                            r2[k2] = keep + __shfl_xor(send, 16, 64);
+                        }
+                        float sum;
+                        {
+                            const float keep = h3 ? r2[1] : r2[0];
+                            const float send = h3 ? r2[0] : r2[1];
+                            sum = keep + __shfl_xor(send, 8, 64);
+                        }
 #pragma unroll
-                            for (int t = 0; t < 8; ++t) {
-                                const int j = jb - t;
-                                if (j < 0) break;
-                                const float sc = part[t] * p.scale;
+                        for (int m = 4; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+                        {
+                            const int t = h3 + 2 * h4 + 4 * h5;   // (lane >> 3) & 7
+                            const int j = jb - t;
+                            if ((lane & 7) == 0 && j >= 0) {
+                                const float sc = sum * p.scale;
                                 if constexpr (kOut) sA[i * L::TP + j] = E::f2l(sc);
                                 else p.dump[((bh * long(p.N) + c) * C + i) * C + j] = sc;
                             }
