@@ -53,6 +53,9 @@ Helpers for the counter runs (used under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
                         FETCH_SIZE / WRITE_SIZE can be scaled to bytes
     --summarize-counters DIR  parses rocprofv3 counter CSVs under DIR and
                         writes profiles/counters_<workload>.json
+    --summarize-mfma DIR [DIR ...]  prints per-pass MFMA instruction counts, busy
+                        fraction and bf16 / fp32 MFMA rates from rocprofv3
+                        counter CSVs under the DIRs
 """
 
 from __future__ import annotations
@@ -571,6 +574,25 @@ def read_counters(wl_name: str):
     return c
 
 
+def kernel_kind(name: str):
+    """The pass a kernel name in a rocprofv3 trace belongs to (None: not ours)."""
+    if "chunk_kernel" in name:
+        return {"0": "output", "1": "segment"}.get(name.split(",")[3].strip(" >")[:1])
+    if "state_kernel" in name:   # 4th template argument: the backward's segment pass
+        return "bwd_segment" if name.split(",")[3].strip(" >)(").startswith("true") else "segment"
+    if "scan_kernel" in name:
+        return "scan"
+    if "decode_kernel" in name:
+        return "decode"
+    if "gdn_walk_kernel" in name:
+        return "gdn_walk"
+    if "gdn_kernel" in name:
+        return "gdn_prep" if "true" in name else "gdn"
+    if "bwd_kernel" in name:
+        return "bwd" if name.split(",")[3].strip(" >)(")[:1] == "1" else "bwd_segment"
+    return None
+
+
 def summarize_counters(outdir: str, wl_name: str):
     """Parse rocprofv3 counter-collection CSVs (one pass for FETCH_SIZE, one
     for WRITE_SIZE, each run with --copy-calibration) and write
@@ -589,24 +611,9 @@ def summarize_counters(outdir: str, wl_name: str):
                          default=-1)
         for r in rows:
             name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
-            if "chunk_kernel" in name:
-                kind = {"0": "output", "1": "segment"}.get(name.split(",")[3].strip(" >")[:1])
-            elif "state_kernel" in name:   # 4th template argument: the backward's segment pass
-                kind = "bwd_segment" if name.split(",")[3].strip(" >)(").startswith("true") else "segment"
-            elif "scan_kernel" in name:
-                kind = "scan"
-            elif "decode_kernel" in name:
-                kind = "decode"
-            elif "gdn_walk_kernel" in name:
-                kind = "gdn_walk"
-            elif "gdn_kernel" in name:
-                kind = "gdn_prep" if "true" in name else "gdn"
-            elif "bwd_kernel" in name:
-                kind = "bwd" if name.split(",")[3].strip(" >)(")[:1] == "1" else "bwd_segment"
-            elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_chunk:
+            kind = kernel_kind(name)
+            if kind is None and "copyBuffer" in name and int(r["Dispatch_Id"]) > last_chunk:
                 kind = "copy"
-            else:
-                kind = None
             if kind:
                 per_counter.setdefault((kind, ctr), []).append(val)
     if not per_counter:
@@ -624,6 +631,57 @@ def summarize_counters(outdir: str, wl_name: str):
     print(json.dumps(out, indent=1))
 
 
+# dense MFMA peaks of MI355X (TFLOP/s) and its SIMD count
+MFMA_PEAK = {"bf16": 2500.0, "fp32": 157.3}
+SIMDS = 1024
+
+
+def summarize_mfma(outdirs):
+    """Per-kernel MFMA figures from rocprofv3 counter CSVs under DIR (medians
+    over dispatches), printed as a markdown table.  Expects a pass with
+    SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE and a pass with
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 (one MOPS unit
+    is 512 flops).  MFMA busy = busy cycles summed over SIMDs / (SIMDs x GPU
+    active cycles, GRBM_GUI_ACTIVE summed over the 8 XCDs / 8); rates use
+    each dispatch's own duration under counter collection."""
+    import csv
+    vals, durs = {}, {}
+    paths = [p for d in outdirs
+             for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)]
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                kind = kernel_kind(r["Kernel_Name"])
+                if kind is None:
+                    continue
+                vals.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+                durs.setdefault(kind, {})[(p, r["Dispatch_Id"])] = d
+    if not vals:
+        raise SystemExit(f"no counter rows under {outdirs}")
+    med = {k: statistics.median(v) for k, v in vals.items()}
+    print("| pass | dispatch us | MFMA instructions | busy cycles each | MFMA busy | "
+          "bf16 TFLOP/s (of 2500) | fp32 TFLOP/s (of 157.3) |")
+    print("|---|---|---|---|---|---|---|")
+    out = {}
+    for kind in sorted(durs):
+        d = statistics.median(durs[kind].values())
+        g = lambda c: med.get((kind, c))
+        ins, busy, gui = g("SQ_INSTS_MFMA"), g("SQ_VALU_MFMA_BUSY_CYCLES"), g("GRBM_GUI_ACTIVE")
+        util = busy / (SIMDS * gui / 8) if busy is not None and gui else None
+        rate = {}
+        for dt, c in (("bf16", "SQ_INSTS_VALU_MFMA_MOPS_BF16"), ("fp32", "SQ_INSTS_VALU_MFMA_MOPS_F32")):
+            if g(c) is not None:
+                rate[dt] = g(c) * 512 / d / 1e12
+        out[kind] = {"dispatch_us": d * 1e6, "insts": ins, "busy": busy, "util": util, **rate}
+        f = lambda x, s: "—" if x is None else s.format(x)
+        fr = lambda dt: "—" if dt not in rate else f"{rate[dt]:.1f} ({rate[dt] / MFMA_PEAK[dt]:.3f})"
+        print(f"| {kind} | {d * 1e6:.1f} | {f(ins, '{:.0f}')} | "
+              f"{f(busy / ins if busy is not None and ins else None, '{:.1f}')} | "
+              f"{f(util, '{:.3f}')} | {fr('bf16')} | {fr('fp32')} |")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -636,9 +694,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--summarize-mfma", metavar="DIR", nargs="+")
     ap.add_argument("--backward", action="store_true", help="time gla_bwd on the workload")
     args = ap.parse_args()
 
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters,
                            args.workload + ("_bwd" if args.backward else ""))

@@ -1,5 +1,6 @@
 """Host logic of bench.py (CPU only): the counter summary's kernel
-classification and copy calibration, from a synthetic rocprofv3 counter CSV."""
+classification and copy calibration, and the MFMA summary's arithmetic, from
+synthetic rocprofv3 counter CSVs."""
 
 import csv
 import json
@@ -18,13 +19,14 @@ FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id",
           "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 
 
-def _write(path, rows):
+def _write(path, rows, dur_ns=0):
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=FIELDS)
         w.writeheader()
         for i, (name, ctr, val) in enumerate(rows):
             r = {k: 0 for k in FIELDS}
-            r.update(Dispatch_Id=i + 1, Kernel_Name=name, Counter_Name=ctr, Counter_Value=val)
+            r.update(Dispatch_Id=i + 1, Kernel_Name=name, Counter_Name=ctr, Counter_Value=val,
+                     Start_Timestamp=1000 * i, End_Timestamp=1000 * i + dur_ns)
             w.writerow(r)
 
 
@@ -60,3 +62,27 @@ def test_summarize_counters_classifies_kernels(tmp_path, monkeypatch):
     assert abs(out["fetch_factor"] - 2.0) < 1e-12
     assert abs(out["write_factor"] - 1.0) < 1e-12
     assert out["source_digest"] == bench.source_digest()
+
+
+def test_summarize_mfma_arithmetic(tmp_path):
+    out_pass = "void gla::chunk_kernel<gla::BF16, 128, 64, 0, false>(gla::KernelParams)"
+    # 1e6 bf16 16x16x32 MFMAs (16384 flops = 32 MOPS units each) in 100 us on
+    # a GPU active for 240000 cycles per XCD, 16 busy cycles per instruction
+    a = tmp_path / "busy"
+    a.mkdir()
+    _write(a / "a_counter_collection.csv",
+           [(out_pass, "SQ_INSTS_MFMA", 1e6), (out_pass, "SQ_VALU_MFMA_BUSY_CYCLES", 16e6),
+            (out_pass, "GRBM_GUI_ACTIVE", 8 * 240000.0),
+            ("__amd_rocclr_copyBuffer", "SQ_INSTS_MFMA", 0.0)], dur_ns=100000)
+    b = tmp_path / "ops"
+    b.mkdir()
+    _write(b / "b_counter_collection.csv",
+           [(out_pass, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 32e6), (out_pass, "SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)],
+           dur_ns=100000)
+    res = bench.summarize_mfma([str(a), str(b)])
+    assert set(res) == {"output"}
+    r = res["output"]
+    assert abs(r["dispatch_us"] - 100.0) < 1e-9
+    assert abs(r["util"] - 16e6 / (1024 * 240000.0)) < 1e-12
+    assert abs(r["bf16"] - 1e6 * 16384 / 100e-6 / 1e12) < 1e-9   # 163.84 TFLOP/s
+    assert r["fp32"] == 0.0
