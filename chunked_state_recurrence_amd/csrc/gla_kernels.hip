@@ -365,6 +365,27 @@ chunk_kernel(const KernelParams p) {
         for (int u = 0; u < CPL; ++u) wide |= -gam[u] > kSpanGuard;
         const bool fast = __ballot(wide) == 0;
 
+        // rows of the exact path. A row runs until its running decay products
+        // underflow (a product that has decayed by 2^149 is below the smallest
+        // fp32 subnormal; at a dim's average rate that takes 149 C / -gam
+        // tokens). When the least-decaying key dim keeps rows alive for more
+        // than about 16 tokens (its chunk total above -kPairSpan, log2 units),
+        // late rows cost far more than early ones: wave w then takes rows
+        // RPW/2 w + m and their mirror images C - 1 - (RPW/2 w + m), m < RPW/2
+        // (the same number of (i, j) pairs for every wave), and re-reads their
+        // raw q from the cache below (rows past T read 0). Otherwise each wave
+        // keeps its own rows. The choice is the same in every wave.
+        constexpr float kPairSpan = 149.f * C / 16;
+        bool longrows = false;
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) longrows |= gam[u] > -kPairSpan;
+        const bool pair = __ballot(longrows) != 0;
+        auto exact_row = [&](int il) {
+            constexpr int H2 = RPW / 2;
+            const int a = H2 * w + (il < H2 ? il : il - H2);
+            return !pair ? r0 + il : il < H2 ? a : C - 1 - a;
+        };
+
         // ---- operand tiles into LDS -----------------------------------------
         float eg[CPL];
 #pragma unroll
@@ -433,14 +454,26 @@ chunk_kernel(const KernelParams p) {
 #pragma unroll
         for (int u = 0; u < CPL; ++u) seg_gamma[u] += gam[u];
 
-        // the exact path reads raw q rows of this wave after the prefetch below
+        // the exact rows' q as floats, materialised here (the empty asm makes
+        // the wait for re-read rows happen before the prefetch below is
+        // issued, not at their first use behind it)
         float qx[RPW][CPL];
         if constexpr (kScores) {
             if (!fast) {
+                Raw<E, CPL> qe[RPW];
+                if (pair) {
 #pragma unroll
-                for (int i = 0; i < RPW; ++i)
+                    for (int il = 0; il < RPW; ++il)
+                        qe[il].load(bq, ((c * C + exact_row(il)) * D + lane * CPL) * es, 0);
+                }
 #pragma unroll
-                    for (int u = 0; u < CPL; ++u) qx[i][u] = rq[i].get(u);
+                for (int il = 0; il < RPW; ++il)
+#pragma unroll
+                    for (int u = 0; u < CPL; ++u) {
+                        if (pair) qx[il][u] = qe[il].get(u);
+                        else qx[il][u] = rq[il].get(u);
+                        __asm__ __volatile__("" : "+v"(qx[il][u]));
+                    }
             }
         }
 
@@ -483,10 +516,10 @@ chunk_kernel(const KernelParams p) {
                             if ((I * NB + J) % NW == w) sink_tile(c, I, J, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 }
             } else {
-                // rows of this wave, elementwise: running product over j = i..0
+                // the wave's exact rows, elementwise: running product over j = i..0
 #pragma unroll 1
                 for (int il = 0; il < RPW; ++il) {
-                    const int i = r0 + il;
+                    const int i = exact_row(il);
                     float qi[CPL], pr[CPL];
 #pragma unroll
                     for (int u = 0; u < CPL; ++u) {
