@@ -183,6 +183,30 @@ def test_bf16_extreme_gates(gate):
     check(x, wl.scale, o, hf, TOL_BF16)
 
 
+# the exact path at every supported (dtype, head dim, chunk): 8 or 16 rows per
+# wave, rows kept (const:-30, rows stop at once) or taken in mirrored pairs
+# (const:-2 and mixed, rows that run long), ragged tail (T = 333)
+EXACT_SHAPES = [("bf16", 128, 32), ("bf16", 64, 64), ("bf16", 64, 32),
+                ("f32", 64, 64), ("f32", 64, 32), ("f32", 128, 32)]
+
+
+@pytest.mark.parametrize("gate", ["const:-30", "const:-2", "mixed"])
+@pytest.mark.parametrize("dtype,D,chunk", EXACT_SHAPES)
+def test_exact_path_shapes(dtype, D, chunk, gate):
+    fp32 = dtype == "f32"
+    wl = dataclass_replace(WORKLOADS["tiny_f32" if fp32 else "prefill_4k"], D=D)
+    say(f"[exact path] {dtype} D={D} chunk={chunk} gate={gate}")
+    if gate == "mixed":
+        x = make_inputs(wl, B=1, H=2, T=333, seed=31, h0_std=0.3)
+        gen = torch.Generator().manual_seed(32)
+        spikes = torch.rand(x["g"].shape, generator=gen) < 0.01
+        x["g"] = torch.where(spikes, torch.full_like(x["g"], -200.0), x["g"])
+    else:
+        x = make_inputs(wl, B=1, H=2, T=333, seed=31, gate=gate, h0_std=0.3)
+    o, hf = gpu_run(x, fp32=fp32, chunk=chunk)
+    check(x, D ** -0.5, o, hf, TOL_F32 if fp32 else TOL_BF16)
+
+
 @pytest.mark.parametrize("gate", ["const:-30", "const:-10000", "mixed"])
 def test_bf16_extreme_gates_full_size(gate):
     """The prefill_16k shape (B=1, H=16, T=16K) with every chunk on the exact
