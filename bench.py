@@ -19,6 +19,11 @@ algorithmic bytes of the workload (bf16 q, k, v, o + fp32 g per token-head,
 plus the fp32 final state); ``cpu_baseline`` is the fp64 oracle timed on the
 host cores over a bounded sample of the same workload.
 
+Other forward configurations (separate lines): --workload prefill_4k,
+batch16_4k or long_128k (bf16), and tiny_f32 (B=1, H=2, T=256, D=64), which
+runs the fp32 path (gla_fwd_f32; 4-byte q, k, v, o in the algorithmic bytes,
+the MFMA fraction against the fp32 peak).
+
 Scalar gate (a separate line, not the headline):
     python bench.py --workload prefill_16k_scalar
 the same step through gla_fwd_scalar (g [B,H,T]); its algorithmic bytes
@@ -77,8 +82,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 METRIC = "prefill tokens/s, chunk GLA fwd H=16 D=128 bf16; % MFMA peak / HBM BW"
 SCALAR_METRIC = "prefill tokens/s, chunk scalar-gate linear attention fwd H=16 D=128 bf16; % HBM BW"
+F32_METRIC = "prefill tokens/s, chunk GLA fwd fp32 q/k/v/o; % fp32 MFMA peak / HBM BW"
 BWD_METRIC = ("backward tokens/s, chunk GLA bwd H=16 D=128 bf16 (forward states recomputed); "
               "% HBM BW")
 GDN_METRIC = "prefill tokens/s, chunk gated delta rule fwd H=16 D=128 bf16; % HBM BW"
@@ -93,8 +100,8 @@ COPY_BYTES = 1 << 30
 
 
 def algorithmic_bytes(wl) -> int:
-    """bf16 q, k, v, o (2 B each) + fp32 g (4 B; one per token for the scalar
-    gate) per token-head element row, plus the fp32 h0 read and h_final write
+    """q, k, v, o (2 B each in bf16, 4 B in fp32) + fp32 g (4 B; one per token
+    for the scalar gate) per token-head element row, plus the fp32 h0 read and h_final write
     when present."""
     th = wl.B * wl.H * wl.T
     es = 2 if wl.dtype == "bf16" else 4
@@ -730,9 +737,8 @@ def main():
             raise SystemExit("--backward measures the bf16 per-key-dim workloads")
         bench_backward(args, wl)
         return
-    fwd = gla.gla_fwd_scalar if wl.scalar_gate else gla.gla_fwd
-    if wl.dtype != "bf16":
-        raise SystemExit("bench.py measures the bf16 workloads")
+    fp32 = wl.dtype == "f32"
+    fwd = gla.gla_fwd_scalar if wl.scalar_gate else gla.gla_fwd_f32 if fp32 else gla.gla_fwd
     dev = torch.device("cuda:0")
     gla.set_tuning(args.target_wgs, args.head_group)
     chunk = args.chunk or 64
@@ -743,7 +749,8 @@ def main():
         d = {n: (None if host[n] is None else host[n].to(dev)) for n in ("q", "k", "v", "g", "h0")}
         if s == 1:  # a second, independent copy of the same inputs
             d = {n: (None if t is None else t.clone()) for n, t in d.items()}
-        d["o"] = torch.empty(wl.B, wl.H, wl.T, wl.D, dtype=torch.bfloat16, device=dev)
+        d["o"] = torch.empty(wl.B, wl.H, wl.T, wl.D, dtype=torch.float32 if fp32 else torch.bfloat16,
+                             device=dev)
         d["hf"] = (torch.empty(wl.B, wl.H, wl.D, wl.D, dtype=torch.float32, device=dev)
                    if wl.want_final else None)
         sets.append(d)
@@ -809,7 +816,7 @@ def main():
             traffic = int(f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"])
 
     res = {
-        "metric": SCALAR_METRIC if wl.scalar_gate else METRIC,
+        "metric": SCALAR_METRIC if wl.scalar_gate else F32_METRIC if fp32 else METRIC,
         "value": wl.B * wl.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -819,7 +826,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if fp32 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "K": wl.D, "V": wl.D,
                    "chunk": chunk, "h_final": wl.want_final, "h0": wl.h0_std is not None,
@@ -827,11 +834,12 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "output pass (chunk_kernel<BF16,128,64,MODE_OUT>)",
+                     "kernel": f"output pass (chunk_kernel<{'F32' if fp32 else 'BF16'},{wl.D},{chunk},MODE_OUT>)",
                      "kernel_ms": out_ms},
         "whole_path": {"hbm_frac": bytes_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                        "mfma_tflops": flops / (ms * 1e-3) / 1e12,
-                       "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                       "mfma_frac": flops / (ms * 1e-3) / 1e12 / (MFMA_F32_PEAK_TFLOPS if fp32
+                                                                  else MFMA_BF16_PEAK_TFLOPS),
                        "algorithmic_bytes": bytes_alg, "algorithmic_flops": flops},
         "kernels_ms": {k: statistics.mean(v) for k, v in by_kind.items()},
         "latency_ms": {"mean": traced_ms, "p50": statistics.median(per_step),
