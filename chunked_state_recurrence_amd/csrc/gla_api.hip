@@ -573,6 +573,7 @@ static int run_stage(int mode, const void *q, const void *k, const float *g, flo
     Call c{gla::DTYPE_BF16, q, k, q, g, nullptr, out, nullptr, nullptr, B, H, T, K, K, chunk, scale,
            static_cast<hipStream_t>(stream)};
     if (B <= 0 || H <= 0 || T < 0 || K <= 0) return GLA_ERR_SHAPE;
+    if (long(B) * H > (1L << 30) || long(T) * K >= (1L << 29)) return GLA_ERR_SHAPE;
     if (K != 64 && K != 128) return GLA_ERR_UNSUPPORTED;
     if (chunk < 0) return GLA_ERR_UNSUPPORTED;
     if (chunk == 0) c.chunk = default_chunk(c.dtype, K);

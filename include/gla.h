@@ -25,7 +25,9 @@
  * in both.  Every base pointer must be 16-byte aligned.
  *
  * Supported shapes: K == V in {64, 128}; T >= 0; B, H >= 1; any T (the last
- * chunk may be partial).  chunk: 0 picks the default (64); gla_fwd accepts
+ * chunk may be partial) with T * K < 2^29 and B * H <= 2^30, since each
+ * (batch, head) row is addressed with 32-bit byte offsets; larger sizes return
+ * GLA_ERR_SHAPE.  chunk: 0 picks the default (64); gla_fwd accepts
  * 32 and 64; gla_fwd_f32 accepts 32 and 64 for K = 64 and 32 for K = 128.
  * Anything else returns GLA_ERR_UNSUPPORTED, never a silent fallback.
  *
@@ -60,7 +62,7 @@ extern "C" {
 
 #define GLA_OK               0
 #define GLA_ERR_NULL        -1  /* a required pointer is NULL                  */
-#define GLA_ERR_SHAPE       -2  /* negative or zero B/H, negative T, K != V    */
+#define GLA_ERR_SHAPE       -2  /* B/H <= 0, T < 0, K != V, or past the limits */
 #define GLA_ERR_UNSUPPORTED -3  /* K/V or chunk outside the supported set      */
 #define GLA_ERR_ALIGN       -4  /* a base pointer is not 16-byte aligned       */
 #define GLA_ERR_LAUNCH      -5  /* a kernel launch failed (hipGetLastError)    */

@@ -24,7 +24,7 @@
  * the null stream) and runs asynchronously; each (batch, head) row is
  * independent and the result is deterministic.
  *
- * Errors: GLA_OK, or GLA_ERR_SHAPE (B, H, K or V <= 0), GLA_ERR_UNSUPPORTED
+ * Errors: GLA_OK, or GLA_ERR_SHAPE (B, H, K or V <= 0, or B * H > 2^30), GLA_ERR_UNSUPPORTED
  * (K != V or K not in {64, 128}), GLA_ERR_NULL (any pointer NULL),
  * GLA_ERR_ALIGN, GLA_ERR_ALIAS (o or state overlapping an input, or each
  * other), GLA_ERR_DEVICE, GLA_ERR_LAUNCH.  Arguments are checked before

@@ -185,3 +185,26 @@ def test_fp32_chunk_support_table():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(gla.GLALibraryMissing):
         gla.load_library(str(tmp_path / "libgla.so"))
+
+
+# Stage entry points: shapes are checked first, so fake pointers never reach
+# a launch; T * K past 2^29 would overflow the kernels' 32-bit row offsets.
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(H=-1), -2), (dict(T=-1), -2), (dict(T=1 << 24), -2),
+    (dict(B=1 << 16, H=1 << 15), -2), (dict(K=96), -3), (dict(chunk=48), -3),
+])
+@pytest.mark.parametrize("stage", ["cumsum", "intra", "states"])
+def test_stage_argument_errors(stage, kw, code):
+    lib = gla.load_library()
+    a = dict(B=1, H=2, T=100, K=128, chunk=64)
+    a.update(kw)
+    p = [ctypes.c_void_p(FAKE + i * STEP) for i in range(8)]
+    if stage == "cumsum":
+        r = lib.gla_stage_cumsum(p[0], p[1], p[2], a["B"], a["H"], a["T"], a["K"], a["chunk"], None)
+    elif stage == "intra":
+        r = lib.gla_stage_intra(p[0], p[1], p[2], p[3], a["B"], a["H"], a["T"], a["K"], a["chunk"],
+                                ctypes.c_float(1.0), None)
+    else:
+        r = lib.gla_stage_states(p[0], p[1], p[2], p[3], None, p[4], None, p[5], a["B"], a["H"],
+                                 a["T"], a["K"], a["K"], a["chunk"], ctypes.c_float(1.0), None)
+    assert r == code
