@@ -99,6 +99,53 @@ KERNEL_SOURCES = [os.path.join(ROOT, "chunked_state_recurrence_amd", "csrc", f)
 COPY_BYTES = 1 << 30
 
 
+def host_threads() -> int:
+    """Every CPU this process may run on (what `nproc` reports)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def environment() -> dict:
+    """GPU, ROCm and host CPU the numbers were measured on."""
+    env = {"nproc": host_threads(), "os_cpu_count": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    env["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+            env["cgroup_cpus"] = None if quota == "max" else int(quota) / int(period)
+    except (OSError, ValueError):
+        pass
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                env["rocm"] = f.read().strip()
+                break
+        except OSError:
+            pass
+    try:
+        import torch
+        env["torch"] = torch.__version__
+        env["torch_hip"] = torch.version.hip
+        if torch.cuda.is_available():
+            prop = torch.cuda.get_device_properties(0)
+            env["gpu"] = prop.name
+            env["gpu_arch"] = getattr(prop, "gcnArchName", None)
+            env["gpu_cus"] = prop.multi_processor_count
+            env["gpu_mem_gib"] = round(prop.total_memory / 2 ** 30, 1)
+    except Exception as e:   # noqa: BLE001 - informational only
+        env["torch_error"] = str(e)
+    return env
+
+
 def algorithmic_bytes(wl) -> int:
     """q, k, v, o (2 B each in bf16, 4 B in fp32) + fp32 g (4 B; one per token
     for the scalar gate) per token-head element row, plus the fp32 h0 read and h_final write
@@ -109,6 +156,17 @@ def algorithmic_bytes(wl) -> int:
     per_token_head = wl.D * 4 * es + gate         # 1536 B at D=128, bf16 (scalar gate: 1028)
     state = wl.B * wl.H * wl.D * wl.D * 4
     return th * per_token_head + (state if wl.want_final else 0) + (state if wl.h0_std else 0)
+
+
+KIND_NAMES = {"output": "output pass (chunk_kernel, MODE_OUT)", "segment": "state pass (state_kernel)",
+              "scan": "segment-state scan (scan_kernel)"}
+
+
+def pass_bytes(wl, kind: str):
+    """Algorithmic bytes of one launch of a forward pass: the output pass
+    reads q, k, v, g and writes o for every token-head (plus h0 / h_final), so
+    its unit is the workload's; other passes are not priced on their own."""
+    return algorithmic_bytes(wl) if kind == "output" else None
 
 
 def backward_bytes(wl, chunk: int) -> int:
@@ -190,7 +248,7 @@ def cpu_baseline(wl, x, budget_s: float = 20.0, min_s: float = 10.0):
     import oracle
     from chunked_state_recurrence_amd.workloads import to_f64_numpy
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    threads = host_threads()
     pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
 
     def run(sel):
@@ -228,7 +286,7 @@ def cpu_baseline_decode(wl, x, min_s: float = 10.0):
     import oracle
     from chunked_state_recurrence_amd.workloads import to_f64_numpy
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    threads = host_threads()
     nb = min(wl.B, 64)
     f = {n: np.ascontiguousarray(to_f64_numpy(x[n][:nb])) for n in ("q", "k", "v", "g", "h0")}
     times = []
@@ -242,6 +300,14 @@ def cpu_baseline_decode(wl, x, min_s: float = 10.0):
                       f"each, {len(times)} passes of {statistics.mean(times) * 1e3:.1f} ms; "
                       "scaled to all rows",
             "seconds": round(sum(times), 3)}
+
+
+def emit(res: dict):
+    """Print the one JSON line, with the machine it was measured on."""
+    res.setdefault("env", environment())
+    if isinstance(res.get("cpu_baseline"), dict):
+        res["cpu_baseline"].setdefault("cpu_model", res["env"].get("cpu_model"))
+    print(json.dumps(res), flush=True)
 
 
 def copy_calibration(dev):
@@ -326,7 +392,7 @@ def bench_decode(args, wl):
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline_decode(wl, host)
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 def cpu_baseline_backward(wl, x, gr, min_s: float = 10.0):
@@ -337,7 +403,7 @@ def cpu_baseline_backward(wl, x, gr, min_s: float = 10.0):
     import oracle
     from chunked_state_recurrence_amd.workloads import to_f64_numpy
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    threads = host_threads()
     pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
     src = dict(x)
     src["do"], src["dhf"] = gr["do"], gr["dh_final"]
@@ -370,7 +436,7 @@ def cpu_baseline_gdn(wl, x, min_s: float = 10.0):
     import oracle
     from chunked_state_recurrence_amd.workloads import to_f64_numpy
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    threads = host_threads()
     pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)][:threads]
     f = {n: (None if x[n] is None else np.stack([to_f64_numpy(x[n][b, h]) for (b, h) in pairs])[None])
          for n in ("q", "k", "v", "g", "beta", "h0")}
@@ -478,7 +544,7 @@ def bench_gdn(args, wl):
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline_gdn(wl, host)
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 def bench_backward(args, wl):
@@ -567,7 +633,7 @@ def bench_backward(args, wl):
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline_backward(wl, host, gr)
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 def read_counters(wl_name: str):
@@ -699,6 +765,7 @@ def main():
     ap.add_argument("--target-wgs", type=int, default=0)
     ap.add_argument("--head-group", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-parity", action="store_true", help="skip the one-sequence parity check")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--summarize-mfma", metavar="DIR", nargs="+")
@@ -777,21 +844,27 @@ def main():
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
 
-    # timed region 2: the same K steps with per-step events and the library's
-    # per-launch HIP-event tracing (kernel durations for the roofline,
-    # latency percentiles); its events sit between kernels, so its step time
-    # is reported separately and not used as the headline
+    # timed region 2: the same K steps with one event between steps (no
+    # library tracing) for the latency percentiles
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    gla.profile_start(8 * args.steps + 8)
     torch.cuda.synchronize()
     ev[0].record(stream)
     for i in range(args.steps):
         step(i)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+
+    # timed region 3: the library's per-launch HIP-event tracing on its launch
+    # stream (kernel durations); those events sit between kernels, so this
+    # region's step time is reported apart from the headline
+    gla.profile_start(8 * args.steps + 8)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
     kernels = gla.profile_stop()
-    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    traced_ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    traced_wall_ms = (time.perf_counter() - t3) * 1e3 / args.steps
 
     if args.copy_calibration:
         copy_calibration(dev)
@@ -799,22 +872,57 @@ def main():
     by_kind = {}
     for kind, kms in kernels:
         by_kind.setdefault(kind, []).append(kms)
-    # the output pass's device time per step: with head groups (--head-group)
-    # a step launches it once per group, each launch covering part of the heads
-    out_launches = len(by_kind["output"]) / args.steps
-    out_ms = sum(by_kind["output"]) / args.steps
+    kernels_ms = {k: statistics.mean(v) for k, v in by_kind.items()}
+    kernels_ms_per_step = {k: sum(v) / args.steps for k, v in by_kind.items()}
+    # the dominant kernel: the one with the most device time per step
+    dom = max(kernels_ms_per_step, key=kernels_ms_per_step.get)
+    dom_launches = len(by_kind[dom]) / args.steps
+    dom_ms = kernels_ms_per_step[dom]
     bytes_alg = algorithmic_bytes(wl)
-    achieved = bytes_alg / (out_ms * 1e-3) / 1e9
     flops = algorithmic_flops(wl, chunk)
-
-    traffic = None
+    achieved_call = bytes_alg / (ms * 1e-3) / 1e9
+    dom_bytes = pass_bytes(wl, dom)
+    traffic_call, traffic_dom = None, None
     c = read_counters(args.workload)
-    if c and "fetch_factor" in c and out_launches == 1:   # counters are taken per launch
+    if c and "fetch_factor" in c:   # counters are per dispatch: one launch per pass and step
         m = c["median_per_dispatch_KiB"]
-        f, w = m.get("output:FETCH_SIZE"), m.get("output:WRITE_SIZE")
-        if f is not None and w is not None:
-            traffic = int(f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"])
+        tot, ok = 0.0, True
+        for k in kernels_ms_per_step:
+            f, w = m.get(f"{k}:FETCH_SIZE"), m.get(f"{k}:WRITE_SIZE")
+            if f is None or w is None or len(by_kind[k]) != args.steps:
+                ok = False
+                break
+            b_k = f * 1024 * c["fetch_factor"] + w * 1024 * c["write_factor"]
+            tot += b_k
+            if k == dom:
+                traffic_dom = int(b_k)
+        traffic_call = int(tot) if ok else None
 
+    # parity of this run: one (batch, head) sequence of the last output of
+    # input set 0 against the oracle
+    parity = None
+    if not args.no_parity:
+        import numpy as np
+        import oracle
+        from chunked_state_recurrence_amd.workloads import to_f64_numpy
+        sel = {n: (None if host[n] is None else to_f64_numpy(host[n][:1, :1])) for n in
+               ("q", "k", "v", "g", "h0")}
+        if wl.scalar_gate:
+            ro, rh, *_ = (*oracle.scalar_gate_recurrence(sel["q"], sel["k"], sel["v"], sel["g"],
+                                                         sel["h0"], wl.scale),)
+        else:
+            ro, rh, _ = oracle.token_recurrence(sel["q"], sel["k"], sel["v"], sel["g"], sel["h0"],
+                                                wl.scale)
+        got = sets[0]["o"][:1, :1].float().cpu().numpy()
+        err = float(np.max(np.abs(got - ro)) / max(float(np.max(np.abs(ro))), 1e-30))
+        parity = {"max_norm_err": err, "tolerance": 1e-3 if fp32 else 1e-2,
+                  "sample": "(batch 0, head 0), whole sequence, against the fp64 oracle"}
+        if wl.want_final:
+            gh = sets[0]["hf"][:1, :1].cpu().numpy()
+            parity["h_final_max_norm_err"] = float(np.max(np.abs(gh - rh)) /
+                                                   max(float(np.max(np.abs(rh))), 1e-30))
+
+    io_bytes = sum(t.numel() * t.element_size() for t in sets[0].values() if t is not None)
     res = {
         "metric": SCALAR_METRIC if wl.scalar_gate else F32_METRIC if fp32 else METRIC,
         "value": wl.B * wl.T / (ms * 1e-3),
@@ -832,25 +940,43 @@ def main():
                    "chunk": chunk, "h_final": wl.want_final, "h0": wl.h0_std is not None,
                    "gate": "scalar [B,H,T]" if wl.scalar_gate else "per key dim [B,H,T,K]",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"output pass (chunk_kernel<{'F32' if fp32 else 'BF16'},{wl.D},{chunk},MODE_OUT>)",
-                     "kernel_ms": out_ms},
+        # the whole gla_fwd call (every launch of the path) priced against HBM
+        # bandwidth with the workload's algorithmic bytes; the dominant
+        # kernel's own figure follows under "dominant_kernel"
+        "roofline": {"bound": "hbm", "achieved": achieved_call, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_call / HBM_PEAK_GBS, "traffic": traffic_call,
+                     "scope": "whole gla_fwd call (ms_per_step)",
+                     "algorithmic_bytes_per_call": bytes_alg,
+                     "dominant_kernel": {
+                         "kind": dom, "kernel": KIND_NAMES.get(dom, dom),
+                         "launches_per_step": dom_launches, "kernel_ms": dom_ms,
+                         "algorithmic_bytes_per_launch": dom_bytes,
+                         "achieved": (dom_bytes / (dom_ms * 1e-3) / 1e9) if dom_bytes else None,
+                         "frac": (dom_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if dom_bytes else None,
+                         "traffic": traffic_dom}},
         "whole_path": {"hbm_frac": bytes_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                        "mfma_tflops": flops / (ms * 1e-3) / 1e12,
                        "mfma_frac": flops / (ms * 1e-3) / 1e12 / (MFMA_F32_PEAK_TFLOPS if fp32
                                                                   else MFMA_BF16_PEAK_TFLOPS),
                        "algorithmic_bytes": bytes_alg, "algorithmic_flops": flops},
-        "kernels_ms": {k: statistics.mean(v) for k, v in by_kind.items()},
-        "latency_ms": {"mean": traced_ms, "p50": statistics.median(per_step),
-                       "p95": sorted(per_step)[min(len(per_step) - 1, int(0.95 * len(per_step)))],
-                       "p99": sorted(per_step)[min(len(per_step) - 1, int(0.99 * len(per_step)))]},
+        "kernels_ms": kernels_ms,
+        "kernels_ms_per_step": kernels_ms_per_step,
+        "traced_step_ms": traced_wall_ms,
+        "latency_ms": {"source": "untraced steps with one event between steps",
+                       "mean": statistics.mean(per_step), "p50": statistics.median(per_step),
+                       "p95": per_step[min(len(per_step) - 1, int(0.95 * len(per_step)))],
+                       "p99": per_step[min(len(per_step) - 1, int(0.99 * len(per_step)))]},
+        "memory": {"io_bytes_per_call": io_bytes, "library_workspace_bytes": gla.workspace_bytes(),
+                   "torch_peak_bytes": torch.cuda.max_memory_allocated(dev),
+                   "note": "io: q, k, v, g, h0, o, h_final of one input set; the bench holds two sets"},
+        "parity": parity,
+        "env": environment(),
     }
     if wl.name in PAGES_TOKENS_PER_S:
         res["vs_baseline"] = res["value"] / PAGES_TOKENS_PER_S[wl.name]
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, host)
-    print(json.dumps(res), flush=True)
+    emit(res)
 
 
 if __name__ == "__main__":

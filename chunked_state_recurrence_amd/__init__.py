@@ -32,4 +32,5 @@ from ._binding import (  # noqa: F401
     gdn_set_path,
     strerror,
     version,
+    workspace_bytes,
 )

@@ -28,7 +28,7 @@ EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_ver
             "gla_release", "gla_profile_start", "gla_profile_stop", "gla_stage_cumsum",
             "gla_stage_intra", "gla_stage_states", "gla_decode", "gla_decode_f32",
             "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd",
-            "gla_gdn_set_path")
+            "gla_gdn_set_path", "gla_workspace_bytes")
 KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode", 5: "bwd_segment",
                 6: "bwd", 7: "gdn", 8: "gdn_prep", 9: "gdn_walk"}
 GDN_PATHS = {"auto": 0, "one": 1, "two": 2}
@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH):
     lib.gla_strerror.restype = ctypes.c_char_p
     lib.gla_version.argtypes = []
     lib.gla_release.argtypes = []
+    lib.gla_workspace_bytes.argtypes = []
+    lib.gla_workspace_bytes.restype = ctypes.c_longlong
     lib.gla_release.restype = None
     lib.gla_profile_start.argtypes = [I]
     lib.gla_profile_stop.argtypes = [ctypes.POINTER(_KernelTime), I, ctypes.POINTER(I)]
@@ -351,3 +353,8 @@ def strerror(code: int) -> str:
 
 def release():
     load_library().gla_release()
+
+
+def workspace_bytes() -> int:
+    """Device workspace the library holds on the current device (bytes)."""
+    return int(load_library().gla_workspace_bytes())

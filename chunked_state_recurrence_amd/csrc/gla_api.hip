@@ -683,6 +683,14 @@ const char *gla_strerror(int code) {
 
 int gla_version(void) { return kVersion; }
 
+long long gla_workspace_bytes(void) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (size_t(dev) >= g_dev.size()) return 0;
+    return (long long)(g_dev[dev].ws_bytes + g_dev[dev].bws_bytes);
+}
+
 void gla_release(void) {
     std::lock_guard<std::mutex> lk(g_mu);
     int cur = -1;

@@ -142,6 +142,14 @@ const char *gla_strerror(int code);
 /* Library version: major*10000 + minor*100 + patch. */
 int gla_version(void);
 
+/*
+ * Bytes of device workspace the library holds on the current device (the
+ * forward's segment states plus the backward's chunk-start states), as
+ * grown by the calls so far; 0 when none is held.  Reported next to the
+ * caller's own buffers as the library's share of peak device memory.
+ */
+long long gla_workspace_bytes(void);
+
 /* Free the cached workspace on every device.  Call with no work pending. */
 void gla_release(void);
 

@@ -23,7 +23,7 @@ def _declared():
     for h in HEADERS:
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gla_\w+)\s*\(", text, flags=re.M)
+        names += re.findall(r"^\s*(?:const\s+)?(?:\w+\s+)*\w+\s*\*?\s*(gla_\w+)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 

@@ -15,8 +15,8 @@ import torch
 
 import chunked_state_recurrence_amd as gla
 import oracle
-from chunked_state_recurrence_amd.workloads import (WORKLOADS, make_grad_inputs, make_inputs,
-                                                    to_f64_numpy)
+from chunked_state_recurrence_amd.workloads import WORKLOADS, make_grad_inputs, make_inputs
+from wholecheck import select_f64, whole_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -58,21 +58,21 @@ def gpu_bwd(x, gr, *, fp32=False, chunk=0):
     return [t.float().cpu().numpy() for t in out]
 
 
-def check(x, gr, got, tol, heads=None):
-    f = {n: to_f64_numpy(x[n]) for n in ("q", "k", "v", "g", "h0")}
-    f["do"] = to_f64_numpy(gr["do"])
-    f["dhf"] = to_f64_numpy(gr["dh_final"])
-    if heads is not None:   # sampled (b, h) pairs, each over its full sequence
-        f = {n: (None if a is None else np.stack([a[b, h] for (b, h) in heads])[None])
-             for n, a in f.items()}
-        got = [np.stack([a[b, h] for (b, h) in heads])[None] for a in got]
-    scale = f["q"].shape[-1] ** -0.5
-    ref = oracle.token_recurrence_backward(f["q"], f["k"], f["v"], f["g"], f["h0"], f["do"],
-                                           f["dhf"], scale)
-    errs = {}
-    for name, a, r in zip(NAMES, got, ref):
-        assert np.isfinite(a).all(), f"non-finite {name}"
-        errs[name] = nerr(a, r)
+def check(x, gr, got, tol):
+    """Every gradient element against the oracle (in groups of sequences),
+    normalised over each whole tensor."""
+    src = dict(x)
+    src["do"], src["dhf"] = gr["do"], gr["dh_final"]
+    B, H, T, K = x["q"].shape
+    scale = K ** -0.5
+
+    def ref(sel):
+        f = select_f64(src, ("q", "k", "v", "g", "h0", "do", "dhf"), sel)
+        r = oracle.token_recurrence_backward(f["q"], f["k"], f["v"], f["g"], f["h0"], f["do"],
+                                             f["dhf"], scale)
+        return dict(zip(NAMES, r))
+
+    errs = whole_errors(dict(zip(NAMES, got)), ref, B, H, T)
     say("    " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f"  (tol {tol:g})")
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, bad
@@ -177,12 +177,11 @@ def test_bitwise_repeatable():
     assert all(np.array_equal(u, v) for u, v in zip(a, b))
 
 
-@pytest.mark.parametrize("name,heads", [("prefill_16k", [(0, 1), (0, 14)])])
-def test_full_size_workload_sampled_heads(name, heads):
-    """The benchmark's workload; sampled heads against the oracle over their
-    whole sequence, every gradient checked finite."""
-    wl = WORKLOADS[name]
-    say(f"[bwd full {name}] B={wl.B} H={wl.H} T={wl.T} sampled={heads}")
+def test_full_size_workload():
+    """The benchmark's workload (prefill_16k) in its launch configuration:
+    every gradient element of every head against the oracle."""
+    wl = WORKLOADS["prefill_16k"]
+    say(f"[bwd full {wl.name}] B={wl.B} H={wl.H} T={wl.T}, all {wl.B * wl.H} sequences")
     x = make_inputs(wl)
     gr = make_grad_inputs(wl)
-    check(x, gr, gpu_bwd(x, gr), TOL_BF16, heads=heads)
+    check(x, gr, gpu_bwd(x, gr), TOL_BF16)
