@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     gla_decode_f32,
     gla_fwd,
     gla_fwd_f32,
+    gla_fwd_noalloc,
     gla_fwd_scalar,
     gla_fwd_scalar_f32,
     gla_stage_cumsum,

@@ -21,6 +21,7 @@ GLA_OK = 0
 ERRORS = {
     -1: "GLA_ERR_NULL", -2: "GLA_ERR_SHAPE", -3: "GLA_ERR_UNSUPPORTED", -4: "GLA_ERR_ALIGN",
     -5: "GLA_ERR_LAUNCH", -6: "GLA_ERR_ALLOC", -7: "GLA_ERR_ALIAS", -8: "GLA_ERR_DEVICE",
+    -9: "GLA_ERR_WORKSPACE",
 }
 
 # every symbol include/gla.h and include/gla_stages.h declare
@@ -28,7 +29,7 @@ EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_ver
             "gla_release", "gla_profile_start", "gla_profile_stop", "gla_stage_cumsum",
             "gla_stage_intra", "gla_stage_states", "gla_decode", "gla_decode_f32",
             "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd",
-            "gla_gdn_set_path", "gla_workspace_bytes")
+            "gla_gdn_set_path", "gla_workspace_bytes", "gla_fwd_noalloc")
 KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode", 5: "bwd_segment",
                 6: "bwd", 7: "gdn", 8: "gdn_prep", 9: "gdn_walk"}
 GDN_PATHS = {"auto": 0, "one": 1, "two": 2}
@@ -64,6 +65,7 @@ def load_library(path: str = LIB_PATH):
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.gla_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_fwd_f32.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
+    lib.gla_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_fwd_scalar.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.gla_bwd.argtypes = [P] * 12 + [I, I, I, I, I, I, F, P]
     lib.gla_bwd_f32.argtypes = [P] * 12 + [I, I, I, I, I, I, F, P]
@@ -87,7 +89,7 @@ def load_library(path: str = LIB_PATH):
     lib.gla_profile_stop.argtypes = [ctypes.POINTER(_KernelTime), I, ctypes.POINTER(I)]
     lib.gla_profile_start.restype = ctypes.c_int
     lib.gla_profile_stop.restype = ctypes.c_int
-    for name in ("gla_fwd", "gla_fwd_f32", "gla_stage_states", "gla_stage_cumsum",
+    for name in ("gla_fwd", "gla_fwd_f32", "gla_fwd_noalloc", "gla_stage_states", "gla_stage_cumsum",
                  "gla_stage_intra", "gla_set_tuning", "gla_version", "gla_decode", "gla_decode_f32",
                  "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd",
                  "gla_gdn_set_path"):
@@ -158,6 +160,16 @@ def gla_fwd(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=False, o=Non
     Returns (o bf16 [B,H,T,D], h_final fp32 [B,H,D,D] or None).
     """
     return _fwd(load_library().gla_fwd, torch.bfloat16, q, k, v, g, h0, chunk, scale,
+                want_final, o, h_final, stream)
+
+
+def gla_fwd_noalloc(q, k, v, g, h0=None, *, chunk=0, scale=None, want_final=False, o=None,
+                    h_final=None, stream=None):
+    """gla_fwd through the entry point that allocates nothing on the device:
+    its segment-state workspace is the library's static scratch (64 MiB per
+    device).  Pass o (and h_final) to keep the call free of allocation; this
+    wrapper otherwise allocates them with torch before the call."""
+    return _fwd(load_library().gla_fwd_noalloc, torch.bfloat16, q, k, v, g, h0, chunk, scale,
                 want_final, o, h_final, stream)
 
 

@@ -18,15 +18,25 @@
 #include "gla_stages.h"
 #include "gla_internal.h"
 
+// Workspace of gla_fwd_noalloc: a file-scope device array, one copy per
+// device, held until the process ends.  Host code never uses its name as an
+// address (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, resolved once per device with that
+// device current, and only that address is passed to kernels.
+static constexpr size_t kScratchBytes = GLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int kDefaultTargetWgs = 256;
 
+
 struct DeviceState {
     int arch_ok = -1;  // -1 unknown, 0 not gfx950, 1 gfx950
     void *ws = nullptr;    // forward: segment states
     size_t ws_bytes = 0;
+    float *scratch = nullptr;   // this device's copy of `scratch` (gla_fwd_noalloc), once resolved
     void *bws = nullptr;   // backward: forward chunk-start states, final states, segment states
     size_t bws_bytes = 0;
 };
@@ -81,6 +91,22 @@ int current_device(DeviceState **out) {
     }
     if (d.arch_ok != 1) return GLA_ERR_DEVICE;
     *out = &d;
+    return GLA_OK;
+}
+
+// This device's address of `scratch`, resolved on the first use on the
+// device (which is current here) and kept.
+int device_scratch(DeviceState *d, float **out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!d->scratch) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return GLA_ERR_DEVICE;
+        }
+        d->scratch = static_cast<float *>(p);
+    }
+    *out = d->scratch;
     return GLA_OK;
 }
 
@@ -188,7 +214,34 @@ Plan plan_segments(int nbh, int N, int target, int state_per_cu) {
     return {P, cps, sub, (P - 1) * sub};
 }
 
-int run_forward(Call &c) {
+// Bytes of segment-state workspace a validated forward call needs with the
+// current schedule knobs (host arithmetic only).
+size_t forward_workspace_bytes(const Call &c) {
+    if (c.T == 0) return 0;
+    const int D = c.K;
+    const long BH = long(c.B) * c.H;
+    const int N = (c.T + c.chunk - 1) / c.chunk;
+    int target, hg;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        target = g_target_wgs;
+        hg = g_head_group;
+    }
+    const int spc = gla::state_units_per_cu(c.dtype, D, c.chunk);
+    long group = hg > 0 ? std::min<long>(hg, BH) : BH;
+    group = std::min<long>(group, 65535);
+    size_t need = 0;
+    for (long g0 = 0; g0 < BH; g0 += group) {
+        const int nbh = int(std::min(group, BH - g0));
+        const Plan pl = plan_segments(nbh, N, target, spc);
+        need = std::max(need, size_t(nbh) * size_t(pl.slots) * size_t(D) * (D + 1) * 4);
+    }
+    return need;
+}
+
+// fixed_ws != nullptr: use that workspace of fixed_cap bytes (no allocation);
+// a call that needs more returns GLA_ERR_WORKSPACE.
+int run_forward(Call &c, float *fixed_ws = nullptr, size_t fixed_cap = 0) {
     int rc = validate(c);
     if (rc != GLA_OK) return rc;
     DeviceState *dev = nullptr;
@@ -217,14 +270,14 @@ int run_forward(Call &c) {
     group = std::min<long>(group, 65535);
 
     // workspace: the largest group's (P-1) segment states and decays
-    size_t need = 0;
-    for (long g0 = 0; g0 < BH; g0 += group) {
-        const int nbh = int(std::min(group, BH - g0));
-        const Plan pl = plan_segments(nbh, N, target, spc);
-        need = std::max(need, size_t(nbh) * size_t(pl.slots) * size_t(D) * (D + 1) * 4);
-    }
+    const size_t need = forward_workspace_bytes(c);
     float *ws = nullptr;
-    if (need > 0 && (rc = ensure_workspace(dev, need, &ws)) != GLA_OK) return rc;
+    if (fixed_ws) {
+        if (need > fixed_cap) return GLA_ERR_WORKSPACE;
+        ws = fixed_ws;
+    } else if (need > 0 && (rc = ensure_workspace(dev, need, &ws)) != GLA_OK) {
+        return rc;
+    }
 
     for (long g0 = 0; g0 < BH; g0 += group) {
         const int nbh = int(std::min(group, BH - g0));
@@ -409,6 +462,22 @@ int gla_fwd_f32(const float *q, const float *k, const float *v, const float *g, 
     Call c{gla::DTYPE_F32, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
            static_cast<hipStream_t>(stream)};
     return run_forward(c);
+}
+
+int gla_fwd_noalloc(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const float *g,
+                    const float *h0, gla_bf16 *o, float *h_final, int B, int H, int T, int K, int V,
+                    int chunk, float scale, void *stream) {
+    Call c{gla::DTYPE_BF16, q, k, v, g, h0, o, h_final, nullptr, B, H, T, K, V, chunk, scale,
+           static_cast<hipStream_t>(stream)};
+    int rc = validate(c);
+    if (rc != GLA_OK) return rc;
+    // the size check is host arithmetic and comes before any device call
+    if (forward_workspace_bytes(c) > kScratchBytes) return GLA_ERR_WORKSPACE;
+    DeviceState *dev = nullptr;
+    if ((rc = current_device(&dev)) != GLA_OK) return rc;
+    float *ws = nullptr;
+    if ((rc = device_scratch(dev, &ws)) != GLA_OK) return rc;
+    return run_forward(c, ws, kScratchBytes);
 }
 
 // Scalar-gate forward (include/gla_scalar.h): g is [B,H,T].
@@ -677,6 +746,7 @@ const char *gla_strerror(int code) {
         case GLA_ERR_ALLOC: return "workspace allocation failed";
         case GLA_ERR_ALIAS: return "an output buffer overlaps an input buffer";
         case GLA_ERR_DEVICE: return "no usable gfx950 HIP device";
+        case GLA_ERR_WORKSPACE: return "the call needs more workspace than the static scratch holds";
         default: return "unknown error code";
     }
 }

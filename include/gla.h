@@ -69,6 +69,8 @@ extern "C" {
 #define GLA_ERR_ALLOC       -6  /* workspace allocation failed                 */
 #define GLA_ERR_ALIAS       -7  /* an output overlaps an input                 */
 #define GLA_ERR_DEVICE      -8  /* no usable HIP device / wrong architecture   */
+#define GLA_ERR_WORKSPACE   -9  /* gla_fwd_noalloc: the call needs more
+                                   workspace than the static scratch holds    */
 
 /* bfloat16 values are passed as their 16-bit storage. */
 typedef uint16_t gla_bf16;
@@ -89,6 +91,29 @@ int gla_fwd_f32(const float *q, const float *k, const float *v,
                 const float *g, const float *h0, float *o, float *h_final,
                 int B, int H, int T, int K, int V, int chunk, float scale,
                 void *stream);
+
+/*
+ * gla_fwd_noalloc — gla_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments, layout, results and errors as
+ * gla_fwd, but the call allocates nothing.  Its segment-state workspace is a
+ * static device array of GLA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on each device it runs on until the process ends; its address is
+ * looked up on the first call on a device.  That covers the default schedule
+ * at every supported shape (at most 32.25 MiB, for K = 128 with chunk 32: the
+ * segment states of about 512 state-pass work-groups); a call whose schedule
+ * needs more (raised target_wgs in gla_set_tuning) returns GLA_ERR_WORKSPACE
+ * before anything is enqueued.
+ * Every call on a device shares that device's array, whose contents are
+ * whatever the last call left (each call writes what it reads first), so
+ * calls that overlap in time on one device race: issue them on one stream or
+ * synchronise between them.
+ */
+#define GLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gla_fwd_noalloc(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v,
+                    const float *g, const float *h0, gla_bf16 *o, float *h_final,
+                    int B, int H, int T, int K, int V, int chunk, float scale,
+                    void *stream);
 
 /*
  * gla_set_tuning — schedule knobs (no effect on results beyond rounding of

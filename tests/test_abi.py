@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 def test_host_only_calls():
     assert gla.version() == 100
     assert gla.strerror(0) == "ok"
-    for code in range(-8, 0):
+    for code in range(-9, 0):
         assert gla.strerror(code) != "unknown error code"
     assert gla.strerror(-99) == "unknown error code"
     gla.set_tuning(0, 0)
@@ -70,9 +70,22 @@ def _call(lib, fn="gla_fwd", **kw):
     (dict(o=FAKE + 64), -7), (dict(hf=FAKE + 4 * STEP + 4096), -7),
     (dict(h0=FAKE + 6 * STEP, hf=FAKE + 6 * STEP), -7),
 ])
-def test_argument_errors(kw, code):
+@pytest.mark.parametrize("fn", ["gla_fwd", "gla_fwd_noalloc"])
+def test_argument_errors(kw, code, fn):
     lib = gla.load_library()
-    assert _call(lib, **kw) == code
+    assert _call(lib, fn, **kw) == code
+
+
+def test_noalloc_rejects_a_schedule_past_its_scratch():
+    """gla_fwd_noalloc: a schedule whose segment states exceed the 64 MiB
+    static scratch is refused before any device call (here 16 heads of 16K
+    tokens split into 256 segments each: 255 x 16 states of 66 KB, 269 MB)."""
+    lib = gla.load_library()
+    gla.set_tuning(100000, 0)
+    try:
+        assert _call(lib, "gla_fwd_noalloc", H=16, T=16384) == -9
+    finally:
+        gla.set_tuning(0, 0)
 
 
 # Scalar-gate entry points: g is [B,H,T] (800 bytes at B=1, H=2, T=100), so an
