@@ -755,6 +755,77 @@ def summarize_mfma(outdirs):
     return out
 
 
+SWEEPS = {
+    # sequence-length doubling at B = 1, H = 16 (the evaluation page's short
+    # vs long T comparison)
+    "t_doubling": [(1, t) for t in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)],
+    # batch against length at equal total tokens (B * T = 65536, H = 16)
+    "equal_tokens": [(1, 65536), (4, 16384), (16, 4096), (64, 1024), (256, 256)],
+}
+
+
+def bench_sweep(args):
+    """Scaling curves ("面向长序列大模型的线性注意力算子性能评测方法与优化实践", section
+    六.2: throughput as T doubles, and batch against length at equal total
+    tokens): the prefill_4k distributions at each (B, T), H = 16, D = 128, one
+    gla_fwd per step, two input sets alternating.  Prints one JSON object
+    with a point per shape."""
+    import dataclasses
+
+    import torch
+
+    import chunked_state_recurrence_amd as gla
+    from chunked_state_recurrence_amd.workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    gla.set_tuning(0, 0)
+    base = WORKLOADS["prefill_4k"]
+    points = []
+    for B, T in SWEEPS[args.sweep]:
+        wl = dataclasses.replace(base, name=f"B{B}_T{T}", B=B, T=T)
+        host = make_inputs(wl)
+        sets = []
+        for s_ in range(2):
+            d = {n: host[n].to(dev) for n in ("q", "k", "v", "g")}
+            if s_ == 1:
+                d = {n: t.clone() for n, t in d.items()}
+            d["o"] = torch.empty(B, wl.H, T, wl.D, dtype=torch.bfloat16, device=dev)
+            sets.append(d)
+        stream = torch.cuda.current_stream()
+
+        def step(i):
+            d = sets[i & 1]
+            gla.gla_fwd(d["q"], d["k"], d["v"], d["g"], None, o=d["o"], stream=stream)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        gla.profile_start(8 * args.steps + 8)
+        for i in range(args.steps):
+            step(i)
+        kern = {}
+        for kind, kms in gla.profile_stop():
+            kern[kind] = kern.get(kind, 0.0) + kms / args.steps
+        nbytes = algorithmic_bytes(wl)
+        points.append({"B": B, "H": wl.H, "T": T, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                       "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "kernels_ms_per_step": kern})
+        print(f"B={B} T={T}: {ms * 1e3:.1f} us, {B * T / (ms * 1e-3):.3e} tok/s, "
+              f"HBM frac {points[-1]['hbm_frac']:.3f}, " +
+              ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in kern.items()), file=sys.stderr, flush=True)
+        del sets, host
+        torch.cuda.empty_cache()
+    emit({"sweep": args.sweep, "metric": METRIC, "unit": "tokens/s", "dtype": "bf16",
+          "data": "synthetic", "steps": args.steps, "warmup": args.warmup, "points": points})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -770,6 +841,7 @@ def main():
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--summarize-mfma", metavar="DIR", nargs="+")
     ap.add_argument("--backward", action="store_true", help="time gla_bwd on the workload")
+    ap.add_argument("--sweep", choices=sorted(SWEEPS), help="scaling curve instead of one workload")
     args = ap.parse_args()
 
     if args.summarize_mfma:
@@ -785,6 +857,10 @@ def main():
               "communication, a sequence split would exchange one segment state per GPU)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        bench_sweep(args)
+        return
 
     import torch
 
