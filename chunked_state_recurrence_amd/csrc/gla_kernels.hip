@@ -425,12 +425,17 @@ chunk_kernel(const KernelParams p) {
                 for (int i = 0; i < RPW; ++i) {
                     float qh[CPL];
 #pragma unroll
-                    for (int u = 0; u < CPL; ++u) {
-                        const int col = lane * CPL + u;
-                        qh[u] = rq[i].get(u) * (p.scale * fexp2(rw[u] + Pf[i][u]));
-                        // raw k and the token's decay factors, natural column order
-                        sKt[(r0 + i) * L::QP + col] = E::f2l(rk[i].get(u));
-                        sDec[(r0 + i) * L::DP + col] = fexp2(rg[i].get(u) * kLog2e);
+                    for (int u = 0; u < CPL; ++u) qh[u] = rq[i].get(u) * (p.scale * fexp2(rw[u] + Pf[i][u]));
+                    // raw k and the token's decay factors, natural column order: this
+                    // lane's CPL key dims are adjacent, so each goes as one store
+                    // (and is read back as one load below)
+                    *reinterpret_cast<decltype(rk[i].x) *>(sKt + (r0 + i) * L::QP + lane * CPL) = rk[i].x;
+                    if constexpr (CPL == 2) {
+                        typedef float f2_t __attribute__((ext_vector_type(2)));
+                        *reinterpret_cast<f2_t *>(sDec + (r0 + i) * L::DP + lane * 2) =
+                            f2_t{fexp2(rg[i].get(0) * kLog2e), fexp2(rg[i].get(1) * kLog2e)};
+                    } else {
+                        sDec[(r0 + i) * L::DP + lane] = fexp2(rg[i].get(0) * kLog2e);
                     }
                     store_row(sQh, r0 + i, qh);
                 }
@@ -520,62 +525,96 @@ chunk_kernel(const KernelParams p) {
 #pragma unroll 1
                 for (int il = 0; il < RPW; ++il) {
                     const int i = exact_row(il);
-                    float qi[CPL], pr[CPL];
+                    // qp: q_i times the running decay product exp(g_{j+1} + ... + g_i)
+                    // of the column j about to be added (starts at q_i for j = i)
+                    float qp[CPL];
 #pragma unroll
                     for (int u = 0; u < CPL; ++u) {
-                        qi[u] = 0.f;
-                        pr[u] = 1.f;
+                        qp[u] = 0.f;
 #pragma unroll
                         for (int x = 0; x < RPW; ++x)
-                            if (x == il) qi[u] = qx[x][u];
+                            if (x == il) qp[u] = qx[x][u];
                     }
                     // columns j = i, i-1, .. in groups of 8: the 8 cross-lane sums of
                     // a group are independent and run interleaved (one at a time,
                     // each waited for the previous one's shuffle chain)
                     for (int jb = i; jb >= 0; jb -= 8) {
+                        // rows j = jb .. jb-7: raw k and decay factors of this lane's
+                        // key dims, one load each, all eight rows' loads issued before
+                        // any is used.  A full group (jb >= 7) addresses its rows from
+                        // one base (row jb-7) with constant offsets and needs no masks;
+                        // the row's last, partial group (its first columns) reads row
+                        // 0 for columns before the chunk and masks them.
                         float part[8];
+                        auto group = [&](auto fullc) {
+                            constexpr bool FULL = decltype(fullc)::value;
+                            Raw<E, CPL> kj[8];
+                            float dj[8][CPL];
+                            const lds_t *kbase = sKt + (FULL ? jb - 7 : 0) * L::QP + lane * CPL;
+                            const float *dbase = sDec + (FULL ? jb - 7 : 0) * L::DP + lane * CPL;
 #pragma unroll
-                        for (int t = 0; t < 8; ++t) {
-                            const int j = jb - t;
-                            const bool ok = j >= 0;
-                            const int jj = ok ? j : 0;
-                            float pt = 0.f;
-#pragma unroll
-                            for (int u = 0; u < CPL; ++u) {
-                                const int col = lane * CPL + u;
-                                pt += qi[u] * E::l2f(sKt[jj * L::QP + col]) * pr[u];
-                                pr[u] *= ok ? sDec[jj * L::DP + col] : 1.f;   // exp(g_j + ... + g_i) for j-1
+                            for (int t = 0; t < 8; ++t) {
+                                const int rr = FULL ? 7 - t : max(jb - t, 0);   // row offset from the base
+                                kj[t].x = *reinterpret_cast<const decltype(kj[t].x) *>(kbase + rr * L::QP);
+                                if constexpr (CPL == 2) {
+                                    typedef float f2_t __attribute__((ext_vector_type(2)));
+                                    const f2_t d2 = *reinterpret_cast<const f2_t *>(dbase + rr * L::DP);
+                                    dj[t][0] = d2.x;
+                                    dj[t][1] = d2.y;
+                                } else {
+                                    dj[t][0] = dbase[rr * L::DP];
+                                }
                             }
-                            part[t] = ok ? pt : 0.f;
-                        }
-                        // the 8 sums over the 64 lanes as one transposing butterfly:
-                        // at the xor-32, -16 and -8 steps each lane keeps the half of
-                        // its values its lane bit selects and adds the partner's copy
-                        // of them (the same pairs a plain butterfly adds, so the same
-                        // result), then three ordinary steps; lane bits 3..5 then name
-                        // the column t a lane holds
-                        const int h5 = (lane >> 5) & 1, h4 = (lane >> 4) & 1, h3 = (lane >> 3) & 1;
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) {
+                                const bool ok = FULL || jb - t >= 0;
+                                float pt = 0.f;
+#pragma unroll
+                                for (int u = 0; u < CPL; ++u) {
+                                    pt = __builtin_fmaf(qp[u], kj[t].get(u), pt);
+                                    qp[u] *= ok ? dj[t][u] : 1.f;   // times exp(g_j): the factor for column j-1
+                                }
+                                part[t] = ok ? pt : 0.f;
+                            }
+                        };
+                        if (jb >= 7) group(std::true_type{});
+                        else group(std::false_type{});
+                        // the 8 sums over the 64 lanes as one transposing butterfly,
+                        // all in VALU cross-lane operations (no LDS permutes): at the
+                        // xor-32, -16 and -8 steps each lane keeps the half of its
+                        // values its lane bit selects and adds the partner's copy of
+                        // them.  A permlane32 (permlane16) swap of the two halves'
+                        // registers exchanges the upper 32 lanes of the first with the
+                        // lower 32 of the second (odd with even 16-lane rows), after
+                        // which the two registers hold exactly keep and the partner's
+                        // copy; the xor-8 partner is a DPP rotate by 8 within each row.
+                        // Then each 8-lane group is summed by DPP (xor 1, xor 2, and
+                        // the mirror within 8 lanes); lane bits 3..5 name the column t
+                        // a lane holds
+                        const int h3 = (lane >> 3) & 1, h4 = (lane >> 4) & 1, h5 = (lane >> 5) & 1;
                         float r4[4], r2[2];
 #pragma unroll
                         for (int k2 = 0; k2 < 4; ++k2) {
-                            const float keep = h5 ? part[k2 + 4] : part[k2];
-                            const float send = h5 ? part[k2] : part[k2 + 4];
-                            r4[k2] = keep + __shfl_xor(send, 32, 64);
+                            const auto sw = __builtin_amdgcn_permlane32_swap(
+                                __float_as_uint(part[k2]), __float_as_uint(part[k2 + 4]), false, false);
+                            r4[k2] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                         }
 #pragma unroll
                         for (int k2 = 0; k2 < 2; ++k2) {
-                            const float keep = h4 ? r4[k2 + 2] : r4[k2];
-                            const float send = h4 ? r4[k2] : r4[k2 + 2];
-                            r2[k2] = keep + __shfl_xor(send, 16, 64);
+                            const auto sw = __builtin_amdgcn_permlane16_swap(
+                                __float_as_uint(r4[k2]), __float_as_uint(r4[k2 + 2]), false, false);
+                            r2[k2] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                         }
                         float sum;
                         {
                             const float keep = h3 ? r2[1] : r2[0];
                             const float send = h3 ? r2[0] : r2[1];
-                            sum = keep + __shfl_xor(send, 8, 64);
+                            sum = keep + __int_as_float(__builtin_amdgcn_update_dpp(
+                                             0, __float_as_int(send), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
                         }
-#pragma unroll
-                        for (int m = 4; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+                        sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0xB1 /* quad_perm 1,0,3,2 */, 0xf, 0xf, false));
+                        sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x4E /* quad_perm 2,3,0,1 */, 0xf, 0xf, false));
+                        sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x141 /* row_half_mirror */, 0xf, 0xf, false));
                         {
                             const int t = h3 + 2 * h4 + 4 * h5;   // (lane >> 3) & 7
                             const int j = jb - t;
@@ -585,12 +624,12 @@ chunk_kernel(const KernelParams p) {
                                 else p.dump[((bh * long(p.N) + c) * C + i) * C + j] = sc;
                             }
                         }
-                        // once every running product has underflowed to 0, every
-                        // further term is exactly 0 (decay factors are finite and
-                        // <= 1): write the remaining columns and stop
+                        // once every q-scaled running product has underflowed to 0,
+                        // every further term is exactly 0 (decay factors are finite
+                        // and <= 1): write the remaining columns and stop
                         bool live = false;
 #pragma unroll
-                        for (int u = 0; u < CPL; ++u) live |= pr[u] != 0.f;
+                        for (int u = 0; u < CPL; ++u) live |= qp[u] != 0.f;
                         if (__ballot(live) == 0) {
                             for (int j = jb - 8 - lane; j >= 0; j -= 64) {
                                 if constexpr (kOut) sA[i * L::TP + j] = E::f2l(0.f);
