@@ -53,7 +53,6 @@ template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int PAD = es == 2 ? 32 : 16;   // row pad (bytes)
     static constexpr int QP = D + PAD / es;  // Qh / Kt row pitch (elements)
     static constexpr int TP = C + PAD / es;  // Kht / Vt / A row pitch (elements)
-    static constexpr int DP = D + 4;         // decay tile row pitch (floats)
     // output pass: v rows staged row-major by direct loads; bf16 rows padded
     // by 32 bytes so the transposing fragment reads hit distinct banks
     static constexpr int VP = es == 2 ? D * 2 + 32 : D * 4;   // bytes
@@ -64,8 +63,8 @@ template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int kht = kt + (scores ? C * QP * es : 0);
     static constexpr int vt = kht + (state ? D * TP * es : 0);             // state pass: v^T
     static constexpr int a = vt + (MODE == MODE_SEG ? D * TP * es : 0);
-    static constexpr int dec = a + (MODE == MODE_OUT ? C * TP * es : 0);
-    static constexpr int btot = dec + (scores ? C * DP * 4 : 0);   // float [2][NW][D]
+    static constexpr int qb = a + (MODE == MODE_OUT ? C * TP * es : 0);   // exact path: q^ (block references)
+    static constexpr int btot = qb + (scores ? C * QP * es : 0);   // float [2][NW][D]
     static constexpr int eg = btot + 2 * NW * D * 4;              // float [D] exp2(Gamma)
     static constexpr int bytes = eg + D * 4;
     static constexpr int gbytes = C * D * 4;                        // gate rows
@@ -73,6 +72,41 @@ template <typename E, int D, int C, int MODE> struct Layout {
     static_assert(bytes + gbytes + vbytes <= 163840, "LDS");
 };
 
+
+// The sums over the 64 lanes of eight values part[0..7], one transposing
+// butterfly in VALU cross-lane operations (no LDS permutes): at the xor-32,
+// -16 and -8 steps each lane keeps the half of its values its lane bit
+// selects and adds the partner's copy of them.  A permlane32 (permlane16)
+// swap of the two halves' registers exchanges the upper 32 lanes of the
+// first with the lower 32 of the second (odd with even 16-lane rows), after
+// which the two registers hold exactly the kept values and the partner's
+// copy; the xor-8 partner is a DPP rotate by 8 within each row.  Each 8-lane
+// group is then summed by DPP (xor 1, xor 2, the mirror within 8 lanes).
+// Returns the total of part[t] for t = (lane >> 3) & 7, in every lane.
+__device__ __forceinline__ float reduce8(const float (&part)[8], int lane) {
+    float r4[4], r2[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[k2]), __float_as_uint(part[k2 + 4]),
+                                                         false, false);
+        r4[k2] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(r4[k2]), __float_as_uint(r4[k2 + 2]),
+                                                         false, false);
+        r2[k2] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const bool h3 = (lane >> 3) & 1;
+    const float keep = h3 ? r2[1] : r2[0];
+    const float send = h3 ? r2[0] : r2[1];
+    float sum = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x128 /* row_ror:8 */,
+                                                                  0xf, 0xf, false));
+    sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0xB1 /* quad_perm 1,0,3,2 */, 0xf, 0xf, false));
+    sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x4E /* quad_perm 2,3,0,1 */, 0xf, 0xf, false));
+    sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x141 /* row_half_mirror */, 0xf, 0xf, false));
+    return sum;
+}
 
 // Two ways to form a chunk's scores, chosen per chunk (uniformly over the
 // work-group: every wave holds all key dims of the chunk totals):
@@ -121,7 +155,7 @@ chunk_kernel(const KernelParams p) {
     __shared__ __attribute__((aligned(16))) float sG[SG ? C : C * D];          // gate rows
     __shared__ __attribute__((aligned(16))) unsigned char sV[L::vbytes];       // v rows (pitch L::VP)
     lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);      // scaled scores, row-major
-    float *sDec = reinterpret_cast<float *>(smem + L::dec);  // exact path: exp(g) per token
+    lds_t *sQb = reinterpret_cast<lds_t *>(smem + L::qb);    // exact path: scale q exp(Gc - r_block), permuted cols
     float *sBtot = reinterpret_cast<float *>(smem + L::btot);
     float *sEG = reinterpret_cast<float *>(smem + L::eg);
 
@@ -365,27 +399,11 @@ chunk_kernel(const KernelParams p) {
         for (int u = 0; u < CPL; ++u) wide |= -gam[u] > kSpanGuard;
         const bool fast = __ballot(wide) == 0;
 
-        // rows of the exact path. A row runs until its running decay products
-        // underflow (a product that has decayed by 2^149 is below the smallest
-        // fp32 subnormal; at a dim's average rate that takes 149 C / -gam
-        // tokens). When the least-decaying key dim keeps rows alive for more
-        // than about 16 tokens (its chunk total above -kPairSpan, log2 units),
-        // late rows cost far more than early ones: wave w then takes rows
-        // RPW/2 w + m and their mirror images C - 1 - (RPW/2 w + m), m < RPW/2
-        // (the same number of (i, j) pairs for every wave), and re-reads their
-        // raw q from the cache below (rows past T read 0). Otherwise each wave
-        // keeps its own rows. The choice is the same in every wave.
-        constexpr float kPairSpan = 149.f * C / 16;
-        bool longrows = false;
-#pragma unroll
-        for (int u = 0; u < CPL; ++u) longrows |= gam[u] > -kPairSpan;
-        const bool pair = __ballot(longrows) != 0;
-        auto exact_row = [&](int il) {
-            constexpr int H2 = RPW / 2;
-            const int a = H2 * w + (il < H2 ? il : il - H2);
-            return !pair ? r0 + il : il < H2 ? a : C - 1 - a;
-        };
-
+        // exact path: the chunk's 16-row blocks.  Wave w's rows lie in block
+        // w / WPB; the block's waves before / after it contribute gate sums
+        // (log2) to the block-referenced exponents below.
+        constexpr int WPB = 16 / RPW;   // waves per 16-row block
+        const int hw = w % WPB;         // this wave's place in its block
         // ---- operand tiles into LDS -----------------------------------------
         float eg[CPL];
 #pragma unroll
@@ -395,6 +413,7 @@ chunk_kernel(const KernelParams p) {
         }
         if constexpr (kScores) {
             float kh[CPL][RPW];
+            float kb_[RPW][CPL];   // exact path: k^_j (block-end reference)
             if (fast) {
 #pragma unroll
                 for (int i = 0; i < RPW; ++i) {
@@ -410,34 +429,50 @@ chunk_kernel(const KernelParams p) {
                     store_row(sKt, r0 + i, kt);
                 }
             } else {
-#pragma unroll
-                for (int u = 0; u < CPL; ++u) aw[u] = rows_after(u);
+                // Sub-block references (every factor <= 1): per 16-row block I,
+                // r_I = Gc at the row before the block, and per row
+                //   q^_i = scale q_i exp2(Gc_i - r_I)     (tile sQb, permuted),
+                //   k^_j = k_j exp2(r_{J+1} - Gc_j)       (tile sKt, permuted),
+                // so a score tile (I, J) is q^_I diag(exp2(r_I - r_{J+1})) k^_J^T;
+                // the inter-chunk term and the state update keep the chunk-start
+                // and chunk-end references (sQh, sKht), which are <= 1 for any gates.
+                // Exponents are sums of gates of one sign, never differences.
+                float bef[CPL], aft[CPL];   // gates of the block's rows before / after this wave's
 #pragma unroll
                 for (int u = 0; u < CPL; ++u) {
-                    float suf = aw[u];   // rows after i within the chunk: exponent <= 0
+                    bef[u] = 0.f;
+                    aft[u] = 0.f;
+#pragma unroll
+                    for (int j = 0; j < WPB; ++j) {
+                        const float t = sBtot[(buf * NW + (w - hw + j)) * D + lane * CPL + u];
+                        if (j < hw) bef[u] += t;
+                        if (j > hw) aft[u] += t;
+                    }
+                    aw[u] = rows_after(u);
+                }
+#pragma unroll
+                for (int u = 0; u < CPL; ++u) {
+                    float suf = aw[u], sufb = aft[u];   // rows after i: in the chunk / in the block
 #pragma unroll
                     for (int i = RPW - 1; i >= 0; --i) {
                         kh[u][i] = rk[i].get(u) * fexp2(suf);
-                        suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
+                        kb_[i][u] = rk[i].get(u) * fexp2(sufb);
+                        const float gl = rg[i].get(u) * kLog2e;
+                        suf += gl;
+                        sufb += gl;
                     }
                 }
 #pragma unroll
                 for (int i = 0; i < RPW; ++i) {
-                    float qh[CPL];
+                    float qh[CPL], qb[CPL];
 #pragma unroll
-                    for (int u = 0; u < CPL; ++u) qh[u] = rq[i].get(u) * (p.scale * fexp2(rw[u] + Pf[i][u]));
-                    // raw k and the token's decay factors, natural column order: this
-                    // lane's CPL key dims are adjacent, so each goes as one store
-                    // (and is read back as one load below)
-                    *reinterpret_cast<decltype(rk[i].x) *>(sKt + (r0 + i) * L::QP + lane * CPL) = rk[i].x;
-                    if constexpr (CPL == 2) {
-                        typedef float f2_t __attribute__((ext_vector_type(2)));
-                        *reinterpret_cast<f2_t *>(sDec + (r0 + i) * L::DP + lane * 2) =
-                            f2_t{fexp2(rg[i].get(0) * kLog2e), fexp2(rg[i].get(1) * kLog2e)};
-                    } else {
-                        sDec[(r0 + i) * L::DP + lane] = fexp2(rg[i].get(0) * kLog2e);
+                    for (int u = 0; u < CPL; ++u) {
+                        qh[u] = rq[i].get(u) * (p.scale * fexp2(rw[u] + Pf[i][u]));
+                        qb[u] = rq[i].get(u) * (p.scale * fexp2(bef[u] + Pf[i][u]));
                     }
                     store_row(sQh, r0 + i, qh);
+                    store_row(sQb, r0 + i, qb);
+                    store_row(sKt, r0 + i, kb_[i]);
                 }
             }
             if constexpr (kOut) {
@@ -458,29 +493,6 @@ chunk_kernel(const KernelParams p) {
         }
 #pragma unroll
         for (int u = 0; u < CPL; ++u) seg_gamma[u] += gam[u];
-
-        // the exact rows' q as floats, materialised here (the empty asm makes
-        // the wait for re-read rows happen before the prefetch below is
-        // issued, not at their first use behind it)
-        float qx[RPW][CPL];
-        if constexpr (kScores) {
-            if (!fast) {
-                Raw<E, CPL> qe[RPW];
-                if (pair) {
-#pragma unroll
-                    for (int il = 0; il < RPW; ++il)
-                        qe[il].load(bq, ((c * C + exact_row(il)) * D + lane * CPL) * es, 0);
-                }
-#pragma unroll
-                for (int il = 0; il < RPW; ++il)
-#pragma unroll
-                    for (int u = 0; u < CPL; ++u) {
-                        if (pair) qx[il][u] = qe[il].get(u);
-                        else qx[il][u] = rq[il].get(u);
-                        __asm__ __volatile__("" : "+v"(qx[il][u]));
-                    }
-            }
-        }
 
         // prefetch the next chunk's gates (score modes) and q / k rows; the
         // loads fly during the matrix work below
@@ -521,127 +533,169 @@ chunk_kernel(const KernelParams p) {
                             if ((I * NB + J) % NW == w) sink_tile(c, I, J, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 }
             } else {
-                // the wave's exact rows, elementwise: running product over j = i..0
-#pragma unroll 1
-                for (int il = 0; il < RPW; ++il) {
-                    const int i = exact_row(il);
-                    // qp: q_i times the running decay product exp(g_{j+1} + ... + g_i)
-                    // of the column j about to be added (starts at q_i for j = i)
-                    float qp[CPL];
+                // Per-block sums of the chunk's gates (log2), B_K = sum of the
+                // wave totals of block K, for key dims d0..d0+3 (f32x4).
+                auto blk4 = [&](int K, int d0) {
+                    f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < WPB; ++j)
+                        t += *reinterpret_cast<const f32x4_t *>(sBtot + (buf * NW + K * WPB + j) * D + d0);
+                    return t;
+                };
+                // Diagonal blocks whose own span stays within the guard in every
+                // key dim take the MFMA form too (one bit per block, the same in
+                // every wave); the others are formed elementwise by their rows' waves.
+                unsigned diag_mma = 0;
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    bool wide_blk = false;
 #pragma unroll
                     for (int u = 0; u < CPL; ++u) {
-                        qp[u] = 0.f;
+                        float t = 0.f;
 #pragma unroll
-                        for (int x = 0; x < RPW; ++x)
-                            if (x == il) qp[u] = qx[x][u];
+                        for (int j = 0; j < WPB; ++j) t += sBtot[(buf * NW + I * WPB + j) * D + lane * CPL + u];
+                        wide_blk |= -t > kSpanGuard;
                     }
-                    // columns j = i, i-1, .. in groups of 8: the 8 cross-lane sums of
-                    // a group are independent and run interleaved (one at a time,
-                    // each waited for the previous one's shuffle chain)
-                    for (int jb = i; jb >= 0; jb -= 8) {
-                        // rows j = jb .. jb-7: raw k and decay factors of this lane's
-                        // key dims, one load each, all eight rows' loads issued before
-                        // any is used.  A full group (jb >= 7) addresses its rows from
-                        // one base (row jb-7) with constant offsets and needs no masks;
-                        // the row's last, partial group (its first columns) reads row
-                        // 0 for columns before the chunk and masks them.
-                        float part[8];
-                        auto group = [&](auto fullc) {
-                            constexpr bool FULL = decltype(fullc)::value;
-                            Raw<E, CPL> kj[8];
-                            float dj[8][CPL];
-                            const lds_t *kbase = sKt + (FULL ? jb - 7 : 0) * L::QP + lane * CPL;
-                            const float *dbase = sDec + (FULL ? jb - 7 : 0) * L::DP + lane * CPL;
+                    if (__ballot(wide_blk) == 0) diag_mma |= 1u << I;
+                }
+                // tile (I, J) = k^_J diag(m) q^_I^T with m = exp2(r_I - r_{J+1}) per key
+                // dim: 1 for I = J + 1, the gates of blocks J+1 .. I-1 (<= 1) further
+                // below, exp2(-B_I) (<= 2^kSpanGuard) on the diagonal; m scales the
+                // k^ fragment (its 8 positions are key dims d0..d0+3, d0+16..d0+19)
 #pragma unroll
-                            for (int t = 0; t < 8; ++t) {
-                                const int rr = FULL ? 7 - t : max(jb - t, 0);   // row offset from the base
-                                kj[t].x = *reinterpret_cast<const decltype(kj[t].x) *>(kbase + rr * L::QP);
-                                if constexpr (CPL == 2) {
-                                    typedef float f2_t __attribute__((ext_vector_type(2)));
-                                    const f2_t d2 = *reinterpret_cast<const f2_t *>(dbase + rr * L::DP);
-                                    dj[t][0] = d2.x;
-                                    dj[t][1] = d2.y;
-                                } else {
-                                    dj[t][0] = dbase[rr * L::DP];
+                for (int t = 0; t < NTILE; ++t) {
+                    if (t % NW != w) continue;
+                    int I = 0, J = t;
+#pragma unroll
+                    for (int r = 0; r < NB; ++r)
+                        if (J > r) { J -= r + 1; I = r + 1; }
+                    if (I == J && !((diag_mma >> I) & 1u)) continue;
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int pos = ks * 32 + 8 * q4;
+                        frag_t kf = E::ld_frag(sKt + (16 * J + n16) * L::QP + pos);
+                        if (I != J + 1) {
+                            const int d0 = ks * 32 + 4 * q4;
+                            f32x4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+                            if (I == J) {
+                                x0 = -blk4(I, d0);
+                                x1 = -blk4(I, d0 + 16);
+                            } else {
+                                for (int K = J + 1; K < I; ++K) {
+                                    x0 += blk4(K, d0);
+                                    x1 += blk4(K, d0 + 16);
                                 }
                             }
+                            float kv[8];
+                            E::unpack(kf, kv);
 #pragma unroll
-                            for (int t = 0; t < 8; ++t) {
-                                const bool ok = FULL || jb - t >= 0;
-                                float pt = 0.f;
-#pragma unroll
-                                for (int u = 0; u < CPL; ++u) {
-                                    pt = __builtin_fmaf(qp[u], kj[t].get(u), pt);
-                                    qp[u] *= ok ? dj[t][u] : 1.f;   // times exp(g_j): the factor for column j-1
-                                }
-                                part[t] = ok ? pt : 0.f;
+                            for (int e = 0; e < 4; ++e) {
+                                kv[e] *= fexp2(x0[e]);
+                                kv[4 + e] *= fexp2(x1[e]);
                             }
-                        };
-                        if (jb >= 7) group(std::true_type{});
-                        else group(std::false_type{});
-                        // the 8 sums over the 64 lanes as one transposing butterfly,
-                        // all in VALU cross-lane operations (no LDS permutes): at the
-                        // xor-32, -16 and -8 steps each lane keeps the half of its
-                        // values its lane bit selects and adds the partner's copy of
-                        // them.  A permlane32 (permlane16) swap of the two halves'
-                        // registers exchanges the upper 32 lanes of the first with the
-                        // lower 32 of the second (odd with even 16-lane rows), after
-                        // which the two registers hold exactly keep and the partner's
-                        // copy; the xor-8 partner is a DPP rotate by 8 within each row.
-                        // Then each 8-lane group is summed by DPP (xor 1, xor 2, and
-                        // the mirror within 8 lanes); lane bits 3..5 name the column t
-                        // a lane holds
-                        const int h3 = (lane >> 3) & 1, h4 = (lane >> 4) & 1, h5 = (lane >> 5) & 1;
-                        float r4[4], r2[2];
+                            kf = E::pack(kv);
+                        }
+                        acc = E::mma(kf, E::ld_frag(sQb + (16 * I + n16) * L::QP + pos), acc);
+                    }
+                    if (I == J) {
 #pragma unroll
-                        for (int k2 = 0; k2 < 4; ++k2) {
-                            const auto sw = __builtin_amdgcn_permlane32_swap(
-                                __float_as_uint(part[k2]), __float_as_uint(part[k2 + 4]), false, false);
-                            r4[k2] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q4 + e > n16) acc[e] = 0.f;
+                    }
+                    sink_tile(c, I, J, acc);
+                }
+                if constexpr (kIntra) {  // zero tiles above the diagonal
 #pragma unroll
-                        for (int k2 = 0; k2 < 2; ++k2) {
-                            const auto sw = __builtin_amdgcn_permlane16_swap(
-                                __float_as_uint(r4[k2]), __float_as_uint(r4[k2 + 2]), false, false);
-                            r2[k2] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                        }
-                        float sum;
-                        {
-                            const float keep = h3 ? r2[1] : r2[0];
-                            const float send = h3 ? r2[0] : r2[1];
-                            sum = keep + __int_as_float(__builtin_amdgcn_update_dpp(
-                                             0, __float_as_int(send), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
-                        }
-                        sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0xB1 /* quad_perm 1,0,3,2 */, 0xf, 0xf, false));
-                        sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x4E /* quad_perm 2,3,0,1 */, 0xf, 0xf, false));
-                        sum += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x141 /* row_half_mirror */, 0xf, 0xf, false));
-                        {
-                            const int t = h3 + 2 * h4 + 4 * h5;   // (lane >> 3) & 7
-                            const int j = jb - t;
-                            if ((lane & 7) == 0 && j >= 0) {
+                    for (int I = 0; I < NB; ++I)
+#pragma unroll
+                        for (int J = I + 1; J < NB; ++J)
+                            if ((I * NB + J) % NW == w) sink_tile(c, I, J, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                }
+                // The wave's block, elementwise, when its span passes the guard:
+                // A_ij = sum_d q_i k_j prod_{r=j+1..i} exp(g_r) for columns j of
+                // the block up to i, from the raw rows of the block (re-read from
+                // the cache; rows past T read 0) with running products of
+                // per-token decays (factors in (0, 1]).  The block's waves take
+                // its rows in turn (row li to wave li % WPB), which evens out
+                // their column counts; each wave's rows are unrolled so that
+                // every column bound is a constant.
+                const int Iw = w / WPB;
+                const int rb = 16 * Iw;   // the block's first chunk row
+                if (!((diag_mma >> Iw) & 1u)) {
+                    Raw<E, CPL> kr[16], qr[RPW];
+                    RawG<CPL> gr[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        kr[r].load(bk, ((c * C + rb + r) * D + lane * CPL) * es, 0);
+                        if constexpr (SG) gr[r].load_one(bg, (c * C + rb + r) * 4, 0);
+                        else gr[r].load(bg, ((c * C + rb + r) * D + lane * CPL) * 4, 0);
+                    }
+#pragma unroll
+                    for (int il = 0; il < RPW; ++il)
+                        qr[il].load(bq, ((c * C + rb + hw + WPB * il) * D + lane * CPL) * es, 0);
+                    float dc[16][CPL];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+#pragma unroll
+                        for (int u = 0; u < CPL; ++u) dc[r][u] = fexp2(gr[r].get(u) * kLog2e);
+                    auto rows = [&](auto hc) {
+                        constexpr int HW = decltype(hc)::value;
+#pragma unroll
+                        for (int il = 0; il < RPW; ++il) {
+                            const int li = HW + WPB * il;   // row within the block
+                            const int i = rb + li;
+                            float qp[CPL];   // q_i times the running decay product
+#pragma unroll
+                            for (int u = 0; u < CPL; ++u) qp[u] = qr[il].get(u);
+                            // columns jl = li .. 0 in two groups of 8, group g holding
+                            // columns 15 - 8 g - t (t = 0..7); rows in the block's
+                            // first half have no column in group 0, and once every
+                            // q-scaled running product has underflowed to 0 the rest
+                            // of the row is exactly 0.  A group's columns past li
+                            // sum to 0, the value those causal-mask entries hold, so
+                            // every lane stores (the 8 lanes of a column the same value)
+                            auto emit = [&](int g2, float sum) {
+                                const int jl = 15 - 8 * g2 - (lane >> 3);
                                 const float sc = sum * p.scale;
-                                if constexpr (kOut) sA[i * L::TP + j] = E::f2l(sc);
-                                else p.dump[((bh * long(p.N) + c) * C + i) * C + j] = sc;
-                            }
-                        }
-                        // once every q-scaled running product has underflowed to 0,
-                        // every further term is exactly 0 (decay factors are finite
-                        // and <= 1): write the remaining columns and stop
-                        bool live = false;
+                                if constexpr (kOut) sA[i * L::TP + rb + jl] = E::f2l(sc);
+                                else p.dump[((bh * long(p.N) + c) * C + i) * C + rb + jl] = sc;
+                            };
+                            auto run_group = [&](auto gc) {
+                                constexpr int G2 = decltype(gc)::value;
+                                float part[8];
 #pragma unroll
-                        for (int u = 0; u < CPL; ++u) live |= qp[u] != 0.f;
-                        if (__ballot(live) == 0) {
-                            for (int j = jb - 8 - lane; j >= 0; j -= 64) {
-                                if constexpr (kOut) sA[i * L::TP + j] = E::f2l(0.f);
-                                else p.dump[((bh * long(p.N) + c) * C + i) * C + j] = 0.f;
+                                for (int t = 0; t < 8; ++t) {
+                                    const int jl = 15 - 8 * G2 - t;
+                                    part[t] = 0.f;
+                                    if (jl <= li) {
+#pragma unroll
+                                        for (int u = 0; u < CPL; ++u) {
+                                            part[t] = __builtin_fmaf(qp[u], kr[jl].get(u), part[t]);
+                                            qp[u] *= dc[jl][u];   // times exp(g_jl): the factor for column jl-1
+                                        }
+                                    }
+                                }
+                                emit(G2, reduce8(part, lane));
+                            };
+                            bool live = true;
+                            if (li >= 8) {
+                                run_group(std::integral_constant<int, 0>{});
+                                bool any = false;
+#pragma unroll
+                                for (int u = 0; u < CPL; ++u) any |= qp[u] != 0.f;
+                                live = __ballot(any) != 0;
                             }
-                            break;
+                            if (live) run_group(std::integral_constant<int, 1>{});
+                            else emit(1, 0.f);
+                            if constexpr (kIntra) {
+                                for (int j = i + 1 + lane; j < C; j += 64)
+                                    if (j < rb + 16) p.dump[((bh * long(p.N) + c) * C + i) * C + j] = 0.f;
+                            }
                         }
-                    }
-                    if constexpr (kIntra) {
-                        for (int j = i + 1 + lane; j < C; j += 64)
-                            p.dump[((bh * long(p.N) + c) * C + i) * C + j] = 0.f;
-                    }
+                    };
+                    if (WPB == 1 || hw == 0) rows(std::integral_constant<int, 0>{});
+                    else rows(std::integral_constant<int, WPB - 1>{});
                 }
             }
         }
