@@ -227,7 +227,7 @@ size_t forward_workspace_bytes(const Call &c) {
         target = g_target_wgs;
         hg = g_head_group;
     }
-    const int spc = gla::state_units_per_cu(c.dtype, D, c.chunk);
+    const int spc = gla::state_units_per_cu(c.dtype, D, gla::state_chunk(c.dtype, c.chunk));
     long group = hg > 0 ? std::min<long>(hg, BH) : BH;
     group = std::min<long>(group, 65535);
     size_t need = 0;
@@ -263,8 +263,8 @@ int run_forward(Call &c, float *fixed_ws = nullptr, size_t fixed_cap = 0) {
         hg = g_head_group;
     }
     // chunk length of the state pass (state units end on output-chunk
-    // boundaries, so it may differ from the output pass's; it is the same here)
-    const int cs = c.chunk;
+    // boundaries, so it may differ from the output pass's)
+    const int cs = gla::state_chunk(c.dtype, c.chunk);
     const int spc = gla::state_units_per_cu(c.dtype, D, cs);
     long group = hg > 0 ? std::min<long>(hg, BH) : BH;
     group = std::min<long>(group, 65535);

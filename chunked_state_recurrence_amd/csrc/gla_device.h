@@ -296,8 +296,8 @@ __device__ __forceinline__ int perm_col(int c) {
 // least one 16-wide tile of value columns, else 16 rows per wave.
 template <int D, int C> struct Shape {
     static constexpr int NW = (C / 8 < D / 16) ? C / 8 : D / 16;
-    static constexpr int RPW = C / NW;   // chunk rows per wave (8 or 16)
-    static_assert(RPW == 8 || RPW == 16, "unsupported chunk / head-dim pair");
+    static constexpr int RPW = C / NW;   // chunk rows per wave (8, 16 or 32)
+    static_assert(RPW == 8 || RPW == 16 || RPW == 32, "unsupported chunk / head-dim pair");
 };
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -75,6 +75,9 @@ hipError_t launch_gdn_prep(int D, const GdnParams &p, int slices, hipStream_t s)
 hipError_t launch_gdn_walk(int D, const GdnParams &p, hipStream_t s);
 
 bool chunk_supported(int dtype, int D, int C);
+// chunk length of the state pass for an output-pass chunk of C tokens (it
+// divides C, so state units end on output-chunk boundaries)
+int state_chunk(int dtype, int C);
 // work-groups of the state pass that fit on one CU (LDS bound), 1 or 2
 int state_units_per_cu(int dtype, int D, int C);
 // scalar_gate: g is [B,H,T] (one log-decay per token), MODE_OUT / MODE_SEG only

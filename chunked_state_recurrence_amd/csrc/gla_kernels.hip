@@ -48,8 +48,19 @@ namespace gla {
 template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int es = sizeof(typename E::lds_t);
     static constexpr int NW = Shape<D, C>::NW;
+    static constexpr int RPW = Shape<D, C>::RPW;
+    // gate-sum units: each wave's rows, in pieces of at most 16 (one score block)
+    static constexpr int NU = C / (RPW < 16 ? RPW : 16);
     static constexpr bool scores = MODE == MODE_OUT || MODE == MODE_INTRA;
     static constexpr bool state = MODE == MODE_OUT || MODE == MODE_SEG;
+    // The large tiles (bf16 at C = 128, fp32 at D = 128 and C = 64) fit only
+    // with up to three savings: the exact path's block-referenced q^ written
+    // over the q tile (the output phase rescales its fragments), the gate rows
+    // loaded into registers instead of LDS, and (bf16, D = C = 128) the score
+    // tile written over the key tile once every wave has read it.
+    static constexpr bool qb_in_qh = C == 128 || (es == 4 && D == 128 && C == 64);
+    static constexpr bool greg = (es == 2 && D == 128 && C == 128) || (es == 4 && D == 128 && C == 64);
+    static constexpr bool a_in_kt = es == 2 && D == 128 && C == 128;
     static constexpr int PAD = es == 2 ? 32 : 16;   // row pad (bytes)
     static constexpr int QP = D + PAD / es;  // Qh / Kt row pitch (elements)
     static constexpr int TP = C + PAD / es;  // Kht / Vt / A row pitch (elements)
@@ -63,11 +74,13 @@ template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int kht = kt + (scores ? C * QP * es : 0);
     static constexpr int vt = kht + (state ? D * TP * es : 0);             // state pass: v^T
     static constexpr int a = vt + (MODE == MODE_SEG ? D * TP * es : 0);
-    static constexpr int qb = a + (MODE == MODE_OUT ? C * TP * es : 0);   // exact path: q^ (block references)
-    static constexpr int btot = qb + (scores ? C * QP * es : 0);   // float [2][NW][D]
-    static constexpr int eg = btot + 2 * NW * D * 4;              // float [D] exp2(Gamma)
+    static constexpr int qb = a + (MODE == MODE_OUT && !a_in_kt ? C * TP * es : 0);   // exact path: q^ (block references)
+    static constexpr int btot = qb + (scores && !qb_in_qh ? C * QP * es : 0);   // float [2][NU][D]
+    static constexpr int eg = btot + 2 * NU * D * 4;              // float [D] exp2(Gamma)
     static constexpr int bytes = eg + D * 4;
-    static constexpr int gbytes = C * D * 4;                        // gate rows
+    static constexpr int aoff = a_in_kt ? kt : a;                  // score tile
+    static constexpr int qboff = qb_in_qh ? qh : qb;               // exact path's q^ tile
+    static constexpr int gbytes = greg ? 16 : C * D * 4;            // gate rows
     static constexpr int vbytes = MODE == MODE_OUT ? E::tile_bytes(C, VP) : 16;   // output pass: v rows
     static_assert(bytes + gbytes + vbytes <= 163840, "LDS");
 };
@@ -133,6 +146,10 @@ chunk_kernel(const KernelParams p) {
     constexpr int KS = D / 32;             // 32-deep key steps
     constexpr int TS = C / 32;             // 32-deep token steps
     constexpr int NTILE = NB * (NB + 1) / 2;   // causal 16x16 score tiles
+    constexpr int UR = RPW < 16 ? RPW : 16;    // rows per gate-sum unit
+    constexpr int NU = C / UR;                 // gate-sum units per chunk
+    constexpr int UPW = RPW / UR;              // units per wave (1, or 2 at 32 rows)
+    constexpr int UPB = 16 / UR;               // units per 16-row block (2 at 8 rows per wave)
     static_assert(NTW >= 1 && TS >= 1 && CPL >= 1, "unsupported tile shape");
     constexpr bool kOut = MODE == MODE_OUT;
     constexpr bool kSeg = MODE == MODE_SEG;
@@ -152,10 +169,10 @@ chunk_kernel(const KernelParams p) {
     lds_t *sVt = reinterpret_cast<lds_t *>(smem + L::vt);    // state pass: v^T
     // Direct-load targets in arrays of their own, so the compiler can tell
     // that fragment reads elsewhere do not touch loads still landing here.
-    __shared__ __attribute__((aligned(16))) float sG[SG ? C : C * D];          // gate rows
+    __shared__ __attribute__((aligned(16))) float sG[L::greg ? 4 : (SG ? C : C * D)];   // gate rows
     __shared__ __attribute__((aligned(16))) unsigned char sV[L::vbytes];       // v rows (pitch L::VP)
-    lds_t *sA = reinterpret_cast<lds_t *>(smem + L::a);      // scaled scores, row-major
-    lds_t *sQb = reinterpret_cast<lds_t *>(smem + L::qb);    // exact path: scale q exp(Gc - r_block), permuted cols
+    lds_t *sA = reinterpret_cast<lds_t *>(smem + L::aoff);   // scaled scores, row-major
+    lds_t *sQb = reinterpret_cast<lds_t *>(smem + L::qboff); // exact path: scale q exp(Gc - r_block), permuted cols
     float *sBtot = reinterpret_cast<float *>(smem + L::btot);
     float *sEG = reinterpret_cast<float *>(smem + L::eg);
 
@@ -214,22 +231,34 @@ chunk_kernel(const KernelParams p) {
     // Issue counts per wave, for the explicit waits: gate rows (direct, 1 KB
     // per load; one load of RPW floats for scalar gates), register rows of
     // q / k (/ v in the state pass), v rows.
-    constexpr int NG = SG ? 1 : RPW * D * 4 / 1024;
+    constexpr int NG = L::greg ? RPW : (SG ? 1 : RPW * D * 4 / 1024);
     constexpr int NQK = (kScores ? RPW : 0) + (kCumsum ? 0 : RPW) + (kVreg ? RPW : 0);
     constexpr int NV = !kVdma ? 0 : (es == 2 ? RPW : RPW * D * 4 / 1024);
     static_assert(RPW * D * 4 % 1024 == 0, "gate rows per wave must fill whole loads");
-    // this wave's gate rows of chunk c into its rows of sG (rows past T read 0)
+    // this wave's gate rows of chunk c into its rows of sG, or into registers
+    // (rows past T read 0)
+    RawG<CPL> rgn[RPW];
     auto load_g = [&](int c) {
-        const int rbase = __builtin_amdgcn_readfirstlane((c * C + r0) * GD * 4);
-        float *dst = sG + __builtin_amdgcn_readfirstlane(r0 * GD);
-        mem_fence_compiler();
-        if constexpr (SG) {
-            if (lane < RPW) dma<4>(bg, reinterpret_cast<unsigned char *>(dst), lane * 4, rbase);
-        } else {
+        if constexpr (L::greg) {
 #pragma unroll
-            for (int i = 0; i < NG; ++i) dma<16>(bg, reinterpret_cast<unsigned char *>(dst) + i * 1024, lane * 16, rbase + i * 1024);
+            for (int i = 0; i < RPW; ++i) {
+                if constexpr (SG) rgn[i].load_one(bg, (c * C + r0) * 4, i * 4);
+                else rgn[i].load(bg, ((c * C + r0) * D + lane * CPL) * 4, i * D * 4);
+            }
+            mem_fence_compiler();
+        } else {
+            const int rbase = __builtin_amdgcn_readfirstlane((c * C + r0) * GD * 4);
+            float *dst = sG + __builtin_amdgcn_readfirstlane(r0 * GD);
+            mem_fence_compiler();
+            if constexpr (SG) {
+                if (lane < RPW) dma<4>(bg, reinterpret_cast<unsigned char *>(dst), lane * 4, rbase);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NG; ++i)
+                    dma<16>(bg, reinterpret_cast<unsigned char *>(dst) + i * 1024, lane * 16, rbase + i * 1024);
+            }
+            mem_fence_compiler();
         }
-        mem_fence_compiler();
     };
     // rows past T read as zero; row offsets go in the uniform soffset
     auto load_qkv = [&](int c) {
@@ -322,18 +351,25 @@ chunk_kernel(const KernelParams p) {
         RawG<CPL> rg[RPW];   // each wave reads back only the rows it loaded itself
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            if constexpr (SG) rg[i].fill(sG[r0 + i]);
+            if constexpr (L::greg) rg[i] = rgn[i];
+            else if constexpr (SG) rg[i].fill(sG[r0 + i]);
             else rg[i].x = *reinterpret_cast<const decltype(rg[i].x) *>(sG + (r0 + i) * D + lane * CPL);
         }
         float Pf[RPW][CPL];   // inclusive prefix within the wave's rows
+        float Pu[UPW > 1 ? RPW : 1][CPL];   // 32-row waves: inclusive prefix within the row's unit
         float Sw[RPW][CPL];   // state pass: suffix after the row within the wave's rows
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
-            float run = 0.f;
+            float run = 0.f, urun = 0.f;
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 run = __builtin_fmaf(rg[i].get(u), kLog2e, run);
                 Pf[i][u] = run;
+                if constexpr (UPW > 1) {   // each unit's total goes to its own slot
+                    urun = __builtin_fmaf(rg[i].get(u), kLog2e, i % UR == 0 ? 0.f : urun);
+                    Pu[i][u] = urun;
+                    if (i % UR == UR - 1) sBtot[(buf * NU + w * UPW + i / UR) * D + lane * CPL + u] = urun;
+                }
             }
             if constexpr (kSeg) {
                 float suf = 0.f;
@@ -343,11 +379,12 @@ chunk_kernel(const KernelParams p) {
                     suf = __builtin_fmaf(rg[i].get(u), kLog2e, suf);
                 }
             }
-            sBtot[(buf * NW + w) * D + lane * CPL + u] = run;
+            if constexpr (UPW == 1) sBtot[(buf * NU + w) * D + lane * CPL + u] = run;
         }
         // the gates are in registers: the next chunk's gate rows load during
-        // the rest of this chunk
-        if constexpr (!kCumsum) load_g(cn);
+        // the rest of this chunk (gate rows into registers wait for the q / k
+        // prefetch below, which keeps them out of the operand phase's registers)
+        if constexpr (!kCumsum && !L::greg) load_g(cn);
         block_sync();  // B1: wave totals visible
 
         // rows before the wave's, after them, all: before and all from one
@@ -358,17 +395,17 @@ chunk_kernel(const KernelParams p) {
         auto rows_after = [&](int u) {
             float after = 0.f;
 #pragma unroll
-            for (int j = 0; j < NW; ++j)
-                if (j > w) after += sBtot[(buf * NW + j) * D + lane * CPL + u];
+            for (int j = 0; j < NU; ++j)
+                if (j >= (w + 1) * UPW) after += sBtot[(buf * NU + j) * D + lane * CPL + u];
             return after;
         };
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
             float pre = 0.f, before = 0.f;
 #pragma unroll
-            for (int j = 0; j < NW; ++j) {
-                if (j == w) before = pre;
-                pre += sBtot[(buf * NW + j) * D + lane * CPL + u];
+            for (int j = 0; j < NU; ++j) {
+                if (j == w * UPW) before = pre;
+                pre += sBtot[(buf * NU + j) * D + lane * CPL + u];
             }
             rw[u] = before;
             gam[u] = pre;
@@ -402,8 +439,18 @@ chunk_kernel(const KernelParams p) {
         // exact path: the chunk's 16-row blocks.  Wave w's rows lie in block
         // w / WPB; the block's waves before / after it contribute gate sums
         // (log2) to the block-referenced exponents below.
-        constexpr int WPB = 16 / RPW;   // waves per 16-row block
+        constexpr int WPB = RPW < 16 ? 16 / RPW : 1;   // waves per 16-row block
+        constexpr int BPW = RPW > 16 ? RPW / 16 : 1;   // 16-row blocks per wave
         const int hw = w % WPB;         // this wave's place in its block
+        // per-block sums of the chunk's gates (log2), B_K = sum of the units of
+        // block K, for key dims d0..d0+3 (f32x4)
+        auto blk4 = [&](int K, int d0) {
+            f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < UPB; ++j)
+                t += *reinterpret_cast<const f32x4_t *>(sBtot + (buf * NU + K * UPB + j) * D + d0);
+            return t;
+        };
         // ---- operand tiles into LDS -----------------------------------------
         float eg[CPL];
 #pragma unroll
@@ -444,7 +491,7 @@ chunk_kernel(const KernelParams p) {
                     aft[u] = 0.f;
 #pragma unroll
                     for (int j = 0; j < WPB; ++j) {
-                        const float t = sBtot[(buf * NW + (w - hw + j)) * D + lane * CPL + u];
+                        const float t = sBtot[(buf * NU + (w - hw + j)) * D + lane * CPL + u];
                         if (j < hw) bef[u] += t;
                         if (j > hw) aft[u] += t;
                     }
@@ -455,6 +502,8 @@ chunk_kernel(const KernelParams p) {
                     float suf = aw[u], sufb = aft[u];   // rows after i: in the chunk / in the block
 #pragma unroll
                     for (int i = RPW - 1; i >= 0; --i) {
+                        if constexpr (UPW > 1)   // a unit's rows see only the gates after them in the unit
+                            if (i % UR == UR - 1) sufb = 0.f;
                         kh[u][i] = rk[i].get(u) * fexp2(suf);
                         kb_[i][u] = rk[i].get(u) * fexp2(sufb);
                         const float gl = rg[i].get(u) * kLog2e;
@@ -468,10 +517,10 @@ chunk_kernel(const KernelParams p) {
 #pragma unroll
                     for (int u = 0; u < CPL; ++u) {
                         qh[u] = rq[i].get(u) * (p.scale * fexp2(rw[u] + Pf[i][u]));
-                        qb[u] = rq[i].get(u) * (p.scale * fexp2(bef[u] + Pf[i][u]));
+                        qb[u] = rq[i].get(u) * (p.scale * fexp2(bef[u] + (UPW > 1 ? Pu[i][u] : Pf[i][u])));
                     }
-                    store_row(sQh, r0 + i, qh);
-                    store_row(sQb, r0 + i, qb);
+                    if constexpr (!L::qb_in_qh) store_row(sQh, r0 + i, qh);
+                    store_row(sQb, r0 + i, qb);   // over the q tile when qb_in_qh
                     store_row(sKt, r0 + i, kb_[i]);
                 }
             }
@@ -497,13 +546,24 @@ chunk_kernel(const KernelParams p) {
         // prefetch the next chunk's gates (score modes) and q / k rows; the
         // loads fly during the matrix work below
         load_qkv(cn);
+        if constexpr (L::greg && !kCumsum) load_g(cn);
         if constexpr (kVdma) wait_vmem<NG + NQK>();   // this chunk's v rows arrived (loads after them: next gates, q, k)
         block_sync();  // B2: operand tiles visible
 
         // ---- a2: causal score tiles -------------------------------------------
-        if constexpr (kScores) {
-            if (fast) {
-                // tile (I, J) = Kt[J] Qh[I]^T; tiles dealt round-robin to the waves
+        // With the score tile over the key tile, a wave holds its tiles in
+        // registers until every wave has read the key tile, then stores them
+        // with zero tiles right of the even diagonal tiles (the output phase's
+        // 32-deep token steps read those, and key rows are still there).
+        constexpr bool kHold = kOut && L::a_in_kt;
+        constexpr int MAXT = (NTILE + NW - 1) / NW;   // tiles per wave, at most
+        // body(slot, I, J) for this wave's tiles t = w, w + NW, ... (tile t is
+        // (I, J) in row-major order of the lower triangle).  Up to 10 tiles the
+        // loop runs over all of them with constant indices; the 36 tiles of a
+        // 128-token chunk would then put 36 tile bodies in every wave's code,
+        // so each wave walks only its own slots there.
+        auto for_my_tiles = [&](auto &&body) {
+            if constexpr (NB <= 4) {
 #pragma unroll
                 for (int t = 0; t < NTILE; ++t) {
                     if (t % NW != w) continue;
@@ -511,6 +571,42 @@ chunk_kernel(const KernelParams p) {
 #pragma unroll
                     for (int r = 0; r < NB; ++r)
                         if (J > r) { J -= r + 1; I = r + 1; }
+                    body(t / NW, I, J);
+                }
+            } else {
+#pragma unroll
+                for (int sl = 0; sl < MAXT; ++sl) {
+                    const int t = w + sl * NW;
+                    if (t >= NTILE) break;
+                    int I = 0, J = t;
+#pragma unroll
+                    for (int r = 0; r < NB; ++r)
+                        if (J > r) { J -= r + 1; I = r + 1; }
+                    body(sl, I, J);
+                }
+            }
+        };
+        f32x4_t held[kHold ? MAXT : 1];
+        auto put_tile = [&](int slot, int I, int J, f32x4_t acc) {
+            if constexpr (kHold) held[slot] = acc;
+            else sink_tile(c, I, J, acc);
+        };
+        auto flush_tiles = [&](unsigned diag_done) {
+            if constexpr (kHold) {
+                block_sync();   // every wave is done with the key tile
+                for_my_tiles([&](int slot, int I, int J) {
+                    if (I == J && !((diag_done >> I) & 1u)) return;
+                    sink_tile(c, I, J, held[slot]);
+                });
+#pragma unroll
+                for (int I = 0; I + 1 < NB; I += 2)
+                    if ((I * NB + I + 1) % NW == w) sink_tile(c, I, I + 1, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            }
+        };
+        if constexpr (kScores) {
+            if (fast) {
+                // tile (I, J) = Kt[J] Qh[I]^T; tiles dealt round-robin to the waves
+                for_my_tiles([&](int slot, int I, int J) {
                     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
@@ -523,8 +619,9 @@ chunk_kernel(const KernelParams p) {
                         for (int e = 0; e < 4; ++e)
                             if (4 * q4 + e > n16) acc[e] = 0.f;
                     }
-                    sink_tile(c, I, J, acc);
-                }
+                    put_tile(slot, I, J, acc);
+                });
+                flush_tiles(~0u);
                 if constexpr (kIntra) {  // zero tiles above the diagonal
 #pragma unroll
                     for (int I = 0; I < NB; ++I)
@@ -533,15 +630,6 @@ chunk_kernel(const KernelParams p) {
                             if ((I * NB + J) % NW == w) sink_tile(c, I, J, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 }
             } else {
-                // Per-block sums of the chunk's gates (log2), B_K = sum of the
-                // wave totals of block K, for key dims d0..d0+3 (f32x4).
-                auto blk4 = [&](int K, int d0) {
-                    f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int j = 0; j < WPB; ++j)
-                        t += *reinterpret_cast<const f32x4_t *>(sBtot + (buf * NW + K * WPB + j) * D + d0);
-                    return t;
-                };
                 // Diagonal blocks whose own span stays within the guard in every
                 // key dim take the MFMA form too (one bit per block, the same in
                 // every wave); the others are formed elementwise by their rows' waves.
@@ -553,7 +641,7 @@ chunk_kernel(const KernelParams p) {
                     for (int u = 0; u < CPL; ++u) {
                         float t = 0.f;
 #pragma unroll
-                        for (int j = 0; j < WPB; ++j) t += sBtot[(buf * NW + I * WPB + j) * D + lane * CPL + u];
+                        for (int j = 0; j < UPB; ++j) t += sBtot[(buf * NU + I * UPB + j) * D + lane * CPL + u];
                         wide_blk |= -t > kSpanGuard;
                     }
                     if (__ballot(wide_blk) == 0) diag_mma |= 1u << I;
@@ -562,14 +650,8 @@ chunk_kernel(const KernelParams p) {
                 // dim: 1 for I = J + 1, the gates of blocks J+1 .. I-1 (<= 1) further
                 // below, exp2(-B_I) (<= 2^kSpanGuard) on the diagonal; m scales the
                 // k^ fragment (its 8 positions are key dims d0..d0+3, d0+16..d0+19)
-#pragma unroll
-                for (int t = 0; t < NTILE; ++t) {
-                    if (t % NW != w) continue;
-                    int I = 0, J = t;
-#pragma unroll
-                    for (int r = 0; r < NB; ++r)
-                        if (J > r) { J -= r + 1; I = r + 1; }
-                    if (I == J && !((diag_mma >> I) & 1u)) continue;
+                for_my_tiles([&](int slot, int I, int J) {
+                    if (I == J && !((diag_mma >> I) & 1u)) return;
                     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
@@ -603,8 +685,9 @@ chunk_kernel(const KernelParams p) {
                         for (int e = 0; e < 4; ++e)
                             if (4 * q4 + e > n16) acc[e] = 0.f;
                     }
-                    sink_tile(c, I, J, acc);
-                }
+                    put_tile(slot, I, J, acc);
+                });
+                flush_tiles(diag_mma);
                 if constexpr (kIntra) {  // zero tiles above the diagonal
 #pragma unroll
                     for (int I = 0; I < NB; ++I)
@@ -619,11 +702,15 @@ chunk_kernel(const KernelParams p) {
                 // per-token decays (factors in (0, 1]).  The block's waves take
                 // its rows in turn (row li to wave li % WPB), which evens out
                 // their column counts; each wave's rows are unrolled so that
-                // every column bound is a constant.
-                const int Iw = w / WPB;
+                // every column bound is a constant.  (A 32-row wave takes its two
+                // blocks in turn.)
+                constexpr int RIB = 16 / WPB;   // rows of the block per wave
+#pragma unroll 1
+                for (int bb = 0; bb < BPW; ++bb) {
+                const int Iw = (w * RPW) / 16 + bb;
                 const int rb = 16 * Iw;   // the block's first chunk row
                 if (!((diag_mma >> Iw) & 1u)) {
-                    Raw<E, CPL> kr[16], qr[RPW];
+                    Raw<E, CPL> kr[16], qr[RIB];
                     RawG<CPL> gr[16];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -632,7 +719,7 @@ chunk_kernel(const KernelParams p) {
                         else gr[r].load(bg, ((c * C + rb + r) * D + lane * CPL) * 4, 0);
                     }
 #pragma unroll
-                    for (int il = 0; il < RPW; ++il)
+                    for (int il = 0; il < RIB; ++il)
                         qr[il].load(bq, ((c * C + rb + hw + WPB * il) * D + lane * CPL) * es, 0);
                     float dc[16][CPL];
 #pragma unroll
@@ -642,7 +729,7 @@ chunk_kernel(const KernelParams p) {
                     auto rows = [&](auto hc) {
                         constexpr int HW = decltype(hc)::value;
 #pragma unroll
-                        for (int il = 0; il < RPW; ++il) {
+                        for (int il = 0; il < RIB; ++il) {
                             const int li = HW + WPB * il;   // row within the block
                             const int i = rb + li;
                             float qp[CPL];   // q_i times the running decay product
@@ -679,7 +766,11 @@ chunk_kernel(const KernelParams p) {
                                 emit(G2, reduce8(part, lane));
                             };
                             bool live = true;
-                            if (li >= 8) {
+                            if (li < 8) {
+                                // the block's columns 8..15 lie right of the diagonal: zero,
+                                // which the key tile's rows under the score tile are not
+                                if constexpr (kHold) emit(0, 0.f);
+                            } else {
                                 run_group(std::integral_constant<int, 0>{});
                                 bool any = false;
 #pragma unroll
@@ -696,6 +787,7 @@ chunk_kernel(const KernelParams p) {
                     };
                     if (WPB == 1 || hw == 0) rows(std::integral_constant<int, 0>{});
                     else rows(std::integral_constant<int, WPB - 1>{});
+                }
                 }
             }
         }
@@ -744,11 +836,34 @@ chunk_kernel(const KernelParams p) {
                     for (int e = 0; e < 4; ++e) { x[e] = S[2 * ks][nt][e]; x[4 + e] = S[2 * ks + 1][nt][e]; }
                     sf[nt] = E::pack(x);
                 }
+                if (!L::qb_in_qh || fast) {
 #pragma unroll
-                for (int m = 0; m < NB; ++m) {
-                    const frag_t b = E::ld_frag(sQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
+                    for (int m = 0; m < NB; ++m) {
+                        const frag_t b = E::ld_frag(sQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) O[nt][m] = E::mma(sf[nt], b, O[nt][m]);
+                        for (int nt = 0; nt < NTW; ++nt) O[nt][m] = E::mma(sf[nt], b, O[nt][m]);
+                    }
+                } else {
+                    // exact chunk with q^ over the q tile: block m's rows hold
+                    // scale q exp2(Gc - r_m); times exp2(r_m) per key dim (r_m, the
+                    // gates of the blocks before m, <= 0) gives the chunk-start form
+                    const int d0 = ks * 32 + 4 * q4;
+                    f32x4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < NB; ++m) {
+                        float qv[8];
+                        E::unpack(E::ld_frag(sQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4), qv);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            qv[e] *= fexp2(x0[e]);
+                            qv[4 + e] *= fexp2(x1[e]);
+                        }
+                        const frag_t b = E::pack(qv);
+#pragma unroll
+                        for (int nt = 0; nt < NTW; ++nt) O[nt][m] = E::mma(sf[nt], b, O[nt][m]);
+                        x0 += blk4(m, d0);
+                        x1 += blk4(m, d0 + 16);
+                    }
                 }
             }
             // intra-chunk: O^T += V^T A^T over causal token steps
@@ -1263,13 +1378,17 @@ hipError_t launch_bwd_segments(int D, int C, const KernelParams &p, int grid_x, 
     return hipErrorInvalidValue;
 }
 
+// Chunk 128 has no state pass of its own: its state units run on 64-token
+// chunks (state_chunk below).
 template <typename E, int D, int C>
 static hipError_t dispatch_mode(int mode, bool sg, const KernelParams &p, int gx, int gy, hipStream_t s) {
+    constexpr bool seg_ok = C <= 64;
     if (sg) {   // scalar gates: the fused output pass and the state pass only
         switch (mode) {
             case MODE_OUT: return launch_one<E, D, C, MODE_OUT, true>(p, gx, gy, s);
             case MODE_SEG:
-                if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C, true>(p, gx, gy, s);
+                if constexpr (!seg_ok) return hipErrorInvalidValue;
+                else if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C, true>(p, gx, gy, s);
                 else return launch_one<E, D, C, MODE_SEG, true>(p, gx, gy, s);
             default: return hipErrorInvalidValue;
         }
@@ -1277,7 +1396,8 @@ static hipError_t dispatch_mode(int mode, bool sg, const KernelParams &p, int gx
     switch (mode) {
         case MODE_OUT: return launch_one<E, D, C, MODE_OUT, false>(p, gx, gy, s);
         case MODE_SEG:
-            if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C, false>(p, gx, gy, s);
+            if constexpr (!seg_ok) return hipErrorInvalidValue;
+            else if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C, false>(p, gx, gy, s);
             else return launch_one<E, D, C, MODE_SEG, false>(p, gx, gy, s);
         case MODE_INTRA: return launch_one<E, D, C, MODE_INTRA, false>(p, gx, gy, s);
         case MODE_CUMSUM: return launch_one<E, D, C, MODE_CUMSUM, false>(p, gx, gy, s);
@@ -1289,14 +1409,17 @@ hipError_t launch_chunk_kernel(int dtype, int D, int C, int mode, bool scalar_ga
                                const KernelParams &p, int gx, int gy, hipStream_t s) {
     const bool sg = scalar_gate;
     if (dtype == DTYPE_BF16) {
+        if (D == 128 && C == 128) return dispatch_mode<BF16, 128, 128>(mode, sg, p, gx, gy, s);
         if (D == 128 && C == 64) return dispatch_mode<BF16, 128, 64>(mode, sg, p, gx, gy, s);
         if (D == 128 && C == 32) return dispatch_mode<BF16, 128, 32>(mode, sg, p, gx, gy, s);
         if (D == 64 && C == 64) return dispatch_mode<BF16, 64, 64>(mode, sg, p, gx, gy, s);
         if (D == 64 && C == 32) return dispatch_mode<BF16, 64, 32>(mode, sg, p, gx, gy, s);
+        if (D == 64 && C == 128) return dispatch_mode<BF16, 64, 128>(mode, sg, p, gx, gy, s);
     } else if (dtype == DTYPE_F32) {
         if (D == 64 && C == 64) return dispatch_mode<F32, 64, 64>(mode, sg, p, gx, gy, s);
         if (D == 64 && C == 32) return dispatch_mode<F32, 64, 32>(mode, sg, p, gx, gy, s);
         if (D == 128 && C == 32) return dispatch_mode<F32, 128, 32>(mode, sg, p, gx, gy, s);
+        if (D == 128 && C == 64) return dispatch_mode<F32, 128, 64>(mode, sg, p, gx, gy, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1312,16 +1435,19 @@ int state_units_per_cu(int dtype, int D, int C) {
         if (D == 64 && C == 64) bytes = Layout<F32, 64, 64, MODE_SEG>::bytes;
         if (D == 64 && C == 32) bytes = Layout<F32, 64, 32, MODE_SEG>::bytes;
         if (D == 128 && C == 32) bytes = Layout<F32, 128, 32, MODE_SEG>::bytes;
+        if (D == 128 && C == 64) bytes = Layout<F32, 128, 64, MODE_SEG>::bytes;
     }
     if (bytes <= 0) return 1;
     return std::max(1, std::min(2, 163840 / bytes));
 }
 
 bool chunk_supported(int dtype, int D, int C) {
-    if (dtype == DTYPE_BF16) return (D == 128 || D == 64) && (C == 64 || C == 32);
-    if (dtype == DTYPE_F32) return (D == 64 && (C == 64 || C == 32)) || (D == 128 && C == 32);
+    if (dtype == DTYPE_BF16) return (D == 128 || D == 64) && (C == 128 || C == 64 || C == 32);
+    if (dtype == DTYPE_F32) return (D == 64 || D == 128) && (C == 64 || C == 32);
     return false;
 }
+
+int state_chunk(int dtype, int C) { return dtype == DTYPE_BF16 && C == 128 ? 64 : C; }
 
 hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0, int nbh,
                        int slots, int D, hipStream_t s) {

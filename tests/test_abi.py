@@ -64,7 +64,7 @@ def _call(lib, fn="gla_fwd", **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), -2), (dict(H=-1), -2), (dict(T=-5), -2), (dict(T=1 << 24), -2),
-    (dict(K=128, V=64), -3), (dict(K=96, V=96), -3), (dict(chunk=48), -3), (dict(chunk=128), -3),
+    (dict(K=128, V=64), -3), (dict(K=96, V=96), -3), (dict(chunk=48), -3), (dict(chunk=256), -3),
     (dict(q=None), -1), (dict(g=None), -1), (dict(o=None), -1),
     (dict(q=FAKE + 8), -4), (dict(hf=FAKE + 5 * STEP + 4), -4),
     (dict(o=FAKE + 64), -7), (dict(hf=FAKE + 4 * STEP + 4096), -7),
@@ -191,8 +191,10 @@ def test_fp32_chunk_support_table():
     def f32(K, chunk):
         return lib.gla_fwd_f32(vp(FAKE), vp(FAKE + STEP), vp(FAKE + 2 * STEP), vp(FAKE + 3 * STEP),
                                None, vp(FAKE + 4 * STEP), None, 1, 1, 10, K, K, chunk, 1.0, None)
-    assert f32(128, 64) == -3
+    # fp32 runs chunks of 32 and 64 tokens at both head dims; 128 is bf16 only
+    assert f32(128, 128) == -3
     assert f32(64, 128) == -3
+    assert f32(128, 96) == -3
 
 
 def test_missing_library_fails_loudly(tmp_path):

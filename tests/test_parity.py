@@ -98,11 +98,12 @@ def test_tiny_f32_workload(gate, chunk):
         assert nerr(o, oc) <= TOL_F32
 
 
-def test_f32_head_dim_128():
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_f32_head_dim_128(chunk):
     wl = WORKLOADS["tiny_f32"]
     x = make_inputs(dataclass_replace(wl, D=128), T=200, H=2)
-    say("[f32 D=128] T=200 chunk=32")
-    o, hf = gpu_run(x, fp32=True, chunk=32)
+    say(f"[f32 D=128] T=200 chunk={chunk}")
+    o, hf = gpu_run(x, fp32=True, chunk=chunk)
     check(x, 128 ** -0.5, o, hf, TOL_F32)
 
 
@@ -123,6 +124,15 @@ SMALL = [
     (2, 2, 1000, 128, 64, True),
     (1, 2, 777, 64, 64, True),
     (1, 2, 300, 64, 32, False),
+    # chunk 128: one token, a tail short of one chunk, exactly one, one past,
+    # several chunks with a ragged tail, at both head dims
+    (1, 2, 1, 128, 128, False),
+    (2, 3, 127, 128, 128, True),
+    (1, 2, 128, 128, 128, False),
+    (2, 2, 129, 128, 128, True),
+    (2, 2, 1000, 128, 128, True),
+    (1, 2, 777, 64, 128, True),
+    (1, 3, 300, 64, 128, False),
 ]
 
 
@@ -135,14 +145,17 @@ def test_bf16_small_shapes(B, H, T, D, chunk, h0):
     check(x, D ** -0.5, o, hf, TOL_BF16)
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("target", [1, 4, 64, 100000])
-def test_bf16_segment_splits(target):
-    """Force 1 .. N segments so the segment-state pass and scan are exercised."""
+def test_bf16_segment_splits(target, chunk):
+    """Force 1 .. N segments so the segment-state pass and scan are exercised
+    (at chunk 128 the state units run on 64-token chunks and end on 128-token
+    boundaries)."""
     wl = WORKLOADS["prefill_4k"]
     x = make_inputs(wl, B=1, H=2, T=1000, seed=5, h0_std=0.3)
-    say(f"[segments] target_wgs={target}")
+    say(f"[segments] target_wgs={target} chunk={chunk}")
     gla.set_tuning(target, 0)
-    o, hf = gpu_run(x)
+    o, hf = gpu_run(x, chunk=chunk)
     check(x, wl.scale, o, hf, TOL_BF16)
 
 
@@ -193,7 +206,8 @@ def test_bf16_extreme_gates(gate):
 # wave, rows kept (const:-30, rows stop at once) or taken in mirrored pairs
 # (const:-2 and mixed, rows that run long), ragged tail (T = 333)
 EXACT_SHAPES = [("bf16", 128, 32), ("bf16", 64, 64), ("bf16", 64, 32),
-                ("f32", 64, 64), ("f32", 64, 32), ("f32", 128, 32)]
+                ("bf16", 128, 128), ("bf16", 64, 128),
+                ("f32", 64, 64), ("f32", 64, 32), ("f32", 128, 32), ("f32", 128, 64)]
 
 
 @pytest.mark.parametrize("gate", ["const:-30", "const:-2", "mixed"])
@@ -230,14 +244,19 @@ def test_bf16_extreme_gates_full_size(gate):
     check(x, wl.scale, o, hf, TOL_BF16)
 
 
-def test_bf16_chunk_invariance():
-    wl = WORKLOADS["prefill_4k"]
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_chunk_invariance(D):
+    """Chunks of 32, 64 and 128 tokens: each within the bar of the oracle and
+    within twice the bar of one another."""
+    wl = dataclass_replace(WORKLOADS["prefill_4k"], D=D)
     x = make_inputs(wl, B=1, H=2, T=640, seed=10, h0_std=0.2)
-    say("[chunk invariance] 32 vs 64")
-    o32, h32 = gpu_run(x, chunk=32)
-    o64, h64 = gpu_run(x, chunk=64)
-    check(x, wl.scale, o32, h32, TOL_BF16)
-    check(x, wl.scale, o64, h64, TOL_BF16)
+    say(f"[chunk invariance] D={D} 32 vs 64 vs 128")
+    runs = {c: gpu_run(x, chunk=c) for c in (32, 64, 128)}
+    for c, (o, hf) in runs.items():
+        check(x, D ** -0.5, o, hf, TOL_BF16)
+    for c in (32, 128):
+        assert nerr(runs[c][0], runs[64][0].astype(np.float64)) <= 2 * TOL_BF16
+        assert nerr(runs[c][1], runs[64][1].astype(np.float64)) <= 2 * TOL_BF16
 
 
 def test_bf16_split_invariance():
@@ -282,48 +301,52 @@ def test_zero_length_sequence():
 
 # ----------------------------------------------------------------- stages ---
 
-def test_stage_cumsum():
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_stage_cumsum(chunk):
     x = make_inputs(WORKLOADS["prefill_4k"], B=1, H=2, T=300, seed=13)
-    say("[stage cumsum]")
-    gc, gam = gla.gla_stage_cumsum(x["g"].to(DEV), chunk=64)
+    say(f"[stage cumsum] chunk={chunk}")
+    gc, gam = gla.gla_stage_cumsum(x["g"].to(DEV), chunk=chunk)
     torch.cuda.synchronize()
-    rgc, rgam = oracle.chunk_cumsum(to_f64_numpy(x["g"]), 64)
+    rgc, rgam = oracle.chunk_cumsum(to_f64_numpy(x["g"]), chunk)
     assert nerr(gc.cpu().numpy(), rgc) < 1e-5
     assert nerr(gam.cpu().numpy(), rgam) < 1e-5
 
 
 # const:-2 takes the exact path with rows that stay alive for about 52 tokens
 # (the waves take rows in mirrored pairs); const:-30 with rows that stop after a few
+@pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("gate", ["ls16", "const:-30", "const:-2"])
-def test_stage_intra(gate):
+def test_stage_intra(gate, chunk):
     wl = WORKLOADS["prefill_4k"]
     x = make_inputs(wl, B=1, H=2, T=200, seed=14, gate=gate)
-    say(f"[stage intra] gate={gate}")
-    A = gla.gla_stage_intra(x["q"].to(DEV), x["k"].to(DEV), x["g"].to(DEV), chunk=64)
+    say(f"[stage intra] gate={gate} chunk={chunk}")
+    A = gla.gla_stage_intra(x["q"].to(DEV), x["k"].to(DEV), x["g"].to(DEV), chunk=chunk)
     torch.cuda.synchronize()
     ref = oracle.intra_scores(to_f64_numpy(x["q"]), to_f64_numpy(x["k"]), to_f64_numpy(x["g"]),
-                              64, scale=wl.scale)
+                              chunk, scale=wl.scale)
     A = A.cpu().numpy()
     # rows/cols past T in the last chunk are don't-care; compare the valid part
     T = 200
+    up = np.triu_indices(chunk, 1)
     for n in range(ref.shape[2]):
-        L = min(64, T - 64 * n)
+        L = min(chunk, T - chunk * n)
         e = nerr(A[:, :, n, :L, :L], ref[:, :, n, :L, :L])
         assert e <= TOL_BF16, (n, e)
-        assert np.all(A[:, :, n][:, :, np.triu_indices(64, 1)[0], np.triu_indices(64, 1)[1]] == 0)
+        assert np.all(A[:, :, n][:, :, up[0], up[1]] == 0)
 
 
-def test_stage_states():
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_stage_states(chunk):
     wl = WORKLOADS["prefill_4k"]
     x = make_inputs(wl, B=1, H=2, T=500, seed=15, h0_std=0.3)
-    say("[stage states]")
+    say(f"[stage states] chunk={chunk}")
     gla.set_tuning(8, 0)  # several segments: states come through the scan
     d = {n: x[n].to(DEV) for n in ("q", "k", "v", "g", "h0")}
-    o, hf, st = gla.gla_stage_states(d["q"], d["k"], d["v"], d["g"], d["h0"], chunk=64)
+    o, hf, st = gla.gla_stage_states(d["q"], d["k"], d["v"], d["g"], d["h0"], chunk=chunk)
     torch.cuda.synchronize()
     f = {n: to_f64_numpy(x[n]) for n in ("q", "k", "v", "g", "h0")}
     _, _, rst = oracle.token_recurrence(f["q"], f["k"], f["v"], f["g"], f["h0"], wl.scale,
-                                        record_every=64)
+                                        record_every=chunk)
     assert nerr(st.cpu().numpy(), rst) <= TOL_BF16
 
 
@@ -346,4 +369,19 @@ def test_full_size_workload(name):
     if hf is None:
         o2, hf = gpu_run(x, want_final=True)
         assert np.array_equal(o, o2), "writing h_final changed the output"
+    check(x, wl.scale, o, hf, TOL_BF16)
+
+
+@pytest.mark.parametrize("gate", ["ls16", "mixed"])
+def test_full_size_chunk128(gate):
+    """prefill_16k at chunk 128: every output element and final state (ordinary
+    gates, and 1% of the gates at -200, every chunk on the exact path)."""
+    wl = WORKLOADS["prefill_16k"]
+    say(f"[full prefill_16k, chunk 128] gate={gate}")
+    x = make_inputs(wl, seed=23, h0_std=0.3)
+    if gate == "mixed":
+        gen = torch.Generator().manual_seed(24)
+        spikes = torch.rand(x["g"].shape, generator=gen) < 0.01
+        x["g"] = torch.where(spikes, torch.full_like(x["g"], -200.0), x["g"])
+    o, hf = gpu_run(x, chunk=128)
     check(x, wl.scale, o, hf, TOL_BF16)

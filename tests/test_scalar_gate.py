@@ -83,10 +83,11 @@ def test_f32_tiny(gate, chunk):
     check(x, o, hf, TOL_F32)
 
 
-def test_f32_head_dim_128():
-    say("[scalar f32] D=128 T=200 chunk=32")
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_f32_head_dim_128(chunk):
+    say(f"[scalar f32] D=128 T=200 chunk={chunk}")
     x = make_inputs(_wl("f32", 128), T=200, H=2, h0_std=0.3)
-    o, hf = gpu_run(x, fp32=True, chunk=32)
+    o, hf = gpu_run(x, fp32=True, chunk=chunk)
     check(x, o, hf, TOL_F32)
 
 
@@ -99,6 +100,9 @@ SMALL = [
     (2, 2, 1000, 128, 64, True),
     (1, 2, 777, 64, 64, True),
     (1, 2, 300, 64, 32, False),
+    (2, 2, 129, 128, 128, True),
+    (2, 2, 1000, 128, 128, True),
+    (1, 2, 777, 64, 128, True),
 ]
 
 
