@@ -136,7 +136,7 @@ bwd_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sBt[NW * D];    // wave totals of the gates
     __shared__ __attribute__((aligned(16))) float sEG[D];         // exp2(Gamma)
     __shared__ __attribute__((aligned(16))) float sGam[D];        // Gamma (log2)
-    __shared__ __attribute__((aligned(16))) float sDot[NW * D];   // per-wave parts of sum_v U_{n+1} S_n
+    __shared__ __attribute__((aligned(16))) float sDot[D];   // sum_v U~_{n+1} S_n per key dim (each wave its own rows)
     __shared__ __attribute__((aligned(16))) float sDiag[C];       // do_i . v_i
     unsigned char *tQ = smem + L::q;
     unsigned char *tK = smem + L::k;
@@ -186,21 +186,6 @@ bwd_kernel(const BwdParams p) {
                 for (int e = 0; e < 4; ++e)
                     U[mt][nt][e] = src ? src[(16 * mt + 4 * q4 + e) * D + cb + 16 * nt + n16] : 0.f;
     }
-    // per-wave parts of sum_v U S_n over this wave's columns, S_n prefetched
-    // in the accumulator layout
-    auto dot_us = [&](const float (&sacc)[MT][NTW][4], float *dst) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float part = 0.f;
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) part += U[mt][nt][e] * sacc[mt][nt][e];
-#pragma unroll
-                for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m, 64);
-                if (n16 == 0) dst[w * D + 16 * mt + 4 * q4 + e] = part;
-            }
-    };
     if constexpr (kFull) {   // entries above the diagonal of the score tiles are never written
         for (int i = tid; i < 2 * L::TA / 4; i += NW * 64) reinterpret_cast<uint32_t *>(tA)[i] = 0u;
     }
@@ -218,20 +203,7 @@ bwd_kernel(const BwdParams p) {
         // ---- this chunk's rows: gates, q, k into registers; v, do into LDS ----
         RawG<CPL> rg[RPW];
         Raw<E, CPL> rq[RPW], rk[RPW];
-        float sacc[MT][NTW][4];   // S_n in the accumulator layout (for the dg state term)
         {
-            if constexpr (kFull) {   // one lane offset, the row in the uniform offset
-                const rsrc_t bs = make_rsrc(p.states + (bh * long(N) + c) * long(D) * D, D * D * 4);
-                const int voff = ((4 * q4) * D + cb + n16) * 4;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sacc[mt][nt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                bs, voff, ((16 * mt + e) * D + 16 * nt) * 4, 0));
-            }
             const int eoff = (t0 + r0) * D + lane * CPL;
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
@@ -258,7 +230,6 @@ bwd_kernel(const BwdParams p) {
             }
             mem_fence_compiler();
             wait_vmem<0>();
-            if constexpr (kFull) dot_us(sacc, sDot);   // sum_v U_{n+1} S_n (e^Gamma applied in the epilogue)
         }
 
         // ---- gate sums (log2 units) over this wave's rows --------------------
@@ -473,6 +444,10 @@ bwd_kernel(const BwdParams p) {
                     Dq[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                     Dk1[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
+                // the same S_n entries, times the U tile's (the rows d of this
+                // wave, 8 value columns per lane and key step), summed over v:
+                // the dg state term sum_v U~_{n+1} S_n for row d = cb + 16 nt + n16
+                float dacc = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int voff = ((cb + n16) * D + 8 * q4) * 4, soff = (16 * nt * D + ks * 32) * 4;
@@ -483,7 +458,14 @@ bwd_kernel(const BwdParams p) {
 #pragma unroll
                     for (int m = 0; m < NB; ++m)
                         Dq[nt][m] = E::mma(sf, E::ld_frag(row_ptr(tO, 16 * m + n16, L::PD) + ks * 32 + 8 * q4), Dq[nt][m]);
+                    float uv[8];
+                    E::unpack(E::ld_frag(row_ptr(tU, cb + 16 * nt + n16, L::PD) + ks * 32 + 8 * q4), uv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dacc = __builtin_fmaf(uv[e], xs[e], dacc);
                 }
+                dacc += __shfl_xor(dacc, 16, 64);
+                dacc += __shfl_xor(dacc, 32, 64);
+                if (q4 == 0) sDot[cb + 16 * nt + n16] = dacc;
                 if (fast) {
 #pragma unroll
                     for (int ts = 0; ts < TS; ++ts) {
@@ -622,13 +604,13 @@ bwd_kernel(const BwdParams p) {
                         carry_x[e] += __shfl(x[e], 15, 16);
                     }
                 }
-                f32x4_t dot = {0.f, 0.f, 0.f, 0.f};
+                // e^Gamma sum_v U_{n+1} S_n for this lane's rows d0 .. d0 + 3 (the
+                // wave's own, from its dq step; the U tile holds U_{n+1} e^Gamma on
+                // the fast path and U_{n+1} on the exact one)
+                f32x4_t dot = *reinterpret_cast<const f32x4_t *>(sDot + d0);
+                if (!fast)
 #pragma unroll
-                for (int j = 0; j < NW; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dot[e] += sDot[j * D + d0 + e];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dot[e] *= sEG[d0 + e];   // e^Gamma sum_v U_{n+1} S_n
+                    for (int e = 0; e < 4; ++e) dot[e] *= sEG[d0 + e];
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {
 #pragma unroll
