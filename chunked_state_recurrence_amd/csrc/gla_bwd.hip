@@ -499,25 +499,24 @@ bwd_kernel(const BwdParams p) {
             const rsrc_t bdq = make_rsrc(reinterpret_cast<gmem_t *>(p.dq) + bh * long(T) * D, long(T) * D * es);
             const rsrc_t bdk = make_rsrc(reinterpret_cast<gmem_t *>(p.dk) + bh * long(T) * D, long(T) * D * es);
             const rsrc_t bdg = make_rsrc(p.dg + bh * long(T) * D, long(T) * D * 4);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const int d0 = cb + 16 * nt + 4 * q4;   // this lane's four columns
-                f32x4_t w1[NB], xk[NB];
-#pragma unroll
-                for (int m = 0; m < NB; ++m) {
-                    const int i = 16 * m + n16;
-                    const int eoff = (t0 + i) * D + d0;
-                    Raw4<E> eqr, ekr;
-                    eqr.load(bq, eoff * es);
-                    ekr.load(bk, eoff * es);
-                    const f32x4_t qv = eqr.get(), kv = ekr.get();
-                    const f32x4_t gc = *reinterpret_cast<const f32x4_t *>(rGc + i * L::RP + d0);
-                    const float dgl = p.scale * sDiag[i];   // scale do_i . v_i
-                    f32x4_t dq2 = {0.f, 0.f, 0.f, 0.f}, dk1s = {0.f, 0.f, 0.f, 0.f};
-                    if (!fast) {
-                        // exact path: dq2_i = sum_{j<i} (do_i.v_j) k_j prod_{r=j+1..i} e^{g_r},
-                        // dk1_i = sum_{i2>i} (do_i2.v_i) q_i2 prod_{r=i+1..i2} e^{g_r}
-                        // (the do v^T tile is zero on its diagonal)
+            // Exact path: the intra-chunk sums of dq and dk1 formed elementwise
+            // with running products of per-token decays,
+            //   dq2_i = sum_{j<i} (do_i.v_j) k_j prod_{r=j+1..i} e^{g_r},
+            //   dk1_i = sum_{i2>i} (do_i2.v_i) q_i2 prod_{r=i+1..i2} e^{g_r}
+            // (the do v^T tile is zero on its diagonal), in a pass of their own:
+            // fp32, staged in this chunk's state slot ([C][D], read for the last
+            // time in the dq step above) and in dg's rows, each value at the
+            // address from which the same lane reads it back in the epilogue.
+            // Kept apart, their loops leave the epilogue's registers alone.
+            const rsrc_t bst = make_rsrc(p.states + (bh * long(N) + c) * long(D) * D, D * D * 4);
+            if (!fast) {
+#pragma unroll 1
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const int d0 = cb + 16 * nt + 4 * q4;
+#pragma unroll 1
+                    for (int m = 0; m < NB; ++m) {
+                        const int i = 16 * m + n16;
+                        f32x4_t dq2 = {0.f, 0.f, 0.f, 0.f}, dk1s = {0.f, 0.f, 0.f, 0.f};
                         f32x4_t pr = {1.f, 1.f, 1.f, 1.f};
                         for (int j = i; j >= 0; --j) {
                             const f32x4_t kj = load4<E>(bk, ((t0 + j) * D + d0) * es);
@@ -541,6 +540,31 @@ bwd_kernel(const BwdParams p) {
                                 for (int e = 0; e < 4; ++e) pr[e] *= fexp2(gn[e] * kLog2e);
                             }
                         }
+                        F32::st4(bst, (i * D + d0) * 4, dq2);
+                        F32::st4(bdg, ((t0 + i) * D + d0) * 4, dk1s);
+                    }
+                }
+                wait_vmem<0>();   // the stores are done before the same lanes read them back
+                mem_fence_compiler();
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const int d0 = cb + 16 * nt + 4 * q4;   // this lane's four columns
+                f32x4_t w1[NB], xk[NB];
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    const int i = 16 * m + n16;
+                    const int eoff = (t0 + i) * D + d0;
+                    Raw4<E> eqr, ekr;
+                    eqr.load(bq, eoff * es);
+                    ekr.load(bk, eoff * es);
+                    const f32x4_t qv = eqr.get(), kv = ekr.get();
+                    const f32x4_t gc = *reinterpret_cast<const f32x4_t *>(rGc + i * L::RP + d0);
+                    const float dgl = p.scale * sDiag[i];   // scale do_i . v_i
+                    f32x4_t dq2 = {0.f, 0.f, 0.f, 0.f}, dk1s = {0.f, 0.f, 0.f, 0.f};
+                    if (!fast) {   // staged by the exact pass above, at this lane's own addresses
+                        dq2 = load4<F32>(bst, (i * D + d0) * 4);
+                        dk1s = load4<F32>(bdg, eoff * 4);
                     }
                     f32x4_t dqo, dko;
 #pragma unroll
