@@ -84,6 +84,14 @@ template <typename E, int D, int C> struct BwdLayout {
 
 // four consecutive values of one row, kept as loaded until get() decodes
 // them (so that issuing the load does not wait for it)
+// v from another lane of the same 16-lane row by DPP: 0x101..0x10F take lane
+// + n, 0x111..0x11F lane - n (0 where that lane lies outside the row),
+// 0x150 + n lane n of the row
+template <int CTRL>
+__device__ __forceinline__ float row_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
 template <typename E> struct Raw4;
 template <> struct Raw4<BF16> {
     u32x2_t x;
@@ -597,35 +605,34 @@ bwd_kernel(const BwdParams p) {
                 for (int m = NB - 1; m >= 0; --m) {   // suffix of w1
                     f32x4_t x = w1[m];
 #pragma unroll
-                    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float y = __shfl_down(x[e], off, 16);
-                            if (n16 + off < 16) x[e] += y;
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] += row_dpp<0x101>(x[e]);   // lane + 1 (0 past the row's end)
+                        x[e] += row_dpp<0x102>(x[e]);
+                        x[e] += row_dpp<0x104>(x[e]);
+                        x[e] += row_dpp<0x108>(x[e]);
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         dgv[m][e] = x[e] + carry_w[e];
-                        carry_w[e] += __shfl(x[e], 0, 16);
+                        carry_w[e] += row_dpp<0x150>(x[e]);   // the row's lane 0
                     }
                 }
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {   // exclusive prefix of k dk2
                     f32x4_t x = xk[m];
 #pragma unroll
-                    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float y = __shfl_up(x[e], off, 16);
-                            if (n16 >= off) x[e] += y;
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] += row_dpp<0x111>(x[e]);   // lane - 1 (0 before the row's start)
+                        x[e] += row_dpp<0x112>(x[e]);
+                        x[e] += row_dpp<0x114>(x[e]);
+                        x[e] += row_dpp<0x118>(x[e]);
+                    }
                     // the previous row's inclusive sum, not x - xk: the row's own
                     // term can be the large one that must not enter dg
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float ex = __shfl_up(x[e], 1, 16);
-                        dgv[m][e] += carry_x[e] + (n16 > 0 ? ex : 0.f);
-                        carry_x[e] += __shfl(x[e], 15, 16);
+                        dgv[m][e] += carry_x[e] + row_dpp<0x111>(x[e]);
+                        carry_x[e] += row_dpp<0x15F>(x[e]);   // the row's lane 15
                     }
                 }
                 // e^Gamma sum_v U_{n+1} S_n for this lane's rows d0 .. d0 + 3 (the
