@@ -47,6 +47,13 @@
 
 namespace gla {
 
+// v moved between lanes by DPP control CTRL, written only in the rows of
+// ROW_MASK; lanes with no source, and rows outside the mask, read 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float wave_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
 template <int D, int C> struct GdnLayout {
     static constexpr int QP = D + 8;                 // permuted-row tiles, bf16 elements per row
     static constexpr int PD = 2 * D + 32;            // bank-spread bf16 tiles, bytes per row
@@ -237,12 +244,17 @@ gdn_kernel(const GdnParams p) {
         const int cn = c + cstep;
         // ---- gates of the chunk scanned (log2 units), one row per lane -------------
         if (w == 0) {
+            // inclusive scan over the wave by DPP: within each 16-lane row
+            // (lane - 1, 2, 4, 8; 0 before the row's start), then the running
+            // totals of the rows before (lane 15 into rows 1 and 3, lane 31
+            // into rows 2 and 3; the other rows add 0)
             float x = gx * kLog2e;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
-            }
+            x += wave_dpp<0x111, 0xf>(x);
+            x += wave_dpp<0x112, 0xf>(x);
+            x += wave_dpp<0x114, 0xf>(x);
+            x += wave_dpp<0x118, 0xf>(x);
+            x += wave_dpp<0x142, 0xa>(x);
+            x += wave_dpp<0x143, 0xc>(x);
             sGc[lane] = x;
             sBeta[lane] = gb;
         }
