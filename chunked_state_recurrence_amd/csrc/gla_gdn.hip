@@ -338,11 +338,15 @@ gdn_kernel(const GdnParams p) {
             }
         }
         block_sync();  // B4: diagonal blocks of T
-        // off-diagonal blocks, by distance from the diagonal: wave J makes T_{J+d, J}
+        // off-diagonal blocks: wave J makes column J of T, T_{J+1,J}, T_{J+2,J}, ...
+        // in turn; each needs only the diagonal blocks, A and the column's own
+        // earlier blocks (this wave's stores, seen after its LDS fence), so the
+        // levels need no barrier between them
+        if (w < NB - 1) {
 #pragma unroll
-        for (int d = 1; d < NB; ++d) {
-            if (w < NB - d) {
+            for (int d = 1; d < NB; ++d) {
                 const int J = w, I = J + d;
+                if (I >= NB) break;
                 f32x4_t x = {0.f, 0.f, 0.f, 0.f};
                 for (int Kb = J; Kb < I; ++Kb)
                     x = mma16_f32(tA + (16 * I) * L::PF + 16 * Kb, L::PF, tT + (16 * Kb) * L::PF + 16 * J, L::PF,
@@ -368,9 +372,10 @@ gdn_kernel(const GdnParams p) {
                     blkIJ[(4 * q4 + e) * L::PF + n16] = -y[e];
                     rowp(tTb, 16 * I + 4 * q4 + e, L::PC)[16 * J + n16] = (__bf16)(-y[e] * bc);
                 }
+                wave_lds_fence();   // T_IJ visible to this wave's next block
             }
-            block_sync();  // B5..B7: one level of T
         }
+        block_sync();  // B5: T complete
         if (cn < N) issue_qk(cn);   // the A / T tiles are no longer read
 
         // ---- W = T diag(beta) (gamma K) and U~ = T diag(beta) V for this wave's
