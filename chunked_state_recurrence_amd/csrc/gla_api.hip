@@ -155,6 +155,7 @@ struct Call {
     hipStream_t stream;
     bool scalar_gate = false;  // g is [B,H,T] instead of [B,H,T,K]
     bool need_o = true;        // false: only states / h_final are wanted (backward)
+    void *states16 = nullptr;  // the backward's chunk-start states in bf16, or nullptr
 };
 
 int default_chunk(int dtype, int D) {
@@ -287,7 +288,7 @@ int run_forward(Call &c, float *fixed_ws = nullptr, size_t fixed_cap = 0) {
         p.o = c.o; p.h_final = c.h_final;
         p.ws_E = ws;
         p.ws_G = ws ? ws + size_t(nbh) * pl.slots * D * D : nullptr;
-        p.dump = c.states; p.dump2 = nullptr;
+        p.dump = c.states; p.dump2 = nullptr; p.dump16 = c.states16;
         p.T = c.T; p.N = N; p.bh0 = g0; p.scale = c.scale;
         p.ws_slots = pl.slots; p.sub = pl.sub;
         if (pl.P > 1) {
@@ -379,12 +380,16 @@ int run_backward(BwdCall &b) {
         seg_need = std::max(seg_need, size_t(nbh) * size_t(pl.P - 1) * size_t(D) * (D + 1) * 4);
     }
     const size_t n_states = size_t(BH) * N * D * D;
+    const bool s16 = gla::bwd_states_bf16(b.dtype, D, b.chunk);
+    const size_t states_bytes = n_states * (s16 ? 2 : 4);
     float *bws = nullptr;
-    if ((rc = ensure_bwd_workspace(dev, n_states * 4 + seg_need, &bws)) != GLA_OK) return rc;
-    float *states = bws, *segws = bws + n_states;
+    if ((rc = ensure_bwd_workspace(dev, states_bytes + seg_need, &bws)) != GLA_OK) return rc;
+    void *states = bws;
+    float *segws = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(bws) + states_bytes);
 
     // forward chunk-start states (no o, no final state)
-    c.states = states;
+    if (s16) c.states16 = states;
+    else c.states = static_cast<float *>(states);
     if ((rc = run_forward(c)) != GLA_OK) return rc;
 
     for (long g0 = 0; g0 < BH; g0 += group) {

@@ -133,6 +133,10 @@ bwd_kernel(const BwdParams p) {
     constexpr int NTILE = NB * (NB + 1) / 2;
     static_assert(NTW >= 1 && TS >= 1 && CPL >= 1, "unsupported tile shape");
     constexpr bool kFull = BM == BM_FULL;
+    // element size of the chunk-start states (bf16 where bwd_states_bf16 says so)
+    constexpr bool kS16 = bwd_states_bf16(std::is_same<E, BF16>::value ? DTYPE_BF16 : DTYPE_F32, D, C);
+    constexpr int kSes = kS16 ? 2 : 4;
+    static_assert(!kS16 || C * D * 4 <= D * D * kSes, "a state slot holds the exact path's fp32 staging");
     using L = BwdLayout<E, D, C>;
     using lds_t = typename E::lds_t;
     using gmem_t = typename E::gmem_t;
@@ -390,7 +394,8 @@ bwd_kernel(const BwdParams p) {
 
             // ---- dv, dk2, U, dq, dk1 column slices of this wave --------------------
             // each product's accumulators retire before the next group starts
-            const rsrc_t bs = make_rsrc(p.states + (bh * long(N) + c) * long(D) * D, D * D * 4);
+            const rsrc_t bs = make_rsrc(static_cast<const unsigned char *>(p.states) + (bh * long(N) + c) * long(D) * D * kSes,
+                                        D * D * kSes);
             const rsrc_t bdv = make_rsrc(reinterpret_cast<gmem_t *>(p.dv) + bh * long(T) * D, long(T) * D * es);
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
@@ -458,11 +463,21 @@ bwd_kernel(const BwdParams p) {
                 float dacc = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int voff = ((cb + n16) * D + 8 * q4) * 4, soff = (16 * nt * D + ks * 32) * 4;
-                    const f32x4_t lo = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff, soff, 0));
-                    const f32x4_t hi = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff + 16, soff, 0));
-                    const float xs[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    const frag_t sf = E::pack(xs);
+                    float xs[8];
+                    frag_t sf;
+                    if constexpr (kS16) {   // eight bf16 states (16 x 16 tiles): the operand as stored
+                        const int voff = 2 * bf16_state_offset<D>(n16, 8 * q4);
+                        const int soff = 2 * bf16_state_offset<D>(cb + 16 * nt, ks * 32);
+                        sf = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff, soff, 0));
+                        E::unpack(sf, xs);
+                    } else {
+                        const int voff = ((cb + n16) * D + 8 * q4) * 4, soff = (16 * nt * D + ks * 32) * 4;
+                        const f32x4_t lo = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff, soff, 0));
+                        const f32x4_t hi = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff + 16, soff, 0));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { xs[e] = lo[e]; xs[4 + e] = hi[e]; }
+                        sf = E::pack(xs);
+                    }
 #pragma unroll
                     for (int m = 0; m < NB; ++m)
                         Dq[nt][m] = E::mma(sf, E::ld_frag(row_ptr(tO, 16 * m + n16, L::PD) + ks * 32 + 8 * q4), Dq[nt][m]);
@@ -516,7 +531,8 @@ bwd_kernel(const BwdParams p) {
             // time in the dq step above) and in dg's rows, each value at the
             // address from which the same lane reads it back in the epilogue.
             // Kept apart, their loops leave the epilogue's registers alone.
-            const rsrc_t bst = make_rsrc(p.states + (bh * long(N) + c) * long(D) * D, D * D * 4);
+            const rsrc_t bst = make_rsrc(static_cast<const unsigned char *>(p.states) + (bh * long(N) + c) * long(D) * D * kSes,
+                                         D * D * kSes);
             if (!fast) {
 #pragma unroll 1
                 for (int nt = 0; nt < NTW; ++nt) {

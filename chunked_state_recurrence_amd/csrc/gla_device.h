@@ -300,6 +300,39 @@ template <int D, int C> struct Shape {
     static_assert(RPW == 8 || RPW == 16 || RPW == 32, "unsupported chunk / head-dim pair");
 };
 
+// The backward's bf16 chunk-start states: D x D in 16 x 16 tiles, tile
+// (r / 16, c / 16) row-major over the tiles, each tile row-major (256
+// elements); element offset of (r, c)
+template <int D>
+__device__ __forceinline__ int bf16_state_offset(int r, int c) {
+    return ((r >> 4) * (D / 16) + (c >> 4)) * 256 + (r & 15) * 16 + (c & 15);
+}
+
+// 4 x 4 transpose across the lanes of a quad: lane j (= lane & 3) holds
+// x[e] = M[j][e] on entry and x[e] = M[e][j] on exit.  Two exchanges: the
+// off-diagonal 2 x 2 blocks with lane j ^ 2, then the off-diagonal entries of
+// each 2 x 2 block with lane j ^ 1 (DPP quad permutes).
+__device__ __forceinline__ void quad_transpose4(float (&x)[4], int j) {
+    auto qp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    const bool lo2 = (j & 2) == 0, lo1 = (j & 1) == 0;
+    float s0 = lo2 ? x[2] : x[0], s1 = lo2 ? x[3] : x[1];
+    float r0 = qp(s0, std::integral_constant<int, 0x4E>{}), r1 = qp(s1, std::integral_constant<int, 0x4E>{});   // lane j ^ 2
+    if (lo2) { x[2] = r0; x[3] = r1; } else { x[0] = r0; x[1] = r1; }
+    s0 = lo1 ? x[1] : x[0];
+    s1 = lo1 ? x[3] : x[2];
+    r0 = qp(s0, std::integral_constant<int, 0xB1>{});   // lane j ^ 1
+    r1 = qp(s1, std::integral_constant<int, 0xB1>{});
+    if (lo1) { x[1] = r0; x[3] = r1; } else { x[0] = r0; x[2] = r1; }
+}
+
+// two floats as packed bf16 (round to nearest even), the first in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+    return uint32_t(__builtin_bit_cast(uint16_t, ha)) | (uint32_t(__builtin_bit_cast(uint16_t, hb)) << 16);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

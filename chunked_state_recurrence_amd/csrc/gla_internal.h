@@ -23,6 +23,7 @@ struct KernelParams {
     float *ws_G;   // [nbh][ws_slots][D]     state-pass total log2-decay
     float *dump;   // stage outputs
     float *dump2;
+    void *dump16;  // chunk-start states in bf16 (the backward's, see bwd_states_bf16)
     int T;         // tokens per (batch, head)
     int N;         // chunks per (batch, head)
     int cps;       // chunks per segment
@@ -33,11 +34,17 @@ struct KernelParams {
     float scale;
 };
 
+// The backward keeps the forward's chunk-start states in bf16 (they enter the
+// dq product as bf16 MFMA operands in any case) where a state slot still
+// holds the exact path's fp32 staging of one chunk's C x D sums, D >= 2 C;
+// fp32 otherwise.
+constexpr bool bwd_states_bf16(int dtype, int D, int C) { return dtype == DTYPE_BF16 && D >= 2 * C; }
+
 // backward chunk kernel (gla_bwd.hip)
 struct BwdParams {
     const void *q, *k, *v, *dout;
     const float *g;
-    const float *states;   // forward chunk-start states [heads][N][D][D]
+    const void *states;    // forward chunk-start states [heads][N][D][D], fp32 or bf16 (bwd_states_bf16)
     const float *dhf;      // dL/dh_final [heads][D][D] or null (zero)
     void *dq, *dk, *dv;
     float *dg;

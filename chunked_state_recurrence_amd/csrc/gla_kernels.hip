@@ -816,6 +816,24 @@ chunk_kernel(const KernelParams p) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
+            } else if (p.dump16) {
+                // the same in bf16 (the backward's), in 16 x 16 tiles (layout of
+                // bf16_state_offset): a 4 x 4 transpose within each lane quad (DPP)
+                // gives a lane four consecutive columns of one row, so a wave
+                // stores a whole 512-byte tile with one 8-byte store per lane
+                unsigned char *dst = static_cast<unsigned char *>(p.dump16) + (bh * long(p.N) + c) * long(D) * D * 2;
+                const int j = n16 & 3;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) {
+                        float x[4] = {S[mt][nt][0], S[mt][nt][1], S[mt][nt][2], S[mt][nt][3]};
+                        quad_transpose4(x, j);
+                        // x[b] = S[16 mt + 4 q4 + j][vb + 16 nt + 4 (n16 / 4) + b]
+                        const uint32_t lo = pack_bf16x2(x[0], x[1]), hi = pack_bf16x2(x[2], x[3]);
+                        *reinterpret_cast<u32x2_t *>(dst + 2 * bf16_state_offset<D>(16 * mt + 4 * q4 + j, vb + 16 * nt + 4 * (n16 >> 2))) =
+                            u32x2_t{lo, hi};
+                    }
             }
             // every wave holds its v fragments: the next chunk's v rows may land
             load_v(cn);
