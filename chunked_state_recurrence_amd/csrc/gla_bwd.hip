@@ -368,9 +368,13 @@ bwd_kernel(const BwdParams p) {
                 // prod_{r=j+1..i} e^{g_r}, from running products of per-token
                 // decays (other rows' k and g re-read from the cache)
                 const int col0 = lane * CPL;
-#pragma unroll
+                // a rolled loop over the wave's rows, each row's q re-read from
+                // the cache: the rare exact chunk keeps its code and registers small
+#pragma unroll 1
                 for (int il = 0; il < RPW; ++il) {
                     const int i = r0 + il;
+                    Raw<E, CPL> qi;
+                    qi.load(bq, ((t0 + i) * D + col0) * es, 0);
                     float pr[CPL];
 #pragma unroll
                     for (int u = 0; u < CPL; ++u) pr[u] = 1.f;
@@ -382,7 +386,7 @@ bwd_kernel(const BwdParams p) {
                         float part = 0.f;
 #pragma unroll
                         for (int u = 0; u < CPL; ++u) {
-                            part += rq[il].get(u) * kj.get(u) * pr[u];
+                            part += qi.get(u) * kj.get(u) * pr[u];
                             pr[u] *= fexp2(gj.get(u) * kLog2e);
                         }
                         const float s = wave_sum(part) * p.scale;
