@@ -7,7 +7,9 @@ and final state must equal gla_fwd's bitwise; both are also compared with the
 fp64 oracle to the forward's bar (max|x - x_ref| / max|x_ref| <= 1e-2 for
 bf16 output and the final state).  Two calls in a row: the full prefill_16k
 shape (B=1, H=16, T=16K, with h0), then a smaller input (B=2, H=3, T=1000),
-so the second call runs on scratch contents the first one left.  The
+so the second call runs on scratch contents the first one left; a third
+call takes 128-token chunks (whose state pass runs on 64-token chunks, a
+different schedule for the same scratch).  The
 entry point is called through the C ABI with preallocated outputs; neither
 the library's own workspace nor torch's allocations may change across it.
 """
@@ -54,12 +56,12 @@ def _oracle_errors(x, scale, o, hf):
     return whole_errors({"o": o, "h_final": hf}, ref, B, H, T)
 
 
-@pytest.mark.parametrize("case", [(1, 16, 16384, 0.02, 2), (2, 3, 1000, 0.3, 7)],
-                         ids=["prefill_16k_shape", "smaller_after"])
+@pytest.mark.parametrize("case", [(1, 16, 16384, 0.02, 2, 0), (2, 3, 1000, 0.3, 7, 0), (1, 4, 3000, 0.1, 9, 128)],
+                         ids=["prefill_16k_shape", "smaller_after", "chunk128_after"])
 def test_noalloc_matches_gla_fwd(case):
-    B, H, T, h0_std, seed = case
+    B, H, T, h0_std, seed, chunk = case
     wl = WORKLOADS["prefill_16k"]
-    say(f"[noalloc] B={B} H={H} T={T} h0_std={h0_std}")
+    say(f"[noalloc] B={B} H={H} T={T} h0_std={h0_std} chunk={chunk}")
     lib = gla.load_library()
     gla.set_tuning(0, 0)
     x = make_inputs(wl, B=B, H=H, T=T, seed=seed, h0_std=h0_std)
@@ -70,12 +72,12 @@ def test_noalloc_matches_gla_fwd(case):
     torch.cuda.synchronize()
     ws_before = gla.workspace_bytes()
     torch_before = torch.cuda.memory_allocated(DEV)
-    rc = _abi_call(lib.gla_fwd_noalloc, d, o_a, h_a, wl.scale)
+    rc = _abi_call(lib.gla_fwd_noalloc, d, o_a, h_a, wl.scale, chunk)
     torch.cuda.synchronize()
     assert rc == 0, gla.strerror(rc)
     assert gla.workspace_bytes() == ws_before, "gla_fwd_noalloc grew the library workspace"
     assert torch.cuda.memory_allocated(DEV) == torch_before
-    assert _abi_call(lib.gla_fwd, d, o_b, h_b, wl.scale) == 0
+    assert _abi_call(lib.gla_fwd, d, o_b, h_b, wl.scale, chunk) == 0
     torch.cuda.synchronize()
     assert torch.equal(o_a, o_b), "output differs from gla_fwd"
     assert torch.equal(h_a, h_b), "final state differs from gla_fwd"
