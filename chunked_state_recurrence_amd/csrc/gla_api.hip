@@ -158,8 +158,10 @@ struct Call {
     void *states16 = nullptr;  // the backward's chunk-start states in bf16, or nullptr
 };
 
+// chunk 0: 64 for bf16; 32 for fp32, which ran faster than (D = 64) or as fast
+// as (D = 128) chunk 64 at H = 16, T = 4K and 16K
 int default_chunk(int dtype, int D) {
-    if (gla::chunk_supported(dtype, D, 64)) return 64;
+    if (dtype == gla::DTYPE_BF16 && gla::chunk_supported(dtype, D, 64)) return 64;
     return 32;
 }
 
@@ -331,12 +333,17 @@ struct BwdCall {
 };
 
 int run_backward(BwdCall &b) {
+    // the backward's own chunk set and default (64 where it has kernels, else
+    // 32), checked before anything is enqueued
+    if (b.chunk == 0 && (b.K == 64 || b.K == 128))
+        b.chunk = gla::bwd_chunk_supported(b.dtype, b.K, 64) ? 64 : 32;
     Call c{b.dtype, b.q, b.k, b.v, b.g, b.h0, nullptr, nullptr, nullptr, b.B, b.H, b.T, b.K, b.V,
            b.chunk, b.scale, b.stream};
     c.need_o = false;
     int rc = validate(c);   // shapes, chunk, input pointers and alignment
     if (rc != GLA_OK) return rc;
     b.chunk = c.chunk;
+    if (!gla::bwd_chunk_supported(b.dtype, b.K, b.chunk)) return GLA_ERR_UNSUPPORTED;
     if (b.T > 0 && (!b.dout || !b.dq || !b.dk || !b.dv || !b.dg)) return GLA_ERR_NULL;
     const void *ptrs[] = {b.dout, b.dhf, b.dq, b.dk, b.dv, b.dg, b.dh0};
     for (const void *p : ptrs)

@@ -715,6 +715,12 @@ static hipError_t launch_bwd_t(int bm, const BwdParams &p, int gx, int gy, hipSt
     return hipGetLastError();
 }
 
+bool bwd_chunk_supported(int dtype, int D, int C) {
+    if (dtype == DTYPE_BF16) return (D == 128 || D == 64) && (C == 64 || C == 32);
+    if (dtype == DTYPE_F32) return (D == 64 && (C == 64 || C == 32)) || (D == 128 && C == 32);
+    return false;
+}
+
 hipError_t launch_bwd(int dtype, int D, int C, bool full, const BwdParams &p, int gx, int gy,
                       hipStream_t s) {
     const int bm = full ? BM_FULL : BM_SEG;

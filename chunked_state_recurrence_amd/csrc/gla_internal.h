@@ -82,6 +82,8 @@ hipError_t launch_gdn_prep(int D, const GdnParams &p, int slices, hipStream_t s)
 hipError_t launch_gdn_walk(int D, const GdnParams &p, hipStream_t s);
 
 bool chunk_supported(int dtype, int D, int C);
+// chunk sizes the backward has kernels for (a subset of the forward's)
+bool bwd_chunk_supported(int dtype, int D, int C);
 // chunk length of the state pass for an output-pass chunk of C tokens (it
 // divides C, so state units end on output-chunk boundaries)
 int state_chunk(int dtype, int C);

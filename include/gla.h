@@ -27,8 +27,8 @@
  * Supported shapes: K == V in {64, 128}; T >= 0; B, H >= 1; any T (the last
  * chunk may be partial) with T * K < 2^29 and B * H <= 2^30, since each
  * (batch, head) row is addressed with 32-bit byte offsets; larger sizes return
- * GLA_ERR_SHAPE.  chunk: 0 picks the default (64); gla_fwd accepts
- * 32, 64 and 128; gla_fwd_f32 accepts 32 and 64.
+ * GLA_ERR_SHAPE.  chunk: 0 picks the default (64 for gla_fwd, 32 for
+ * gla_fwd_f32); gla_fwd accepts 32, 64 and 128; gla_fwd_f32 accepts 32 and 64.
  * Anything else returns GLA_ERR_UNSUPPORTED, never a silent fallback.
  *
  * Ownership: the caller owns every buffer.  The library keeps no pointer to

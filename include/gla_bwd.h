@@ -24,7 +24,10 @@
  *     h0, dh_final, dh0     [B, H, K, V] fp32
  * gla_bwd: q, k, v, do, dq, dk, dv bfloat16 (outputs rounded to nearest
  * even); gla_bwd_f32: float32.  g and dg are float32 in both.
- * Supported shapes and chunk sizes are those of gla_fwd / gla_fwd_f32.
+ * Supported shapes are those of gla_fwd / gla_fwd_f32; chunk sizes: 32 and 64
+ * for gla_bwd, 32 and 64 for gla_bwd_f32 at K = 64 and 32 at K = 128 (chunk
+ * 0 picks 64 where supported, else 32).  Any other chunk returns
+ * GLA_ERR_UNSUPPORTED before anything is enqueued.
  *
  * Nullability: h0 NULL = zero initial state; dh_final NULL = zero; dh0 NULL =
  * not written.  q, k, v, g, do, dq, dk, dv, dg are required when T > 0.

@@ -154,6 +154,16 @@ def test_backward_argument_errors(fn, kw, code):
     assert _bwd(lib, fn, **kw) == code
 
 
+def test_backward_chunk_table():
+    """The backward runs chunks 32 and 64 (fp32 at K = 128: 32 only); a chunk the
+    forward also takes (128, or fp32 64 at K = 128) is rejected before any work."""
+    lib = gla.load_library()
+    assert _bwd(lib, "gla_bwd", chunk=128) == -3
+    assert _bwd(lib, "gla_bwd", chunk=128, K=64, V=64) == -3
+    assert _bwd(lib, "gla_bwd_f32", chunk=64) == -3              # K = 128
+    assert _bwd(lib, "gla_bwd_f32", chunk=128, K=64, V=64) == -3
+
+
 def _gdn(lib, **kw):
     a = dict(q=FAKE, k=FAKE + STEP, v=FAKE + 2 * STEP, g=FAKE + 3 * STEP, beta=FAKE + 4 * STEP,
              h0=None, o=FAKE + 5 * STEP, hf=None, B=1, H=2, T=100, K=128, V=128, chunk=0, scale=0.1)

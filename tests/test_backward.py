@@ -88,12 +88,13 @@ def test_f32_tiny(gate, chunk):
     check(x, gr, gpu_bwd(x, gr, fp32=True, chunk=chunk), TOL_F32)
 
 
-def test_f32_head_dim_128():
-    say("[bwd f32] D=128 T=200 chunk=32")
+@pytest.mark.parametrize("chunk", [32, 0])   # 0: the backward's default (32 at this shape)
+def test_f32_head_dim_128(chunk):
+    say(f"[bwd f32] D=128 T=200 chunk={chunk}")
     wl = _wl("f32", 128)
     x = make_inputs(wl, T=200, H=2, h0_std=0.3)
     gr = make_grad_inputs(wl, T=200, H=2)
-    check(x, gr, gpu_bwd(x, gr, fp32=True, chunk=32), TOL_F32)
+    check(x, gr, gpu_bwd(x, gr, fp32=True, chunk=chunk), TOL_F32)
 
 
 SMALL = [
