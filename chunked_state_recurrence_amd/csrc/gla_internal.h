@@ -11,7 +11,9 @@ enum { DTYPE_BF16 = 0, DTYPE_F32 = 1 };
 //           and optionally the chunk-start states into `dump`).
 // MODE_SEG: end state of each segment from a zero start (writes ws_E, ws_G).
 // MODE_INTRA / MODE_CUMSUM: single stages written to `dump` / `dump2`.
-enum { MODE_OUT = 0, MODE_SEG = 1, MODE_INTRA = 2, MODE_CUMSUM = 3 };
+// MODE_STATES: the chunk-start states only (into `dump` or `dump16`, and
+//           h_final), from given segment start states; no scores, no o.
+enum { MODE_OUT = 0, MODE_SEG = 1, MODE_INTRA = 2, MODE_CUMSUM = 3, MODE_STATES = 4 };
 
 struct KernelParams {
     const void *q, *k, *v;

@@ -52,7 +52,8 @@ template <typename E, int D, int C, int MODE> struct Layout {
     // gate-sum units: each wave's rows, in pieces of at most 16 (one score block)
     static constexpr int NU = C / (RPW < 16 ? RPW : 16);
     static constexpr bool scores = MODE == MODE_OUT || MODE == MODE_INTRA;
-    static constexpr bool state = MODE == MODE_OUT || MODE == MODE_SEG;
+    static constexpr bool state = MODE == MODE_OUT || MODE == MODE_SEG || MODE == MODE_STATES;
+    static constexpr bool vreg = MODE == MODE_SEG || MODE == MODE_STATES;   // v^T tile
     // The large tiles (bf16 at C = 128, fp32 at D = 128 and C = 64) fit only
     // with up to three savings: the exact path's block-referenced q^ written
     // over the q tile (the output phase rescales its fragments), the gate rows
@@ -73,7 +74,7 @@ template <typename E, int D, int C, int MODE> struct Layout {
     static constexpr int kt = qh + (scores ? C * QP * es : 0);
     static constexpr int kht = kt + (scores ? C * QP * es : 0);
     static constexpr int vt = kht + (state ? D * TP * es : 0);             // state pass: v^T
-    static constexpr int a = vt + (MODE == MODE_SEG ? D * TP * es : 0);
+    static constexpr int a = vt + (vreg ? D * TP * es : 0);
     static constexpr int qb = a + (MODE == MODE_OUT && !a_in_kt ? C * TP * es : 0);   // exact path: q^ (block references)
     static constexpr int btot = qb + (scores && !qb_in_qh ? C * QP * es : 0);   // float [2][NU][D]
     static constexpr int eg = btot + 2 * NU * D * 4;              // float [D] exp2(Gamma)
@@ -155,8 +156,11 @@ chunk_kernel(const KernelParams p) {
     constexpr bool kSeg = MODE == MODE_SEG;
     constexpr bool kIntra = MODE == MODE_INTRA;
     constexpr bool kCumsum = MODE == MODE_CUMSUM;
+    constexpr bool kStates = MODE == MODE_STATES;
     constexpr bool kScores = kOut || kIntra;     // needs the score matrix
-    constexpr bool kState = kOut || kSeg;        // carries S
+    constexpr bool kState = kOut || kSeg || kStates;   // carries S
+    constexpr bool kFrom = kOut || kStates;      // S starts from h0 / the scanned segment states
+    constexpr bool kEnd = kSeg || kStates;       // update operand k exp(Gamma - Gc) from suffix sums
     using L = Layout<E, D, C, MODE>;
     using lds_t = typename E::lds_t;
     using gmem_t = typename E::gmem_t;
@@ -200,7 +204,7 @@ chunk_kernel(const KernelParams p) {
     f32x4_t S[MT][NTW];
     if constexpr (kState) {
         const float *src = nullptr;
-        if constexpr (kOut) {
+        if constexpr (kFrom) {
             if (seg == 0) src = p.h0 ? p.h0 + bh * D * D : nullptr;
             else src = p.ws_E + (bhl * p.ws_slots + seg * p.sub - 1) * long(D) * D;
         }
@@ -220,7 +224,7 @@ chunk_kernel(const KernelParams p) {
     for (int u = 0; u < CPL; ++u) seg_gamma[u] = 0.f;
 
     // ---- raw rows of the current chunk (this wave's RPW rows, CPL columns) --
-    constexpr bool kVreg = kSeg;   // v through registers into v^T (state pass)
+    constexpr bool kVreg = kEnd;   // v through registers into v^T (state-only passes)
     constexpr bool kVdma = kOut;   // v straight into LDS rows (output pass)
     Raw<E, CPL> rq[RPW], rk[RPW], rv[RPW];
     constexpr int es = sizeof(gmem_t);
@@ -335,6 +339,38 @@ chunk_kernel(const KernelParams p) {
         }
     };
 
+    // chunk c's start state S into `dump` (fp32, row-major D x D per chunk)
+    // or, states-only mode, `dump16` (bf16 in 16 x 16 tiles, the layout of
+    // bf16_state_offset: a 4 x 4 transpose within each lane quad (DPP) gives
+    // a lane four consecutive columns of one row, so a wave stores a whole
+    // 512-byte tile with one 8-byte store per lane)
+    auto dump_start = [&](int c) {
+        if (p.dump) {
+            float *dst = p.dump + (bh * long(p.N) + c) * long(D) * D;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
+        } else if (kStates && p.dump16) {
+            unsigned char *dst = static_cast<unsigned char *>(p.dump16) + (bh * long(p.N) + c) * long(D) * D * 2;
+            const int j = n16 & 3;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    float x[4] = {S[mt][nt][0], S[mt][nt][1], S[mt][nt][2], S[mt][nt][3]};
+                    quad_transpose4(x, j);
+                    // x[b] = S[16 mt + 4 q4 + j][vb + 16 nt + 4 (n16 / 4) + b]
+                    const uint32_t lo = pack_bf16x2(x[0], x[1]), hi = pack_bf16x2(x[2], x[3]);
+                    *reinterpret_cast<u32x2_t *>(dst + 2 * bf16_state_offset<D>(16 * mt + 4 * q4 + j, vb + 16 * nt + 4 * (n16 >> 2))) =
+                        u32x2_t{lo, hi};
+                }
+        }
+    };
+
     int buf = 0;
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
@@ -371,7 +407,7 @@ chunk_kernel(const KernelParams p) {
                     if (i % UR == UR - 1) sBtot[(buf * NU + w * UPW + i / UR) * D + lane * CPL + u] = urun;
                 }
             }
-            if constexpr (kSeg) {
+            if constexpr (kEnd) {
                 float suf = 0.f;
 #pragma unroll
                 for (int i = RPW - 1; i >= 0; --i) {
@@ -529,7 +565,7 @@ chunk_kernel(const KernelParams p) {
                 for (int u = 0; u < CPL; ++u) store_col(sKht, lane * CPL + u, kh[u]);
             }
         }
-        if constexpr (kSeg) {
+        if constexpr (kEnd) {
 #pragma unroll
             for (int u = 0; u < CPL; ++u) {
                 float kk[RPW];
@@ -805,36 +841,10 @@ chunk_kernel(const KernelParams p) {
                 if constexpr (kVdma) vf[nt][ts] = E::ld_col8(sV, L::VP, ts * 32 + 8 * q4, vb + 16 * nt, n16);
                 else vf[nt][ts] = E::ld_frag(sVt + (vb + 16 * nt + n16) * L::TP + ts * 32 + 8 * q4);
 
+        if constexpr (kStates) dump_start(c);
         if constexpr (kOut) {
             block_sync();  // B3: score tiles visible
-            if (p.dump) {     // chunk-start states (stage test only)
-                float *dst = p.dump + (bh * long(p.N) + c) * long(D) * D;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            dst[(16 * mt + 4 * q4 + e) * D + vb + 16 * nt + n16] = S[mt][nt][e];
-            } else if (p.dump16) {
-                // the same in bf16 (the backward's), in 16 x 16 tiles (layout of
-                // bf16_state_offset): a 4 x 4 transpose within each lane quad (DPP)
-                // gives a lane four consecutive columns of one row, so a wave
-                // stores a whole 512-byte tile with one 8-byte store per lane
-                unsigned char *dst = static_cast<unsigned char *>(p.dump16) + (bh * long(p.N) + c) * long(D) * D * 2;
-                const int j = n16 & 3;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) {
-                        float x[4] = {S[mt][nt][0], S[mt][nt][1], S[mt][nt][2], S[mt][nt][3]};
-                        quad_transpose4(x, j);
-                        // x[b] = S[16 mt + 4 q4 + j][vb + 16 nt + 4 (n16 / 4) + b]
-                        const uint32_t lo = pack_bf16x2(x[0], x[1]), hi = pack_bf16x2(x[2], x[3]);
-                        *reinterpret_cast<u32x2_t *>(dst + 2 * bf16_state_offset<D>(16 * mt + 4 * q4 + j, vb + 16 * nt + 4 * (n16 >> 2))) =
-                            u32x2_t{lo, hi};
-                    }
-            }
+            dump_start(c);   // chunk-start states, when asked for (stage output)
             // every wave holds its v fragments: the next chunk's v rows may land
             load_v(cn);
             // ---- a4: O^T tiles (value tile nt, token tile m) ---------------------
@@ -932,7 +942,7 @@ chunk_kernel(const KernelParams p) {
     // ---- segment end --------------------------------------------------------
     if constexpr (kState) {
         float *dst = nullptr;
-        if constexpr (kOut) {
+        if constexpr (kFrom) {
             if (seg == p.P - 1 && p.h_final) dst = p.h_final + bh * long(D) * D;
         } else {
             dst = p.ws_E + (bhl * p.ws_slots + seg) * long(D) * D;
@@ -1417,6 +1427,9 @@ static hipError_t dispatch_mode(int mode, bool sg, const KernelParams &p, int gx
             if constexpr (!seg_ok) return hipErrorInvalidValue;
             else if constexpr (std::is_same<E, BF16>::value) return launch_state<D, C, false>(p, gx, gy, s);
             else return launch_one<E, D, C, MODE_SEG, false>(p, gx, gy, s);
+        case MODE_STATES:
+            if constexpr (!seg_ok) return hipErrorInvalidValue;
+            else return launch_one<E, D, C, MODE_STATES, false>(p, gx, gy, s);
         case MODE_INTRA: return launch_one<E, D, C, MODE_INTRA, false>(p, gx, gy, s);
         case MODE_CUMSUM: return launch_one<E, D, C, MODE_CUMSUM, false>(p, gx, gy, s);
         default: return hipErrorInvalidValue;
