@@ -159,7 +159,8 @@ def algorithmic_bytes(wl) -> int:
 
 
 KIND_NAMES = {"output": "output pass (chunk_kernel, MODE_OUT)", "segment": "state pass (state_kernel)",
-              "scan": "segment-state scan (scan_kernel)"}
+              "scan": "segment-state scan (scan_kernel)",
+              "states": "states-only forward pass of the backward (chunk_kernel, MODE_STATES)"}
 
 
 def pass_bytes(wl, kind: str):
@@ -650,7 +651,7 @@ def read_counters(wl_name: str):
 def kernel_kind(name: str):
     """The pass a kernel name in a rocprofv3 trace belongs to (None: not ours)."""
     if "chunk_kernel" in name:
-        return {"0": "output", "1": "segment"}.get(name.split(",")[3].strip(" >")[:1])
+        return {"0": "output", "1": "segment", "4": "states"}.get(name.split(",")[3].strip(" >")[:1])
     if "state_kernel" in name:   # 4th template argument: the backward's segment pass
         return "bwd_segment" if name.split(",")[3].strip(" >)(").startswith("true") else "segment"
     if "scan_kernel" in name:

@@ -31,7 +31,8 @@ EXPORTED = ("gla_fwd", "gla_fwd_f32", "gla_set_tuning", "gla_strerror", "gla_ver
             "gla_fwd_scalar", "gla_fwd_scalar_f32", "gla_bwd", "gla_bwd_f32", "gla_gdn_fwd",
             "gla_gdn_set_path", "gla_workspace_bytes", "gla_fwd_noalloc")
 KERNEL_KINDS = {0: "output", 1: "segment", 2: "scan", 3: "other", 4: "decode", 5: "bwd_segment",
-                6: "bwd", 7: "gdn", 8: "gdn_prep", 9: "gdn_walk"}
+                6: "bwd", 7: "gdn", 8: "gdn_prep", 9: "gdn_walk",
+                10: "states"}
 GDN_PATHS = {"auto": 0, "one": 1, "two": 2}
 
 

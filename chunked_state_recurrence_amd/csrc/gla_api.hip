@@ -313,7 +313,7 @@ int run_forward(Call &c, float *fixed_ws = nullptr, size_t fixed_cap = 0) {
         // no o wanted (the backward's chunk-start states): the states-only
         // mode, which forms no scores
         const int mode = !c.need_o && (c.states || c.states16) ? gla::MODE_STATES : gla::MODE_OUT;
-        if (traced(GLA_KERNEL_OUTPUT, c.stream, [&] {
+        if (traced(mode == gla::MODE_STATES ? GLA_KERNEL_STATES : GLA_KERNEL_OUTPUT, c.stream, [&] {
                 return gla::launch_chunk_kernel(c.dtype, D, c.chunk, mode, c.scalar_gate, p, pl.P, nbh, c.stream);
             }) != hipSuccess)
             return GLA_ERR_LAUNCH;

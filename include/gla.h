@@ -128,8 +128,8 @@ int gla_set_tuning(int target_wgs, int head_group);
  * Launch tracing.  Between gla_profile_start and gla_profile_stop every
  * kernel the library enqueues is bracketed by two HIP events recorded on
  * the launch stream, so its device duration can be read back.  Kinds:
- * GLA_KERNEL_OUTPUT (the fused chunk pass that writes o, or in the
- * backward the chunk-start states), GLA_KERNEL_SEGMENT
+ * GLA_KERNEL_OUTPUT (the fused chunk pass that writes o), GLA_KERNEL_STATES
+ * (the backward's states-only forward chunk pass), GLA_KERNEL_SEGMENT
  * (segment end states), GLA_KERNEL_SCAN (segment-state scan),
  * GLA_KERNEL_DECODE (a gla_decode step, gla_decode.h), GLA_KERNEL_BWD_SEGMENT
  * and GLA_KERNEL_BWD (the backward's segment pass and chunk pass,
@@ -154,6 +154,7 @@ int gla_set_tuning(int target_wgs, int head_group);
 #define GLA_KERNEL_GDN     7
 #define GLA_KERNEL_GDN_PREP 8
 #define GLA_KERNEL_GDN_WALK 9
+#define GLA_KERNEL_STATES  10
 typedef struct {
     int kind;     /* GLA_KERNEL_* */
     float ms;     /* device time between the bracketing events */

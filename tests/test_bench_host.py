@@ -36,6 +36,7 @@ def test_summarize_counters_classifies_kernels(tmp_path, monkeypatch):
         "void gla::state_kernel<128, 64, false, true>(gla::KernelParams)": "bwd_segment",
         "gla::scan_kernel(float*, float const*, float const*, long, int, int, int)": "scan",
         "void gla::chunk_kernel<gla::BF16, 128, 64, 0, false>(gla::KernelParams)": "output",
+        "void gla::chunk_kernel<gla::BF16, 128, 64, 4, false>(gla::KernelParams)": "states",
         "void gla::bwd_kernel<gla::BF16, 128, 64, 1>(gla::BwdParams)": "bwd",
     }
     rows = []
