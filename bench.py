@@ -107,6 +107,25 @@ def host_threads() -> int:
         return os.cpu_count() or 1
 
 
+def gpu_product_name():
+    """The GPU's marketing name where the device properties leave it empty:
+    the first "Marketing Name" of a GPU agent in rocminfo's listing (a child
+    process), else None."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    name = None
+    for line in out.splitlines():
+        line = line.strip()
+        if line.startswith("Marketing Name:"):
+            name = line.split(":", 1)[1].strip()
+        elif line.startswith("Device Type:") and line.split(":", 1)[1].strip() == "GPU" and name:
+            return name
+    return None
+
+
 def environment() -> dict:
     """GPU, ROCm and host CPU the numbers were measured on."""
     env = {"nproc": host_threads(), "os_cpu_count": os.cpu_count()}
@@ -137,7 +156,7 @@ def environment() -> dict:
         env["torch_hip"] = torch.version.hip
         if torch.cuda.is_available():
             prop = torch.cuda.get_device_properties(0)
-            env["gpu"] = prop.name
+            env["gpu"] = prop.name or gpu_product_name()
             env["gpu_arch"] = getattr(prop, "gcnArchName", None)
             env["gpu_cus"] = prop.multi_processor_count
             env["gpu_mem_gib"] = round(prop.total_memory / 2 ** 30, 1)
