@@ -67,6 +67,20 @@ struct BF16 {
         const s8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         return __builtin_bit_cast(frag_t, v);
     }
+    // the same from two runs of 4 rows, k_lo.. and k_hi..: the order in which
+    // a 16 x 16 accumulator pair (rows 4 q4 + e of tiles 2 ts and 2 ts + 1)
+    // holds a 32-deep token step, so such a pair packed to bf16 is the other
+    // operand as it stands
+    __device__ static frag_t ld_col4x2(const unsigned char *tile, int pitch, int k_lo, int k_hi, int c0, int n16) {
+        typedef short s4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s4_t *lds_s4_p;
+        const int lane_off = (n16 >> 2) * pitch + (c0 + 4 * (n16 & 3)) * 2;
+        const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_p)(tile + rowoff(k_lo, pitch) + lane_off));
+        const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_p)(tile + rowoff(k_hi, pitch) + lane_off));
+        typedef short s8_t __attribute__((ext_vector_type(8)));
+        const s8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(frag_t, v);
+    }
     // store 4 consecutive outputs (8 bytes) at byte offset `off`
     __device__ static void st4(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
         typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));

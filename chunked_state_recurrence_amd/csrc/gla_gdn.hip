@@ -613,15 +613,13 @@ gdn_walk_kernel(const GdnParams p) {
     constexpr int KS = D / 32;
     constexpr int TS = C / 32;
     constexpr int NVB = D / 16;
-    constexpr int PU = 32;                                     // U tile: 16 bf16 columns a row
     constexpr int OU = R::images, OO = OU + R::blk, OG = OO + R::blk;
     constexpr int BUF = OG + 256;                              // one chunk's staged record
     constexpr int NIMG = R::images / 1024, NBLK = R::blk / 1024;
     constexpr int NISSUE = NIMG + 2 * NBLK + 1;                // direct loads per chunk
     static_assert(NISSUE <= 63, "vmcnt range");
-    static_assert(2 * BUF + E::tile_bytes(C, PU) <= 163840, "LDS");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF + E::tile_bytes(C, PU)];
-    unsigned char *tU = smem + 2 * BUF;
+    static_assert(2 * BUF <= 163840, "LDS");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
 
     const int lane = threadIdx.x;
     const int n16 = lane & 15;
@@ -679,11 +677,18 @@ gdn_walk_kernel(const GdnParams p) {
         const unsigned char *buf = smem + (c & 1) * BUF;
         const __bf16 *wi = reinterpret_cast<const __bf16 *>(buf + R::wi);
         const __bf16 *qi = reinterpret_cast<const __bf16 *>(buf + R::qi);
+        // O^T tiles as the record holds them (lane: one token, four value
+        // columns); U in the other orientation (lane: four tokens 16 m + 4 q4 + e
+        // of value column n16), so that it feeds the state update from its
+        // accumulators: U~ is read transposed out of the staged record
         f32x4_t U[NB], O[NB];
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
-            U[m] = *reinterpret_cast<const f32x4_t *>(buf + OU + m * 1024 + lane * 16);
             O[m] = *reinterpret_cast<const f32x4_t *>(buf + OO + m * 1024 + lane * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                U[m][e] = *reinterpret_cast<const float *>(buf + OU + m * 1024 + ((n16 >> 2) * 16 + 4 * q4 + e) * 16 +
+                                                          (n16 & 3) * 4);
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -693,30 +698,31 @@ gdn_walk_kernel(const GdnParams p) {
             const frag_t sf = E::pack(x);
 #pragma unroll
             for (int m = 0; m < NB; ++m) {
-                U[m] = E::mma(sf, E::ld_frag(wi + (16 * m + n16) * L::QP + ks * 32 + 8 * q4), U[m]);
+                U[m] = E::mma(E::ld_frag(wi + (16 * m + n16) * L::QP + ks * 32 + 8 * q4), sf, U[m]);
                 O[m] = E::mma(sf, E::ld_frag(qi + (16 * m + n16) * L::QP + ks * 32 + 8 * q4), O[m]);
             }
         }
         const int t0 = (p.c0 + c) * C;
 #pragma unroll
-        for (int m = 0; m < NB; ++m) {
-            E::st4(bo, ((t0 + 16 * m + n16) * D + vb + 4 * q4) * 2, O[m]);
-            __bf16 *dst = reinterpret_cast<__bf16 *>(tU + E::rowoff(16 * m + n16, PU)) + 4 * q4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = (__bf16)U[m][e];
-        }
-        wave_lds_fence();
+        for (int m = 0; m < NB; ++m) E::st4(bo, ((t0 + 16 * m + n16) * D + vb + 4 * q4) * 2, O[m]);
         const float gC = *reinterpret_cast<const float *>(buf + OG);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[mt][e] *= gC;
+        // U straight from its accumulators: lane (q4, n16) holds tokens
+        // 32 ts + 4 q4 + e and 32 ts + 16 + 4 q4 + e of column n16, and the
+        // k^ operand is read in the same token order
 #pragma unroll
         for (int ts = 0; ts < TS; ++ts) {
-            const frag_t uf = E::ld_col8(tU, PU, ts * 32 + 8 * q4, 0, n16);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[e] = U[2 * ts][e]; x[4 + e] = U[2 * ts + 1][e]; }
+            const frag_t uf = E::pack(x);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                S[mt] = E::mma(E::ld_col8(buf + R::ki, L::PD, ts * 32 + 8 * q4, 16 * mt, n16), uf, S[mt]);
+                S[mt] = E::mma(E::ld_col4x2(buf + R::ki, L::PD, ts * 32 + 4 * q4, ts * 32 + 16 + 4 * q4, 16 * mt, n16),
+                               uf, S[mt]);
         }
     }
     if (p.h_final) {
