@@ -210,12 +210,71 @@ bwd_kernel(const BwdParams p) {
         return reinterpret_cast<lds_t *>(tile + E::rowoff(r, pitch));
     };
 
+    // Chunk pass: the next chunk's v, do and gate rows are requested during
+    // this chunk's epilogue, once the v, do and U tiles are free (after B6):
+    // v and do rows into their tiles, gate rows (fp32, dense rows) into the U
+    // tile, which is written again only after B2.  The loads are untracked
+    // (dma_untracked): every operand tile and the Gc tile share one array, so
+    // the compiler, unable to tell them apart, would hold them at each read of
+    // the Gc tile.  Requested before the epilogue's own q / k rows, they land
+    // while those are awaited.  (bf16 at D = 64, C = 64: the gate rows do not
+    // fit the U tile, and each chunk loads its rows itself.)
+    constexpr bool kPre = kFull && C * D * 4 <= L::TU;
+    constexpr int NGL = RPW * D * 4 / 1024;   // 1 KB direct loads of a wave's gate rows
+    static_assert(!kPre || RPW * D * 4 % 1024 == 0, "gate rows per wave must fill whole loads");
+    auto prefetch = [&](int c) {
+        if constexpr (kPre) {
+            const int row0 = __builtin_amdgcn_readfirstlane(c * C + r0);
+            const int lr0 = __builtin_amdgcn_readfirstlane(r0);
+            // descriptor words in scalar registers (the loads below sit in lane-masked code)
+            auto uni = [](u32x4_t x) {
+                return u32x4_t{uint32_t(__builtin_amdgcn_readfirstlane(int(x[0]))), uint32_t(__builtin_amdgcn_readfirstlane(int(x[1]))),
+                               uint32_t(__builtin_amdgcn_readfirstlane(int(x[2]))), uint32_t(__builtin_amdgcn_readfirstlane(int(x[3])))};
+            };
+            const u32x4_t wg = uni(rsrc_words(p.g + bh * long(T) * D, long(T) * D * 4));
+            const u32x4_t wv = uni(rsrc_words(reinterpret_cast<const gmem_t *>(p.v) + bh * long(T) * D, long(T) * D * es));
+            const u32x4_t wo = uni(rsrc_words(reinterpret_cast<const gmem_t *>(p.dout) + bh * long(T) * D, long(T) * D * es));
+            mem_fence_compiler();
+#pragma unroll
+            for (int i = 0; i < NGL; ++i)
+                dma_untracked<16>(wg, lds_addr(tU) + lr0 * D * 4 + i * 1024, lane * 16, row0 * D * 4 + i * 1024);
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                if constexpr (es == 2) {   // 4 bytes per lane: a 64-wide row takes lanes 0..31
+                    if (CPL == 2 || lane < 32) {
+                        dma_untracked<4>(wv, lds_addr(tV) + E::rowoff(lr0 + i, L::PD), lane * 4, (row0 + i) * D * 2);
+                        dma_untracked<4>(wo, lds_addr(tO) + E::rowoff(lr0 + i, L::PD), lane * 4, (row0 + i) * D * 2);
+                    }
+                } else {                   // 16 bytes per lane, D / 4 lanes per row
+                    if (lane < D / 4) {
+                        dma_untracked<16>(wv, lds_addr(tV) + E::rowoff(lr0 + i, L::PD), lane * 16, (row0 + i) * D * 4);
+                        dma_untracked<16>(wo, lds_addr(tO) + E::rowoff(lr0 + i, L::PD), lane * 16, (row0 + i) * D * 4);
+                    }
+                }
+            }
+            mem_fence_compiler();
+        }
+    };
+    if (c_begin < c_end) prefetch(c_end - 1);
+
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int t0 = c * C;
         // ---- this chunk's rows: gates, q, k into registers; v, do into LDS ----
         RawG<CPL> rg[RPW];
         Raw<E, CPL> rq[RPW], rk[RPW];
-        {
+        if constexpr (kPre) {   // v, do and gate rows requested earlier
+            const int eoff = (t0 + r0) * D + lane * CPL;
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                rq[i].load(bq, eoff * es, i * D * es);
+                rk[i].load(bk, eoff * es, i * D * es);
+            }
+            mem_fence_compiler();
+            wait_vmem<2 * RPW>();   // everything before the q / k rows just requested
+#pragma unroll
+            for (int i = 0; i < RPW; ++i)
+                rg[i].x = *reinterpret_cast<const decltype(rg[i].x) *>(tU + ((r0 + i) * D + lane * CPL) * 4);
+        } else {
             const int eoff = (t0 + r0) * D + lane * CPL;
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
@@ -537,6 +596,7 @@ bwd_kernel(const BwdParams p) {
             // Kept apart, their loops leave the epilogue's registers alone.
             const rsrc_t bst = make_rsrc(static_cast<const unsigned char *>(p.states) + (bh * long(N) + c) * long(D) * D * kSes,
                                          D * D * kSes);
+            if (c > c_begin) prefetch(c - 1);
             if (!fast) {
 #pragma unroll 1
                 for (int nt = 0; nt < NTW; ++nt) {
