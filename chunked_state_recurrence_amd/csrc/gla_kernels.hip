@@ -1318,21 +1318,25 @@ scan_kernel(float *__restrict__ ws_E, const float *__restrict__ ws_G,
 // the same recurrence one token at a time (blog "Linear Attention 在 GPU 上到底
 // 慢在哪", section 学长的反馈; "线性注意力GPU算子库的定义与技术解析", section 四).
 // Bound by the state traffic: each (batch, head) reads and writes D*D fp32.
-// Work-group = 32 value columns of one (batch, head); thread t owns columns
-// c0 + 4 (t % 8) .. +3 and rows t / 8 + 32 i.
+// Work-group = one (batch, head), 256 threads: thread t owns value columns
+// 4 (t % QN) .. +3 (QN = D / 4 column quads) and state rows t / QN + RB i
+// (RB = 256 / QN row groups), each row piece one 16-byte load and store.
+// Whole rows per work-group measured faster than 32 or 64 columns (fewer,
+// longer work-groups with more state in flight each).
 // ---------------------------------------------------------------------------
-template <typename E, int D>
+template <typename E, int D, int CB = D>
 __global__ void __launch_bounds__(256)
 decode_kernel(const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
               const float *__restrict__ g, float *__restrict__ state, void *__restrict__ o, float scale) {
     using gmem_t = typename E::gmem_t;
-    constexpr int CB = 32;   // value columns per work-group
-    constexpr int RB = 32;   // row groups (256 threads = 32 row groups x 8 column quads)
+    constexpr int QN = CB / 4;      // column quads
+    constexpr int RB = 256 / QN;    // row groups
+    static_assert(QN <= 64 && D % RB == 0, "decode tile");
     const long bh = blockIdx.x;
     const int c0 = blockIdx.y * CB;
     const int t = threadIdx.x;
-    const int cq = t & 7;
-    const int rb = t >> 3;
+    const int cq = t % QN;
+    const int rb = t / QN;
     const gmem_t *qp = reinterpret_cast<const gmem_t *>(q) + bh * D;
     const gmem_t *kp = reinterpret_cast<const gmem_t *>(k) + bh * D;
     const gmem_t *vp = reinterpret_cast<const gmem_t *>(v) + bh * D;
@@ -1357,13 +1361,13 @@ decode_kernel(const void *__restrict__ q, const void *__restrict__ k, const void
         }
         *reinterpret_cast<f32x4_t *>(S + r * D) = sv;
     }
-    // sum over the row groups: 8 per wave (lane / 8), then over the 4 waves
+    // sum over the row groups: 64 / QN per wave (lane / QN), then over the 4 waves
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int m = 8; m <= 32; m <<= 1) acc[e] += __shfl_xor(acc[e], m, 64);
+        for (int m = QN; m <= 32; m <<= 1) acc[e] += __shfl_xor(acc[e], m, 64);
     __shared__ float red[4][CB];
-    if ((t & 63) < 8)
+    if ((t & 63) < QN)
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[t >> 6][4 * cq + e] = acc[e];
     __syncthreads();
@@ -1491,7 +1495,7 @@ hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0
 hipError_t launch_decode(int dtype, int D, const void *q, const void *k, const void *v, const float *g,
                          float *state, void *o, long nbh, float scale, hipStream_t s) {
     if (nbh <= 0) return hipSuccess;
-    const dim3 grid(unsigned(nbh), unsigned(D / 32));
+    const dim3 grid(unsigned(nbh), 1u);
     if (dtype == DTYPE_BF16) {
         if (D == 128) hipLaunchKernelGGL((decode_kernel<BF16, 128>), grid, dim3(256), 0, s, q, k, v, g, state, o, scale);
         else if (D == 64) hipLaunchKernelGGL((decode_kernel<BF16, 64>), grid, dim3(256), 0, s, q, k, v, g, state, o, scale);
