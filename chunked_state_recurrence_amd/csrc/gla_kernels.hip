@@ -1324,16 +1324,15 @@ scan_kernel(float *__restrict__ ws_E, const float *__restrict__ ws_G,
 // Whole rows per work-group measured faster than 32 or 64 columns (fewer,
 // longer work-groups with more state in flight each).
 // ---------------------------------------------------------------------------
-template <typename E, int D, int CB = D>
+template <typename E, int D>
 __global__ void __launch_bounds__(256)
 decode_kernel(const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
               const float *__restrict__ g, float *__restrict__ state, void *__restrict__ o, float scale) {
     using gmem_t = typename E::gmem_t;
-    constexpr int QN = CB / 4;      // column quads
+    constexpr int QN = D / 4;       // column quads
     constexpr int RB = 256 / QN;    // row groups
     static_assert(QN <= 64 && D % RB == 0, "decode tile");
     const long bh = blockIdx.x;
-    const int c0 = blockIdx.y * CB;
     const int t = threadIdx.x;
     const int cq = t % QN;
     const int rb = t / QN;
@@ -1341,11 +1340,11 @@ decode_kernel(const void *__restrict__ q, const void *__restrict__ k, const void
     const gmem_t *kp = reinterpret_cast<const gmem_t *>(k) + bh * D;
     const gmem_t *vp = reinterpret_cast<const gmem_t *>(v) + bh * D;
     const float *gp = g + bh * D;
-    float *S = state + bh * D * D + c0 + 4 * cq;
+    float *S = state + bh * D * D + 4 * cq;
     float vv[4], acc[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        vv[e] = E::g2f(vp[c0 + 4 * cq + e]);
+        vv[e] = E::g2f(vp[4 * cq + e]);
         acc[e] = 0.f;
     }
 #pragma unroll
@@ -1366,15 +1365,15 @@ decode_kernel(const void *__restrict__ q, const void *__restrict__ k, const void
     for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int m = QN; m <= 32; m <<= 1) acc[e] += __shfl_xor(acc[e], m, 64);
-    __shared__ float red[4][CB];
+    __shared__ float red[4][D];
     if ((t & 63) < QN)
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[t >> 6][4 * cq + e] = acc[e];
     __syncthreads();
-    if (t < CB) {
+    if (t < D) {
         const float x = scale * (red[0][t] + red[1][t] + red[2][t] + red[3][t]);
-        if constexpr (sizeof(gmem_t) == 2) reinterpret_cast<__bf16 *>(o)[bh * D + c0 + t] = (__bf16)x;
-        else reinterpret_cast<float *>(o)[bh * D + c0 + t] = x;
+        if constexpr (sizeof(gmem_t) == 2) reinterpret_cast<__bf16 *>(o)[bh * D + t] = (__bf16)x;
+        else reinterpret_cast<float *>(o)[bh * D + t] = x;
     }
 }
 
@@ -1495,7 +1494,7 @@ hipError_t launch_scan(float *ws_E, const float *ws_G, const float *h0, long bh0
 hipError_t launch_decode(int dtype, int D, const void *q, const void *k, const void *v, const float *g,
                          float *state, void *o, long nbh, float scale, hipStream_t s) {
     if (nbh <= 0) return hipSuccess;
-    const dim3 grid(unsigned(nbh), 1u);
+    const dim3 grid(static_cast<unsigned>(nbh));
     if (dtype == DTYPE_BF16) {
         if (D == 128) hipLaunchKernelGGL((decode_kernel<BF16, 128>), grid, dim3(256), 0, s, q, k, v, g, state, o, scale);
         else if (D == 64) hipLaunchKernelGGL((decode_kernel<BF16, 64>), grid, dim3(256), 0, s, q, k, v, g, state, o, scale);
