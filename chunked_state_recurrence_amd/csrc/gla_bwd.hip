@@ -460,6 +460,24 @@ bwd_kernel(const BwdParams p) {
             const rsrc_t bs = make_rsrc(static_cast<const unsigned char *>(p.states) + (bh * long(N) + c) * long(D) * D * kSes,
                                         D * D * kSes);
             const rsrc_t bdv = make_rsrc(reinterpret_cast<gmem_t *>(p.dv) + bh * long(T) * D, long(T) * D * es);
+            // this wave's rows of the chunk-start state S_n for the dq step,
+            // requested now so that they arrive during the dv, dk2 and U products
+            constexpr int SL = kS16 ? 1 : 2;   // 16-byte loads per key step
+            u32x4_t sraw[NTW][KS][SL];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if constexpr (kS16) {   // eight bf16 states (16 x 16 tiles): the operand as stored
+                        const int voff = 2 * bf16_state_offset<D>(n16, 8 * q4);
+                        const int soff = 2 * bf16_state_offset<D>(cb + 16 * nt, ks * 32);
+                        sraw[nt][ks][0] = __builtin_amdgcn_raw_buffer_load_b128(bs, voff, soff, 0);
+                    } else {
+                        const int voff = ((cb + n16) * D + 8 * q4) * 4, soff = (16 * nt * D + ks * 32) * 4;
+                        sraw[nt][ks][0] = __builtin_amdgcn_raw_buffer_load_b128(bs, voff, soff, 0);
+                        sraw[nt][ks][SL - 1] = __builtin_amdgcn_raw_buffer_load_b128(bs, voff + 16, soff, 0);
+                    }
+                }
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 f32x4_t Dv[NB];
@@ -528,15 +546,12 @@ bwd_kernel(const BwdParams p) {
                 for (int ks = 0; ks < KS; ++ks) {
                     float xs[8];
                     frag_t sf;
-                    if constexpr (kS16) {   // eight bf16 states (16 x 16 tiles): the operand as stored
-                        const int voff = 2 * bf16_state_offset<D>(n16, 8 * q4);
-                        const int soff = 2 * bf16_state_offset<D>(cb + 16 * nt, ks * 32);
-                        sf = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff, soff, 0));
+                    if constexpr (kS16) {
+                        sf = __builtin_bit_cast(frag_t, sraw[nt][ks][0]);
                         E::unpack(sf, xs);
                     } else {
-                        const int voff = ((cb + n16) * D + 8 * q4) * 4, soff = (16 * nt * D + ks * 32) * 4;
-                        const f32x4_t lo = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff, soff, 0));
-                        const f32x4_t hi = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bs, voff + 16, soff, 0));
+                        const f32x4_t lo = __builtin_bit_cast(f32x4_t, sraw[nt][ks][0]);
+                        const f32x4_t hi = __builtin_bit_cast(f32x4_t, sraw[nt][ks][SL - 1]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) { xs[e] = lo[e]; xs[4 + e] = hi[e]; }
                         sf = E::pack(xs);
