@@ -13,7 +13,8 @@
 // state, u_i = beta_i (v_i - exp(g_i) k_i S_{i-1}), satisfy
 //     (I + A) U = diag(beta) V - diag(beta gamma) K S,
 //     A_ij = beta_i (gamma_i / gamma_j) (k_i . k_j)        (j < i),
-// so with T = (I + A)^{-1}:  U = T diag(beta) V - W S,  W = T diag(beta) (gamma K),
+// so with T = (I + A)^{-1}:  U = T diag(beta) (V - (gamma K) S) = U~ - W S with
+// U~ = T diag(beta) V and W = T diag(beta) (gamma K), and
 //     o_i    = scale [ gamma_i q_i S + sum_{j<=i} (gamma_i / gamma_j) (q_i . k_j) u_j ]
 //     S_next = gamma_C S + sum_j (gamma_C / gamma_j) k_j^T u_j.
 // Every factor is at most 1 (gamma_i / gamma_j with j <= i), so extreme gates
@@ -25,7 +26,10 @@
 // in order.  Value columns of S evolve independently (the state is mixed only
 // along its key rows), so when batch x heads would leave CUs idle the value
 // columns are split over several work-groups; each one forms the chunk-local
-// A, P, T and W for all key dims and U, o, S for its own columns.  S stays in
+// A, P and T for all key dims and U, o, S for its own columns.  The products
+// that need S but not T, V - (gamma K) S and (scale gamma q) S, run while one
+// wave solves T's diagonal blocks and three more its off-diagonal ones; U is
+// then T diag(beta) times the first, and W is never formed.  S stays in
 // MFMA accumulators (the block's value columns are spread 16 per wave over
 // its first waves) and is fed to the S products straight from them (the row
 // operand's columns are permuted in LDS, as in the forward output pass).
@@ -54,8 +58,12 @@ __device__ __forceinline__ float wave_dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
 }
 
-template <int D, int C> struct GdnLayout {
-    static constexpr int QP = D + 8;                 // permuted-row tiles, bf16 elements per row
+// WIDE (the one-launch kernel): permuted rows padded by 32 bytes (288 / 160
+// bytes), on which a 16-row fragment read takes one LDS pass instead of two;
+// the prep kernel keeps 16-byte pads, since its tiles are the byte images of
+// the records, whose size bounds the walk's direct loads per chunk.
+template <int D, int C, bool WIDE = false> struct GdnLayout {
+    static constexpr int QP = D + (WIDE ? 16 : 8);   // permuted-row tiles, bf16 elements per row
     static constexpr int PD = 2 * D + 32;            // bank-spread bf16 tiles, bytes per row
     static constexpr int PC = 2 * C + 32;            // bank-spread bf16 C x C tiles
     static constexpr int PF = C + 4;                 // fp32 C x C tiles, floats per row
@@ -113,6 +121,16 @@ __device__ __forceinline__ f32x4_t mma16_f32(const float *A, int pa, const float
 
 __device__ __forceinline__ void wave_lds_fence() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// four consecutive bf16 of an LDS row (8 bytes) from fp32
+__device__ __forceinline__ void st_row4(__bf16 *dst, f32x4_t x) {
+    bf16x4_t b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = (__bf16)x[e];
+    *reinterpret_cast<bf16x4_t *>(dst) = b;
+}
+
 // PREP = false: the whole recurrence, one work-group per (batch, head, value
 // block) walking every chunk.  PREP = true: the chunk-local half only (no
 // state), work-group (head, slice) taking chunks slice, slice + slices, ... of
@@ -121,7 +139,7 @@ template <int D, int C, bool PREP>
 __global__ void __launch_bounds__((Shape<D, C>::NW * 64))
 gdn_kernel(const GdnParams p) {
     using E = BF16;
-    using L = GdnLayout<D, C>;
+    using L = GdnLayout<D, C, !PREP>;
     using frag_t = E::frag_t;
     constexpr int NW = Shape<D, C>::NW;
     constexpr int RPW = Shape<D, C>::RPW;
@@ -134,6 +152,7 @@ gdn_kernel(const GdnParams p) {
     constexpr int TS = C / 32;
     constexpr int NTILE = NB * (NB + 1) / 2;
     static_assert(C == 64 && NB == 4, "the blocked inverse is written for 64-row chunks");
+    static_assert(NW >= NB, "one wave per column of T's off-diagonal blocks, another for its diagonal");
     static_assert(L::bytes + 2 * C * 4 <= 163840, "LDS");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::main_bytes];
@@ -141,6 +160,7 @@ gdn_kernel(const GdnParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char sVV[L::v_bytes];
     __shared__ float sGc[C];     // chunk-local inclusive cumsum of g, log2 units
     __shared__ float sBeta[C];
+
     unsigned char *tKr = smem + L::kr;   // raw k, row-major (then -W, permuted)
     unsigned char *tQr = smem + L::qr;   // raw q, row-major (then U, bank-spread)
     unsigned char *tKg = smem + L::kg;   // gamma k, then (gamma_C / gamma) k
@@ -151,6 +171,8 @@ gdn_kernel(const GdnParams p) {
     float *tA = reinterpret_cast<float *>(sAT);
     float *tT = tA + C * L::PF;
     __bf16 *tW = reinterpret_cast<__bf16 *>(tKr);
+    __bf16 *tKh = reinterpret_cast<__bf16 *>(tKg);   // one launch: gamma k, permuted columns
+    static_assert(L::TQ <= L::TD, "permuted gamma k over the gamma k tile");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -280,7 +302,8 @@ gdn_kernel(const GdnParams p) {
                 const float qv = rq[i].get(u), kv = rk[i].get(u);
                 reinterpret_cast<__bf16 *>(tKr)[r * L::QP + col] = (__bf16)kv;
                 reinterpret_cast<__bf16 *>(tQr)[r * L::QP + col] = (__bf16)qv;
-                rowp(tKg, r, L::PD)[col] = (__bf16)(kv * gam);
+                if constexpr (PREP) rowp(tKg, r, L::PD)[col] = (__bf16)(kv * gam);
+                else tKh[r * L::QP + perm_col(col)] = (__bf16)(kv * gam);
                 tQh[r * L::QP + perm_col(col)] = (__bf16)(qv * gam * p.scale);
             }
         }
@@ -318,9 +341,59 @@ gdn_kernel(const GdnParams p) {
         }
         block_sync();  // B3: A, P
 
-        // ---- T = (I + A)^{-1}: diagonal blocks by substitution (wave 0, one lane
-        //      per column of each of the four blocks) ---------------------------------
-        if (w == 0) {
+        // One launch: the products that do not need T run while it is formed, in
+        // each wave that owns value columns and is not making T at the time:
+        //   O = (scale gamma q) S  and  V' = V - (gamma K) S  for its columns, S
+        //   straight from its accumulators, V' (bf16) into the former raw q tile;
+        // after T, U = T diag(beta) V' replaces U~ - W S, so W is never formed.
+        f32x4_t O[NTW][NB];
+        auto resid_and_o = [&]() {
+            f32x4_t G[NTW][NB];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    O[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    G[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                frag_t sf[NTW];
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { x[e] = S[2 * ks][nt][e]; x[4 + e] = S[2 * ks + 1][nt][e]; }
+                    sf[nt] = E::pack(x);
+                }
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    const frag_t kf = E::ld_frag(tKh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
+                    const frag_t qf = E::ld_frag(tQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) {
+                        G[nt][m] = E::mma(sf[nt], kf, G[nt][m]);
+                        O[nt][m] = E::mma(sf[nt], qf, O[nt][m]);
+                    }
+                }
+            }
+            // acc[e] = X[row 16m + n16][col vb + 16nt + 4q4 + e]
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int m = 0; m < NB; ++m) {
+                    const int co = vb + 16 * nt + 4 * q4;
+                    const bf16x4_t v = *reinterpret_cast<const bf16x4_t *>(rowp(tV, 16 * m + n16, L::PD) + co);
+                    f32x4_t r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[e] = float(v[e]) - G[nt][m][e];
+                    st_row4(rowp(tQr, 16 * m + n16, L::PD) + co, r);
+                }
+        };
+
+        // ---- T = (I + A)^{-1}: diagonal blocks by substitution (the last wave, one
+        //      lane per column of each of the four blocks) ----------------------------
+        if (w == NW - 1) {
             const int blk = lane >> 4, col = lane & 15;
             float tcol[16];
 #pragma unroll
@@ -336,16 +409,18 @@ gdn_kernel(const GdnParams p) {
                 tT[(16 * blk + i) * L::PF + 16 * blk + col] = tcol[i];
                 rowp(tTb, 16 * blk + i, L::PC)[16 * blk + col] = (__bf16)(tcol[i] * bc);
             }
+        } else if constexpr (!PREP) {
+            if (vw) resid_and_o();
         }
         block_sync();  // B4: diagonal blocks of T
-        // off-diagonal blocks: wave J makes column J of T, T_{J+1,J}, T_{J+2,J}, ...
-        // in turn; each needs only the diagonal blocks, A and the column's own
-        // earlier blocks (this wave's stores, seen after its LDS fence), so the
-        // levels need no barrier between them
-        if (w < NB - 1) {
+        // off-diagonal blocks: wave NW - NB + J makes column J of T, T_{J+1,J},
+        // T_{J+2,J}, ... in turn; each needs only the diagonal blocks, A and the
+        // column's own earlier blocks (this wave's stores, seen after its LDS
+        // fence), so the levels need no barrier between them
+        if (w >= NW - NB && w < NW - 1) {
 #pragma unroll
             for (int d = 1; d < NB; ++d) {
-                const int J = w, I = J + d;
+                const int J = w - (NW - NB), I = J + d;
                 if (I >= NB) break;
                 f32x4_t x = {0.f, 0.f, 0.f, 0.f};
                 for (int Kb = J; Kb < I; ++Kb)
@@ -374,8 +449,11 @@ gdn_kernel(const GdnParams p) {
                 }
                 wave_lds_fence();   // T_IJ visible to this wave's next block
             }
+        } else if constexpr (!PREP) {
+            if (w == NW - 1 && vw) resid_and_o();
         }
         block_sync();  // B5: T complete
+        if constexpr (PREP) {
         if (cn < N) issue_qk(cn);   // the A / T tiles are no longer read
 
         // ---- W = T diag(beta) (gamma K) and U~ = T diag(beta) V for this wave's
@@ -410,7 +488,6 @@ gdn_kernel(const GdnParams p) {
                 }
             }
         block_sync();  // B8: gamma k and v no longer read
-        if (!PREP && cn < N) issue_vg(cn);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
@@ -448,7 +525,6 @@ gdn_kernel(const GdnParams p) {
         }
         block_sync();  // B9: -W and the state-update rows visible
 
-        if constexpr (PREP) {
             // ---- Q' = scale gamma q - P W (in place over the permuted q tile) and
             //      O0 = P U~ (fp32, into the record); acc[e] = X[row 16m + n16][col + 4q4 + e]
             f32x4_t Qa[NTW][NB], Oa[NTW][NB];
@@ -499,82 +575,78 @@ gdn_kernel(const GdnParams p) {
             if (tid == 0) p.ws_gc[size_t(bh) * p.nc + c] = fexp2(gcl);
         } else {
 
-        // ---- U = U~ - W S and O = (scale gamma q) S, S straight from its accumulators ----
-        // (waves that own value columns only; the others wait at the barriers)
-        f32x4_t O[NTW][NB];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-            for (int m = 0; m < NB; ++m) O[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (vw) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            frag_t sf[NTW];
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { x[e] = S[2 * ks][nt][e]; x[4 + e] = S[2 * ks + 1][nt][e]; }
-                sf[nt] = E::pack(x);
-            }
-#pragma unroll
-            for (int m = 0; m < NB; ++m) {
-                const frag_t wf = E::ld_frag(tW + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
-                const frag_t qf = E::ld_frag(tQh + (16 * m + n16) * L::QP + ks * 32 + 8 * q4);
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    Ua[nt][m] = E::mma(sf[nt], wf, Ua[nt][m]);
-                    O[nt][m] = E::mma(sf[nt], qf, O[nt][m]);
-                }
-            }
+        // ---- U = T diag(beta) V' for this wave's columns (V' formed while T was),
+        //      into the former raw k tile; (gamma_C / gamma) k over gamma k;
+        //      O += P U; o rows to HBM; S <- gamma_C S + ((gamma_C / gamma) k)^T U ------
+        if (cn < N) {   // the A / T area and the v tile are no longer read
+            issue_qk(cn);
+            issue_vg(cn);
         }
-        // U rows into the (former raw q) region, bank-spread layout
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-            for (int m = 0; m < NB; ++m) {
-                __bf16 *dst = rowp(tQr, 16 * m + n16, L::PD) + vb + 16 * nt + 4 * q4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[e] = (__bf16)Ua[nt][m][e];
-            }
-        }
-        block_sync();  // B10: U visible
-
-        // ---- O += P U; o rows to HBM; S <- gamma_C S + ((gamma_C / gamma) k)^T U --------
-        const float gC = fexp2(gcl);
         if (vw) {
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-            for (int ts = 0; ts < TS; ++ts) {
-                if (ts * 32 > 16 * m + 15) continue;
-                const frag_t pf = E::ld_frag(rowp(tP, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    O[nt][m] = E::mma(E::ld_col8(tQr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), pf, O[nt][m]);
-            }
-#pragma unroll
-        for (int m = 0; m < NB; ++m)
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                E::st4(bo, ((t0 + 16 * m + n16) * D + vb + 16 * nt + 4 * q4) * 2, O[nt][m]);
-            }
-
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            f32x4_t Ua[NTW][NB];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[mt][nt][e] *= gC;
+                for (int m = 0; m < NB; ++m) Ua[nt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
-            for (int ts = 0; ts < TS; ++ts) {
-                const frag_t a = E::ld_col8(tKg, L::PD, ts * 32 + 8 * q4, 16 * mt, n16);
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const frag_t vf = E::ld_col8(tQr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16);
+#pragma unroll
+                    for (int m = 0; m < NB; ++m) {
+                        if (ts * 32 > 16 * m + 15) continue;   // T is lower triangular
+                        const frag_t tf = E::ld_frag(rowp(tTb, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
+                        Ua[nt][m] = E::mma(vf, tf, Ua[nt][m]);
+                    }
+                }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int m = 0; m < NB; ++m) st_row4(rowp(tKr, 16 * m + n16, L::PD) + vb + 16 * nt + 4 * q4, Ua[nt][m]);
+        }
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {   // (gamma_C / gamma) k over gamma k
+            const int r = r0 + i;
+            const float gk = fexp2(gcl - sGc[r]);
+#pragma unroll
+            for (int u = 0; u < CPL; ++u) rowp(tKg, r, L::PD)[lane * CPL + u] = (__bf16)(rk[i].get(u) * gk);
+        }
+        wave_lds_fence();   // this wave's U columns, read back below
+        const float gC = fexp2(gcl);
+        if (vw) {
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+                    if (ts * 32 > 16 * m + 15) continue;
+                    const frag_t pf = E::ld_frag(rowp(tP, 16 * m + n16, L::PC) + ts * 32 + 8 * q4);
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+                        O[nt][m] = E::mma(E::ld_col8(tKr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), pf, O[nt][m]);
+                }
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) E::st4(bo, ((t0 + 16 * m + n16) * D + vb + 16 * nt + 4 * q4) * 2, O[nt][m]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
-                    S[mt][nt] = E::mma(a, E::ld_col8(tQr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), S[mt][nt]);
-            }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S[mt][nt][e] *= gC;
+        }
+        block_sync();  // B10: the (gamma_C / gamma) k rows complete
+        if (vw) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+                    const frag_t a = E::ld_col8(tKg, L::PD, ts * 32 + 8 * q4, 16 * mt, n16);
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt)
+                        S[mt][nt] = E::mma(a, E::ld_col8(tKr, L::PD, ts * 32 + 8 * q4, vb + 16 * nt, n16), S[mt][nt]);
+                }
         }
         }
         block_sync();  // B11: tiles free for the next chunk
