@@ -123,6 +123,21 @@ __device__ __forceinline__ void wave_lds_fence() { __asm__ __volatile__("s_waitc
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
+// N consecutive bf16 of an LDS row from fp32, one 4-byte store for a pair
+// (dst then 4-byte aligned)
+template <int N>
+__device__ __forceinline__ void st_cols(__bf16 *dst, const float (&v)[N]) {
+    if constexpr (N == 2) {
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        // one conversion of the pair (round to nearest even), first value low
+        *reinterpret_cast<bf16x2_t *>(dst) = __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) dst[n] = (__bf16)v[n];
+    }
+}
+
 // four consecutive bf16 of an LDS row (8 bytes) from fp32
 __device__ __forceinline__ void st_row4(__bf16 *dst, f32x4_t x) {
     bf16x4_t b;
@@ -291,21 +306,28 @@ gdn_kernel(const GdnParams p) {
             rq[i].x = reinterpret_cast<const decltype(rq[i].x) *>(stq + (r0 + i) * D * 2)[lane];
             rk[i].x = reinterpret_cast<const decltype(rk[i].x) *>(stk + (r0 + i) * D * 2)[lane];
         }
+        // a lane's CPL columns stay adjacent in every layout (perm_col keeps the
+        // pair 2l, 2l + 1 together), so each row of each tile is one store
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int r = r0 + i;
             const float gr = sGc[r];
             const float gam = fexp2(gr);
+            const int col = lane * CPL;
+            float kv[CPL], qv[CPL], kgv[CPL], qhv[CPL];
 #pragma unroll
             for (int u = 0; u < CPL; ++u) {
-                const int col = lane * CPL + u;
-                const float qv = rq[i].get(u), kv = rk[i].get(u);
-                reinterpret_cast<__bf16 *>(tKr)[r * L::QP + col] = (__bf16)kv;
-                reinterpret_cast<__bf16 *>(tQr)[r * L::QP + col] = (__bf16)qv;
-                if constexpr (PREP) rowp(tKg, r, L::PD)[col] = (__bf16)(kv * gam);
-                else tKh[r * L::QP + perm_col(col)] = (__bf16)(kv * gam);
-                tQh[r * L::QP + perm_col(col)] = (__bf16)(qv * gam * p.scale);
+                kv[u] = rk[i].get(u);
+                qv[u] = rq[i].get(u);
+                kgv[u] = kv[u] * gam;
+                qhv[u] = qv[u] * gam * p.scale;
             }
+            using raw_t = decltype(rk[i].x);   // the raw rows as loaded, no conversion
+            *reinterpret_cast<raw_t *>(reinterpret_cast<__bf16 *>(tKr) + r * L::QP + col) = rk[i].x;
+            *reinterpret_cast<raw_t *>(reinterpret_cast<__bf16 *>(tQr) + r * L::QP + col) = rq[i].x;
+            if constexpr (PREP) st_cols(rowp(tKg, r, L::PD) + col, kgv);
+            else st_cols(tKh + r * L::QP + perm_col(col), kgv);
+            st_cols(tQh + r * L::QP + perm_col(col), qhv);
         }
         block_sync();  // B2: operand tiles
 
@@ -499,8 +521,10 @@ gdn_kernel(const GdnParams p) {
         for (int i = 0; i < RPW; ++i) {   // (gamma_C / gamma) k over gamma k
             const int r = r0 + i;
             const float gk = fexp2(gcl - sGc[r]);
+            float kv[CPL];
 #pragma unroll
-            for (int u = 0; u < CPL; ++u) rowp(tKg, r, L::PD)[lane * CPL + u] = (__bf16)(rk[i].get(u) * gk);
+            for (int u = 0; u < CPL; ++u) kv[u] = rk[i].get(u) * gk;
+            st_cols(rowp(tKg, r, L::PD) + lane * CPL, kv);
         }
         using R = GdnRec<D, C>;
         unsigned char *rec = nullptr;
@@ -609,8 +633,10 @@ gdn_kernel(const GdnParams p) {
         for (int i = 0; i < RPW; ++i) {   // (gamma_C / gamma) k over gamma k
             const int r = r0 + i;
             const float gk = fexp2(gcl - sGc[r]);
+            float kv[CPL];
 #pragma unroll
-            for (int u = 0; u < CPL; ++u) rowp(tKg, r, L::PD)[lane * CPL + u] = (__bf16)(rk[i].get(u) * gk);
+            for (int u = 0; u < CPL; ++u) kv[u] = rk[i].get(u) * gk;
+            st_cols(rowp(tKg, r, L::PD) + lane * CPL, kv);
         }
         wave_lds_fence();   // this wave's U columns, read back below
         const float gC = fexp2(gcl);
