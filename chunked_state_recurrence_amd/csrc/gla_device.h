@@ -341,6 +341,25 @@ __device__ __forceinline__ void quad_transpose4(float (&x)[4], int j) {
     if (lo1) { x[1] = r0; x[3] = r1; } else { x[0] = r0; x[2] = r1; }
 }
 
+// N consecutive elements of an LDS row from fp32 with one store (N = 2 or 4;
+// dst aligned to the store's size), element-wise for N = 1.  bf16 values are
+// rounded to nearest even, one conversion per pair.
+template <typename E, int N>
+__device__ __forceinline__ void st_lds_cols(typename E::lds_t *dst, const float (&v)[N]) {
+    using l_t = typename E::lds_t;
+    if constexpr (N == 2 || N == 4) {
+        typedef float fN_t __attribute__((ext_vector_type(N)));
+        typedef l_t lN_t __attribute__((ext_vector_type(N)));
+        fN_t x;
+#pragma unroll
+        for (int n = 0; n < N; ++n) x[n] = v[n];
+        *reinterpret_cast<lN_t *>(dst) = __builtin_convertvector(x, lN_t);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) dst[n] = E::f2l(v[n]);
+    }
+}
+
 // two floats as packed bf16 (round to nearest even), the first in the low half
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     const __bf16 ha = (__bf16)a, hb = (__bf16)b;

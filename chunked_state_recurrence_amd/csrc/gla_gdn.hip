@@ -123,21 +123,6 @@ __device__ __forceinline__ void wave_lds_fence() { __asm__ __volatile__("s_waitc
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-// N consecutive bf16 of an LDS row from fp32, one 4-byte store for a pair
-// (dst then 4-byte aligned)
-template <int N>
-__device__ __forceinline__ void st_cols(__bf16 *dst, const float (&v)[N]) {
-    if constexpr (N == 2) {
-        typedef float f32x2_t __attribute__((ext_vector_type(2)));
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        // one conversion of the pair (round to nearest even), first value low
-        *reinterpret_cast<bf16x2_t *>(dst) = __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t);
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n) dst[n] = (__bf16)v[n];
-    }
-}
-
 // four consecutive bf16 of an LDS row (8 bytes) from fp32
 __device__ __forceinline__ void st_row4(__bf16 *dst, f32x4_t x) {
     bf16x4_t b;
@@ -325,9 +310,9 @@ gdn_kernel(const GdnParams p) {
             using raw_t = decltype(rk[i].x);   // the raw rows as loaded, no conversion
             *reinterpret_cast<raw_t *>(reinterpret_cast<__bf16 *>(tKr) + r * L::QP + col) = rk[i].x;
             *reinterpret_cast<raw_t *>(reinterpret_cast<__bf16 *>(tQr) + r * L::QP + col) = rq[i].x;
-            if constexpr (PREP) st_cols(rowp(tKg, r, L::PD) + col, kgv);
-            else st_cols(tKh + r * L::QP + perm_col(col), kgv);
-            st_cols(tQh + r * L::QP + perm_col(col), qhv);
+            if constexpr (PREP) st_lds_cols<E>(rowp(tKg, r, L::PD) + col, kgv);
+            else st_lds_cols<E>(tKh + r * L::QP + perm_col(col), kgv);
+            st_lds_cols<E>(tQh + r * L::QP + perm_col(col), qhv);
         }
         block_sync();  // B2: operand tiles
 
@@ -524,7 +509,7 @@ gdn_kernel(const GdnParams p) {
             float kv[CPL];
 #pragma unroll
             for (int u = 0; u < CPL; ++u) kv[u] = rk[i].get(u) * gk;
-            st_cols(rowp(tKg, r, L::PD) + lane * CPL, kv);
+            st_lds_cols<E>(rowp(tKg, r, L::PD) + lane * CPL, kv);
         }
         using R = GdnRec<D, C>;
         unsigned char *rec = nullptr;
@@ -636,7 +621,7 @@ gdn_kernel(const GdnParams p) {
             float kv[CPL];
 #pragma unroll
             for (int u = 0; u < CPL; ++u) kv[u] = rk[i].get(u) * gk;
-            st_cols(rowp(tKg, r, L::PD) + lane * CPL, kv);
+            st_lds_cols<E>(rowp(tKg, r, L::PD) + lane * CPL, kv);
         }
         wave_lds_fence();   // this wave's U columns, read back below
         const float gC = fexp2(gcl);
