@@ -158,7 +158,7 @@ gdn_kernel(const GdnParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::main_bytes];
     __shared__ __attribute__((aligned(16))) unsigned char sAT[L::at_bytes];
     __shared__ __attribute__((aligned(16))) unsigned char sVV[L::v_bytes];
-    __shared__ float sGc[C];     // chunk-local inclusive cumsum of g, log2 units
+    __shared__ __attribute__((aligned(16))) float sGc[C];   // chunk-local inclusive cumsum of g, log2 units
     __shared__ float sBeta[C];
 
     unsigned char *tKr = smem + L::kr;   // raw k, row-major (then -W, permuted)
@@ -335,16 +335,24 @@ gdn_kernel(const GdnParams p) {
                 kk = E::mma(kj, E::ld_frag(kraw + (16 * I + n16) * L::QP + pos), kk);
                 qk = E::mma(kj, E::ld_frag(qraw + (16 * I + n16) * L::QP + pos), qk);
             }
-            // acc[e] = (. . k_j)[i = 16I + n16][j = 16J + 4q4 + e]
+            // acc[e] = (. . k_j)[i = 16I + n16][j = 16J + 4q4 + e]; the factors are
+            // formed for every j and masked by selects (no branches), and the four
+            // values go out as one store per tile
             const int i = 16 * I + n16;
             const float gi = sGc[i], bi = sBeta[i];
+            const f32x4_t gj = *reinterpret_cast<const f32x4_t *>(sGc + 16 * J + 4 * q4);
+            f32x4_t av;
+            float pv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 16 * J + 4 * q4 + e;
-                const float ratio = j <= i ? fexp2(gi - sGc[j]) : 0.f;
-                tA[i * L::PF + j] = j < i ? bi * ratio * kk[e] : 0.f;
-                rowp(tP, i, L::PC)[j] = (__bf16)(p.scale * ratio * qk[e]);
+                const float rt = fexp2(gi - gj[e]);   // may overflow above the diagonal: never used there
+                const float ratio = j <= i ? rt : 0.f;
+                av[e] = j < i ? bi * ratio * kk[e] : 0.f;
+                pv[e] = p.scale * ratio * qk[e];
             }
+            *reinterpret_cast<f32x4_t *>(tA + i * L::PF + 16 * J + 4 * q4) = av;
+            st_lds_cols<E>(rowp(tP, i, L::PC) + 16 * J + 4 * q4, pv);
         }
         block_sync();  // B3: A, P
 
