@@ -107,23 +107,48 @@ def host_threads() -> int:
         return os.cpu_count() or 1
 
 
-def gpu_product_name():
-    """The GPU's marketing name where the device properties leave it empty:
-    the first "Marketing Name" of a GPU agent in rocminfo's listing (a child
-    process), else None."""
-    import subprocess
+def hsa_gpu_info():
+    """The first GPU agent's board name (HSA_AMD_AGENT_INFO_PRODUCT_NAME,
+    0xA009, 64 chars; the runtime fills it from the KFD node's marketing name
+    and falls back to a generic one where libdrm's ID table is missing) and
+    its maximum engine clock in MHz (HSA_AMD_AGENT_INFO_MAX_CLOCK_FREQUENCY,
+    0xA003), asked of the HSA runtime in this process (hsa_init is reference
+    counted); (None, None) where there is none.  No child process is started:
+    a GPU process must not exec another program."""
+    import ctypes
     try:
-        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=20).stdout
-    except (OSError, subprocess.SubprocessError):
-        return None
-    name = None
-    for line in out.splitlines():
-        line = line.strip()
-        if line.startswith("Marketing Name:"):
-            name = line.split(":", 1)[1].strip()
-        elif line.startswith("Device Type:") and line.split(":", 1)[1].strip() == "GPU" and name:
-            return name
-    return None
+        hsa = ctypes.CDLL("libhsa-runtime64.so.1")
+    except OSError:
+        return None, None
+    if hsa.hsa_init() != 0:
+        return None, None
+    found = []
+    cb_t = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p)
+
+    def visit(agent, _data):
+        dev = ctypes.c_uint32(0)
+        if hsa.hsa_agent_get_info(ctypes.c_uint64(agent), 17, ctypes.byref(dev)) == 0 and dev.value == 1:
+            buf = ctypes.create_string_buffer(64)
+            clk = ctypes.c_uint32(0)
+            name = (buf.value.decode(errors="replace").strip()
+                    if hsa.hsa_agent_get_info(ctypes.c_uint64(agent), 0xA009, buf) == 0 else None)
+            mhz = clk.value if hsa.hsa_agent_get_info(ctypes.c_uint64(agent), 0xA003, ctypes.byref(clk)) == 0 else None
+            found.append((name or None, mhz or None))
+        return 0   # HSA_STATUS_SUCCESS: keep iterating
+
+    try:
+        hsa.hsa_iterate_agents(cb_t(visit), None)
+    finally:
+        hsa.hsa_shut_down()
+    return found[0] if found else (None, None)
+
+
+def gpu_label(arch, cus, mhz, board):
+    """The product: gfx950 with 256 CUs is MI355X at a 2400 MHz peak engine
+    clock and MI350X below it (labelled as inferred); else the board name."""
+    if arch and arch.startswith("gfx950") and cus == 256 and mhz:
+        return f"AMD Instinct {'MI355X' if mhz >= 2400 else 'MI350X'} (inferred: gfx950, 256 CUs, {mhz} MHz)"
+    return board
 
 
 def environment() -> dict:
@@ -156,10 +181,13 @@ def environment() -> dict:
         env["torch_hip"] = torch.version.hip
         if torch.cuda.is_available():
             prop = torch.cuda.get_device_properties(0)
-            env["gpu"] = prop.name or gpu_product_name()
+            board, mhz = hsa_gpu_info()
             env["gpu_arch"] = getattr(prop, "gcnArchName", None)
             env["gpu_cus"] = prop.multi_processor_count
             env["gpu_mem_gib"] = round(prop.total_memory / 2 ** 30, 1)
+            env["gpu_max_clock_mhz"] = mhz
+            env["gpu_board_name"] = prop.name or board
+            env["gpu"] = gpu_label(env["gpu_arch"], env["gpu_cus"], mhz, env["gpu_board_name"])
     except Exception as e:   # noqa: BLE001 - informational only
         env["torch_error"] = str(e)
     return env
@@ -881,6 +909,12 @@ def main():
               "communication, a sequence split would exchange one segment state per GPU)",
               file=sys.stderr)
         sys.exit(2)
+
+    if not (args.no_cpu and args.no_parity):
+        # the oracle (CPU baseline, parity sample) is compiled here if it is
+        # missing, before anything touches the GPU
+        from oracle.reference import ensure_built
+        ensure_built()
 
     if args.sweep:
         bench_sweep(args)

@@ -43,11 +43,19 @@ def build_oracle_library(force: bool = True) -> str:
     return _LIB
 
 
+def ensure_built() -> str:
+    """Compile liboracle.so if it is missing.  Callers do this before anything
+    touches the GPU: compiling starts gcc as a child process, which a process
+    that has initialised the GPU must not do."""
+    return build_oracle_library(force=False)
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
-            build_oracle_library(force=True)
+            raise RuntimeError(f"{_LIB} is not built: run __graft_entry__.build() or "
+                               "oracle.reference.ensure_built() before any GPU work")
         lib = ctypes.CDLL(_LIB)
         dp = ctypes.POINTER(ctypes.c_double)
         lib.gla_oracle_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,

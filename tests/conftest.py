@@ -8,3 +8,6 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # the C oracle is compiled here, if it is missing, before any test touches the GPU
+    from oracle.reference import ensure_built
+    ensure_built()

@@ -87,3 +87,16 @@ def test_summarize_mfma_arithmetic(tmp_path):
     assert abs(r["util"] - 16e6 / (1024 * 240000.0)) < 1e-12
     assert abs(r["bf16"] - 1e6 * 16384 / 100e-6 / 1e12) < 1e-9   # 163.84 TFLOP/s
     assert r["fp32"] == 0.0
+
+
+def test_gpu_label():
+    # the product from the arch, CU count and peak engine clock, marked as inferred
+    assert bench.gpu_label("gfx950:sramecc+:xnack-", 256, 2400, "AMD Radeon Graphics").startswith(
+        "AMD Instinct MI355X (inferred")
+    assert bench.gpu_label("gfx950", 256, 2200, None).startswith("AMD Instinct MI350X (inferred")
+    # anything else keeps the board name the runtime gave
+    assert bench.gpu_label("gfx942", 304, 2100, "AMD Instinct MI300X") == "AMD Instinct MI300X"
+    assert bench.gpu_label("gfx950", 256, None, "board") == "board"
+    # no GPU agent here: the in-process query answers (None, None) or a pair, never raises
+    info = bench.hsa_gpu_info()
+    assert isinstance(info, tuple) and len(info) == 2
