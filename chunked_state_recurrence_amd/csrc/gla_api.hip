@@ -549,7 +549,12 @@ int gla_gdn_fwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v, const f
         wcap = g_gdn_window;
     }
     const int N = (T + 63) / 64;
-    const bool two = path == GLA_GDN_TWO_LAUNCH || (path == GLA_GDN_AUTO && long(bh) * 4 <= target);
+    // The walk runs K / 16 one-wave work-groups per (batch, head), one per CU;
+    // while they all fit at once the two launches win, beyond that the walk
+    // takes a second round (T = 4K, K = 128: two launches 0.149 / 0.202 ms
+    // against one 0.301 / 0.309 ms at B*H = 16 / 32; from B*H = 40 one launch,
+    // 0.312 against 0.390 ms)
+    const bool two = path == GLA_GDN_TWO_LAUNCH || (path == GLA_GDN_AUTO && long(bh) * (K / 16) <= target);
     if (!two) {
         // split value columns over work-groups while batch x heads leaves CUs idle
         int nvb = 1;

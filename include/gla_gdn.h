@@ -61,8 +61,9 @@ int gla_gdn_fwd(const gla_bf16 *q, const gla_bf16 *k, const gla_bf16 *v,
 /*
  * gla_gdn_set_path — which form gla_gdn_fwd uses (process-wide; a schedule
  * knob with no effect on results beyond rounding): GLA_GDN_AUTO (default:
- * two launches when 4*B*H <= the work-group target of gla_set_tuning, 256 by
- * default), GLA_GDN_ONE_LAUNCH, GLA_GDN_TWO_LAUNCH.  window_chunks > 0 caps
+ * two launches when B*H*K/16, the walk's one-wave work-groups, is at most
+ * the work-group target of gla_set_tuning, 256 by default: B*H <= 32 at
+ * K = 128, B*H <= 64 at K = 64), GLA_GDN_ONE_LAUNCH, GLA_GDN_TWO_LAUNCH.  window_chunks > 0 caps
  * the two-launch form's windows at that many 64-token chunks (0 = only the
  * 1 GiB record cap).  Returns GLA_OK, or GLA_ERR_SHAPE for another path or a
  * negative window.

@@ -5,7 +5,9 @@ header defines.  The GPU test checks, for one call of each entry point, the
 launches the library records and their order: the forward's state pass, scan
 and output pass; the backward's forward state pass, scan, states-only pass,
 its own segment pass, scan and chunk pass; a decode step; the T = 0 copy of
-h0 into h_final; and that tracing stops at the capacity it was given.
+h0 into h_final; that tracing stops at the capacity it was given; and the
+gated delta rule's automatic form on each side of its boundary (prep + walk
+while B*H*D/16 <= 256, one launch beyond).
 """
 
 import re
@@ -77,3 +79,22 @@ def test_launch_kinds_per_entry_point():
     _say("[trace] capacity")
     recs = _trace(lambda: gla.gla_fwd(q, k, v, g, None, want_final=True), capacity=2)
     assert [kind for kind, _ in recs] == ["segment", "scan"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D,BH,two", [(128, 32, True), (128, 40, False), (64, 64, True), (64, 72, False)])
+def test_gdn_automatic_form(D, BH, two):
+    # two launches (prep + walk) while the walk's B*H*D/16 one-wave work-groups
+    # fit the 256 work-group target, one launch beyond (include/gla_gdn.h)
+    gla.set_tuning(0, 0)
+    gla.gdn_set_path("auto")
+    B, H, T = BH // 8, 8, 128
+    gen = torch.Generator().manual_seed(BH)
+    q, k = (torch.nn.functional.normalize(torch.randn(B, H, T, D, generator=gen), dim=-1).bfloat16().to(DEV)
+            for _ in range(2))
+    v = torch.randn(B, H, T, D, generator=gen).bfloat16().to(DEV)
+    g = (torch.nn.functional.logsigmoid(torch.randn(B, H, T, generator=gen)) / 16).to(DEV)
+    beta = torch.sigmoid(torch.randn(B, H, T, generator=gen)).to(DEV)
+    _say(f"[trace gdn auto] D={D} B*H={BH}")
+    recs = _trace(lambda: gla.gla_gdn_fwd(q, k, v, g, beta, None))
+    assert [kind for kind, _ in recs] == (["gdn_prep", "gdn_walk"] if two else ["gdn"])
