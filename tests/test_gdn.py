@@ -117,6 +117,21 @@ def test_value_block_split(target):
     check(x, o, hf)
 
 
+@pytest.mark.parametrize("target", [1, 8, 0])
+def test_value_block_split_d64(target):
+    """The same at D = 64 (four waves): value columns over 1 (every wave owns
+    columns, the one that solves T's diagonal blocks included), 2 or 4 (only the
+    first waves own columns) work-groups per head."""
+    import dataclasses
+    say(f"[gdn value blocks D=64] target_wgs={target}")
+    wl = dataclasses.replace(BASE, D=64)
+    x = make_gdn_inputs(wl, B=2, H=2, T=333, seed=64, h0_std=0.2)
+    gla.gdn_set_path("one")
+    gla.set_tuning(target, 0)
+    o, hf = gpu_run(x)
+    check(x, o, hf)
+
+
 @pytest.mark.parametrize("window,slices_target", [(1, 0), (3, 0), (2, 1), (0, 100000)])
 def test_two_launch_windows_and_slices(window, slices_target):
     """Two-launch form over windows of 1 or 3 chunks (state carried between
